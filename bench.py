@@ -1,0 +1,236 @@
+"""Decode-megakernel benchmark: forward passes/s on the Llama-1B-shaped
+batch-1 decode (16 layers, hidden 2048, 32/8 heads, head_dim 64, SwiGLU 8192,
+vocab 128256, tied embeddings, bf16 weights ~N(0, 0.02), KV cache prefilled
+with bf16 N(0,1) up to position 1024, decode from position 1024).
+
+One "step" is one decoder forward pass (one persistent kernel launch),
+enqueued back to back with the on-device token/position advance, inputs
+resident in HBM.  Prints one JSON line with the headline number, the HBM
+roofline of the megakernel, the CPU-oracle baseline, and extras (the
+multi-launch build of the same ops, the flag-synchronised variant, the
+grid-barrier microbenchmark and the streaming-read probe).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def bytes_per_pass(shape, positions):
+    """Algorithmic HBM bytes of one pass: every bf16 parameter once (the
+    embedding matrix once, as the tied LM head; one embedding row otherwise
+    extra), keys/values of the cached positions read, the new position's
+    keys/values written, fp32 logits written, the token's embedding row."""
+    s = shape
+    d, L, H = s.head_dim, s.n_layers, s.hidden
+    params = L * (H * (s.n_q_heads + 2 * s.n_kv_heads) * d + s.n_q_heads * d * H + 3 * H * s.ffn + 2 * H) \
+        + s.vocab * H + H
+    if not s.tied:
+        params += s.vocab * H  # separate LM head; the embedding contributes one row below
+    kv_b = L * s.n_kv_heads * d * 2 * 2  # bytes per cached position (keys + values)
+    total = 0.0
+    for p in positions:
+        total += 2 * params + p * kv_b + kv_b + 4 * s.vocab + 2 * H
+    return total / len(positions)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama1b_pos1024")
+    ap.add_argument("--mode", default="mega", choices=["mega", "multi", "mega-flag"],
+                    help="what to time for the headline (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode megakernel path "
+                                   "is single-GPU (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    from persistent_megakernel_decode_02_amd import engine, mk
+
+    mk.load_library()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    dev = "cuda:0"
+    wl = si.WORKLOADS[args.workload]
+    s = wl.shape
+    B = wl.batch
+    K, W = args.steps, args.warmup
+    max_ctx = max(wl.max_ctx, (wl.start_pos if wl.start_pos > 0 else 0) + K + 1)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    t0 = time.time()
+    w = si.make_weights(s, master=0)
+    gw = engine.to_gpu(w, dev)
+    pos0 = wl.positions0(0)
+    kv_cpu = si.make_kv_cache(s, B, max_ctx, pos0, master=0)
+    kv = kv_cpu.to(dev)
+    first = si.workload_tokens(wl, 0)[:B]
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s ({args.workload})")
+
+    stream = torch.cuda.current_stream()
+    tokens = torch.tensor(first, dtype=torch.int32, device=dev)
+    positions = torch.tensor(pos0, dtype=torch.int32, device=dev)
+    logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def timed(exec_mode, sync_mode, k, w_):
+        eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, sync_mode=sync_mode, exec_mode=exec_mode,
+                            stream=stream)
+        try:
+            tokens.copy_(torch.tensor(first, dtype=torch.int32))
+            positions.copy_(torch.tensor(pos0, dtype=torch.int32))
+            for _ in range(w_):
+                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+            rc, det = eng.device_error()
+            if rc != 0:
+                raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
+            tokens.copy_(torch.tensor(first, dtype=torch.int32))
+            positions.copy_(torch.tensor(pos0, dtype=torch.int32))
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(k):
+                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rc, det = eng.device_error()
+            if rc != 0:
+                raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
+            ms = e0.elapsed_time(e1)
+            return ms, eng.info
+        finally:
+            eng.close()
+
+    modes = {"mega": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
+             "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG)}
+    ms, info = timed(*modes[args.mode], K, W)
+    log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
+    ms_per = ms / K
+    passes_s = 1000.0 / ms_per * 1.0
+    positions_timed = [p + t for t in range(K) for p in pos0]
+    bpp = bytes_per_pass(s, positions_timed) if B == 1 else bytes_per_pass(s, positions_timed) * 1.0
+    achieved = bpp / (ms_per * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "mk_mega_kernel" if args.mode != "multi" else "mk_level_kernel",
+            "bytes_per_launch": bpp if args.mode != "multi" else None}
+
+    extras = {"plan": {"cus": info.num_cus, "instructions": info.n_instructions, "levels": info.n_levels,
+                       "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
+                       "block_threads": info.block_threads}}
+    if not args.no_extras:
+        for name in [m for m in modes if m != args.mode]:
+            ms2, _ = timed(*modes[name], K, W)
+            extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
+                            "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] {name}: {K} passes in {ms2:.3f} ms")
+        if "multi" in extras:
+            extras["bubble_us_per_pass"] = round((extras["multi"]["ms_per_pass"] - ms_per) * 1000.0, 2)
+            extras["launches_per_pass_multi"] = info.n_levels
+        # grid-barrier microbenchmark
+        dinfo = mk.mk_device_query(0)
+        n = dinfo.num_cus
+        scratch = torch.empty(mk.mk_gridsync_scratch_bytes(n) + 256, dtype=torch.uint8, device=dev)
+        base = (scratch.data_ptr() + 255) // 256 * 256
+        res = torch.zeros(4, dtype=torch.int32, device=dev)
+        gs = {}
+        nb = 5000
+        for v, vname in mk.GRIDSYNC_VARIANTS.items():
+            mk.mk_gridsync_bench(v, 20, n, base, res.data_ptr(), stream.cuda_stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mk.mk_gridsync_bench(v, nb, n, base, res.data_ptr(), stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gs[vname] = round(e0.elapsed_time(e1) * 1000.0 / nb, 3)
+        r = res.cpu().tolist()
+        extras["gridsync_us_per_barrier"] = gs
+        extras["gridsync_blocks"] = n
+        extras["gridsync_errors"] = r[0]
+        extras["gridsync_timeouts"] = r[1]
+        log(f"[bench] gridsync {gs}")
+        del scratch
+        # streaming-read probe over 4 GiB (well beyond the 256 MiB Infinity Cache)
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        out = torch.empty(n * 8, dtype=torch.int32, device=dev)
+        mk.mk_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), n * 8, stream.cuda_stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 5
+        for _ in range(reps):
+            mk.mk_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), n * 8, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        extras["stream_read_gbs"] = round(reps * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        log(f"[bench] stream read {extras['stream_read_gbs']} GB/s")
+        del buf
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        model = orc.Model(s, w)
+        kv_o = si.bf16_bits(kv_cpu).reshape(kv_cpu.shape).copy()
+        tok = list(first)
+        pos = list(pos0)
+        n_done = 0
+        t1 = time.time()
+        while n_done == 0 or (time.time() - t1 < args.cpu_seconds and n_done < K):
+            _, nx = model.step(tok, pos, kv_o, B, max_ctx)
+            tok = [int(v) for v in nx]
+            pos = [p + 1 for p in pos]
+            n_done += 1
+        el = time.time() - t1
+        cpu = {"value": round(n_done / el, 4), "unit": "passes/s", "cores": orc.num_threads(), "kind": "oracle",
+               "sample": f"{n_done} greedy passes of {args.workload} from position {pos0[0]} (fp64 oracle, "
+                         f"OpenMP over output rows), {el:.1f} s"}
+        log(f"[bench] cpu oracle {cpu}")
+
+    line = {
+        "metric": "forward passes/s at batch 1 (Llama-1B shape) and % of HBM roofline",
+        "value": round(passes_s, 2),
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights, fp32 accumulate",
+        "data": "synthetic (seeded bf16 N(0,0.02) weights, bf16 N(0,1) KV prefill, uniform token ids)",
+        "config": {"workload": args.workload, "batch": B, "start_position": pos0[0], "passes": K,
+                   "layers": s.n_layers, "hidden": s.hidden, "heads": f"{s.n_q_heads}/{s.n_kv_heads}",
+                   "head_dim": s.head_dim, "ffn": s.ffn, "vocab": s.vocab, "tied": s.tied,
+                   "exec": args.mode},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+/*
+ * mk.h -- C ABI of the persistent decode megakernel library (libmk.so).
+ *
+ * One Llama-style decoder forward pass per generated token, run on an
+ * MI355X (gfx950) as ONE persistent launch: one workgroup per compute unit,
+ * each walking a host-built list of instructions and waiting on dependency
+ * counters in global memory instead of kernel boundaries.  The megakernel
+ * page ("2 . Definition et genealogie") defines the object in section 2.1
+ * (single launch, persistence, fine dependencies in global memory, internal
+ * dispatch of heterogeneous ops), states in section 2.5 that the host builds
+ * the instruction lists the GPU consumes, and lists in section 2.6 the five
+ * mechanisms this library implements: a grid sized for full residency,
+ * opcode dispatch, dependency counters, a paged shared-memory allocator and
+ * static scheduling.
+ *
+ * Conventions for every call:
+ *   - Plain C types only.  `stream` arguments are hipStream_t values passed as
+ *     void* (NULL = the legacy default stream).  "d_" pointers are device
+ *     memory, everything else is host memory.
+ *   - The library never allocates device memory.  All device buffers
+ *     (weights, KV cache, workspace, logits, tokens, positions) belong to the
+ *     caller and must outlive every call that was enqueued with them.
+ *   - Device-touching calls enqueue work on `stream` and return without
+ *     synchronising, except mk_get_device_error which synchronises `stream`.
+ *   - Return value: MK_OK (0) or a negative MK_ERR_* code; mk_strerror turns
+ *     it into text.  A failing call leaves its outputs untouched.
+ *   - A plan or a context is used by one host thread at a time.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ error codes */
+#define MK_OK 0
+#define MK_ERR_INVALID_ARG (-1)   /* NULL pointer, out-of-range option */
+#define MK_ERR_SHAPE (-2)         /* model shape the kernels do not support */
+#define MK_ERR_ALIGN (-3)         /* a device pointer is not 16-byte aligned */
+#define MK_ERR_NOT_RESIDENT (-4)  /* grid larger than the co-resident limit */
+#define MK_ERR_CTX_OVERFLOW (-5)  /* batch > max_batch or workspace too small */
+#define MK_ERR_HIP (-6)           /* a HIP runtime call failed */
+#define MK_ERR_TIMEOUT (-7)       /* device watchdog: a dependency wait expired */
+#define MK_ERR_INPUT (-8)         /* device saw a token or position out of range */
+#define MK_ERR_PLAN (-9)          /* plan validation failed */
+#define MK_ERR_STATE (-10)        /* context poisoned by a device error; reset it */
+#define MK_ERR_UNSUPPORTED (-11)  /* option combination not built */
+
+/* ------------------------------------------------------------ model shape */
+/* Standard Llama decoder, nn.Linear weight convention W[out][in], bf16.
+ * Rotate-half RoPE pairs element i with i + head_dim/2; q head h reads kv head
+ * h * n_kv_heads / n_q_heads.  Requirements: head_dim in {64, 128};
+ * n_q_heads % n_kv_heads == 0; hidden, ffn and n_q_heads*head_dim multiples
+ * of 256. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  double rms_eps;      /* RMSNorm epsilon, added inside the square root */
+  double rope_theta;   /* RoPE base: angle(p, i) = p * theta^(-2i/head_dim) */
+  int32_t tie_embeddings; /* 1: the LM head is the embedding matrix */
+} mk_model_shape;
+
+/* ------------------------------------------------------------ plan options */
+enum { MK_SYNC_COUNTER = 0, /* one monotonic counter per event, atomic add */
+       MK_SYNC_FLAG = 1     /* one epoch flag per producer, plain stores */ };
+enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step */
+       MK_EXEC_MULTI = 1    /* one launch per op level (kernel boundaries) */ };
+
+typedef struct {
+  int32_t max_batch;   /* sequences per step, 1..16 */
+  int32_t max_ctx;     /* KV slots per sequence */
+  int32_t kv_splits;   /* attention splits per (sequence, kv head); 0 = auto */
+  int32_t sync_mode;   /* MK_SYNC_* */
+  int32_t exec_mode;   /* MK_EXEC_* */
+  int32_t num_cus;     /* 0 = query the current device; >0 = plan for that many
+                          (host-only planning, tests) */
+  int32_t flags;       /* reserved, 0 */
+} mk_plan_opts;
+
+typedef struct mk_plan mk_plan; /* opaque, host memory, owned by the library */
+typedef struct mk_ctx mk_ctx;   /* opaque, host memory, owned by the library */
+
+/* Read-only description of a plan (for tests and tools). */
+typedef struct {
+  int32_t num_cus, n_instructions, n_levels, n_counters, kv_splits;
+  int32_t max_instr_per_cu, block_threads, lds_bytes;
+  int32_t sync_mode, exec_mode, max_batch, max_ctx;
+  double weight_bytes;   /* bf16 parameter bytes one pass streams */
+} mk_plan_info;
+
+/* One instruction as the planner emitted it (for tests and tools). */
+typedef struct {
+  int32_t cu, slot;          /* executing workgroup and position in its list */
+  int32_t op, layer, level;
+  int32_t r0, r1;            /* GEMV: output rows [r0, r1); ATTN: seq, kv head */
+  int32_t split, n_splits;   /* ATTN: key range split index / count */
+  int32_t wait_event, wait_count; /* event it waits for (-1 none), triggers per step */
+  int32_t signal_event;      /* event it triggers when done (-1 none) */
+} mk_instr_desc;
+
+enum { MK_OP_QKV = 1, MK_OP_ATTN = 2, MK_OP_OPROJ = 3, MK_OP_GATEUP = 4, MK_OP_DOWN = 5,
+       MK_OP_LMHEAD = 6 };
+
+/* Build a plan on the host: split every layer into per-CU instructions
+ * (QKV row slices with the RMSNorm prologue; RoPE + KV append + split-KV
+ * decode attention per (sequence, kv head, split); O-projection + residual;
+ * gate/up + SiLU; down-projection + residual; LM-head row slices with
+ * argmax), give each instruction the event it waits for and the event it
+ * triggers, order each CU's list by dependency level (deadlock-free under
+ * co-residency), and validate the result.  Host only; no device work unless
+ * opts->num_cus == 0, which queries the current device's CU count.
+ * (Megakernel page, section 2.5: the CPU builds the per-unit instruction
+ * lists; section 2.6 item 5: static per-unit lists.) */
+int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan **out);
+
+/* Re-check a plan: every RAW dependency is covered by a waited event whose
+ * triggers all precede it by level, no event is waited for more often than it
+ * is triggered, lists are level-sorted, and the counters' targets are
+ * reachable.  MK_OK or MK_ERR_PLAN. */
+int mk_plan_validate(const mk_plan *plan);
+
+/* Bytes the caller must allocate: workspace (device, 256-byte aligned), KV
+ * cache (bf16 [n_layers][2][max_batch][n_kv_heads][max_ctx][head_dim]; plane
+ * 0 keys, plane 1 values), logits (fp32 [max_batch][vocab]). */
+int mk_plan_sizes(const mk_plan *plan, size_t *workspace_bytes, size_t *kv_cache_bytes,
+                  size_t *logits_bytes, size_t *n_instructions);
+int mk_plan_get_info(const mk_plan *plan, mk_plan_info *out);
+/* Copy up to `cap` instruction descriptors into `out` (host array); *n_out
+ * receives the total count. */
+int mk_plan_export(const mk_plan *plan, mk_instr_desc *out, size_t cap, size_t *n_out);
+/* Run the host-side schedule simulator: execute the plan's lists under
+ * `n_trials` random interleavings (seeded) with no arithmetic, checking that
+ * every wait is eventually satisfied and every read follows its producers.
+ * MK_OK or MK_ERR_PLAN. */
+int mk_plan_simulate(const mk_plan *plan, int32_t n_trials, uint64_t seed);
+void mk_plan_destroy(mk_plan *plan);
+
+/* Bind a plan to caller-owned device workspace (d_workspace, at least the
+ * size mk_plan_sizes reports, 256-byte aligned).  Enqueues the upload of the
+ * instruction lists and RoPE table and the zeroing of the counters on
+ * `stream`.  The plan may be destroyed afterwards. */
+int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t workspace_bytes, void *stream,
+                  mk_ctx **out);
+
+/* Weight tensors, all bf16 device pointers, 16-byte aligned, row-major
+ * W[out][in].  Per-layer tensors come as host arrays of n_layers device
+ * pointers.  lm_head is ignored (may be NULL) when the shape ties
+ * embeddings.  The library borrows the pointers; they must outlive ctx. */
+typedef struct {
+  const void *embed;       /* [vocab][hidden] */
+  const void *lm_head;     /* [vocab][hidden] */
+  const void *final_norm;  /* [hidden] */
+  const void *const *attn_norm; /* [hidden] */
+  const void *const *wq;   /* [n_q_heads*head_dim][hidden] */
+  const void *const *wk;   /* [n_kv_heads*head_dim][hidden] */
+  const void *const *wv;   /* [n_kv_heads*head_dim][hidden] */
+  const void *const *wo;   /* [hidden][n_q_heads*head_dim] */
+  const void *const *mlp_norm;  /* [hidden] */
+  const void *const *wg;   /* [ffn][hidden] */
+  const void *const *wu;   /* [ffn][hidden] */
+  const void *const *wd;   /* [hidden][ffn] */
+} mk_weights;
+
+/* Check and record the weight pointers and enqueue their upload into the
+ * workspace's pointer table on `stream`. */
+int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
+
+#define MK_ADVANCE 1u  /* after the step: tokens[b] = next token, positions[b] += 1 */
+
+/* The hot path: one decoder forward pass for `batch` sequences.
+ * d_tokens[b] (int32) is read at position d_positions[b] (int32); the step
+ * writes keys/values of that position into d_kv_cache for every layer,
+ * attends over slots [0, positions[b]], writes fp32 logits d_logits[b][vocab]
+ * and, when d_next_tokens is not NULL, the greedy next token (smallest index
+ * among equal maxima).  With MK_ADVANCE the step also stores the next token
+ * into d_tokens and increments d_positions on the device, so steps can be
+ * enqueued back to back without the host.  Enqueued on `stream`; device-side
+ * input errors (token or position out of range) and watchdog expiries are
+ * reported by mk_get_device_error.  MK_EXEC_MEGA: exactly one kernel launch;
+ * MK_EXEC_MULTI: one launch per dependency level. */
+int mk_decode_step(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
+                   float *d_logits, int32_t *d_next_tokens, uint32_t flags, void *stream);
+
+/* Synchronise `stream`, read the device error word: MK_OK, MK_ERR_TIMEOUT or
+ * MK_ERR_INPUT.  *detail (optional) receives the instruction/ CU code.  A
+ * non-OK result poisons ctx (mk_decode_step returns MK_ERR_STATE) until
+ * mk_ctx_reset. */
+int mk_get_device_error(mk_ctx *ctx, void *stream, int32_t *detail);
+/* Zero the counters, flags and error word and restart the epoch. */
+int mk_ctx_reset(mk_ctx *ctx, void *stream);
+/* Number of decode steps enqueued since creation or the last reset. */
+int64_t mk_ctx_epoch(const mk_ctx *ctx);
+void mk_ctx_destroy(mk_ctx *ctx);
+
+const char *mk_strerror(int code);
+
+/* ------------------------------------------------------------ device facts */
+typedef struct {
+  int32_t num_cus, lds_per_block, lds_per_cu, warp_size, clock_khz, mem_clock_khz, mem_bus_bits;
+  int32_t max_threads_per_block, mega_blocks_per_cu; /* occupancy of the megakernel */
+  char arch[64];
+} mk_device_info;
+int mk_device_query(int32_t device, mk_device_info *out);
+
+/* ------------------------------------------------------------ measurement */
+/* Grid-wide barrier microbenchmark (megakernel page, section 2.6 item 3 and
+ * the executive-summary page's comparison of atomic versus sentinel grid
+ * synchronisation).  Launches n_blocks persistent workgroups that perform
+ * n_barriers grid barriers with the chosen variant:
+ *   0 cooperative-groups grid sync (cooperative launch),
+ *   1 monotonic counter, agent-scope release add + acquire poll,
+ *   2 monotonic counter, write-through data + relaxed atomics, no cache
+ *     maintenance,
+ *   3 per-block epoch flags (plain stores, one vector poll of all flags),
+ *   4 data sentinel: each block's payload word starts as a NaN pattern no
+ *     arithmetic produces and the barrier waits until every payload changed.
+ * d_scratch: device memory of at least mk_gridsync_scratch_bytes(n_blocks)
+ * bytes; d_result: device int32[4]: [0] = number of data-visibility errors
+ * seen, [1] = watchdog expiries.  Enqueued on `stream`. */
+size_t mk_gridsync_scratch_bytes(int32_t n_blocks);
+int mk_gridsync_bench(int32_t variant, int32_t n_barriers, int32_t n_blocks, void *d_scratch,
+                      int32_t *d_result, void *stream);
+
+/* Streaming-read probe: read `bytes` (multiple of 16) of d_buf with 16-byte
+ * non-temporal loads from n_blocks workgroups and write one checksum word per
+ * block to d_out (uint32[n_blocks]).  Gives the achievable HBM read rate. */
+int mk_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_blocks, void *stream);
+
+/* ------------------------------------------------------------ test hooks */
+/* Replace a plan's instruction list with `n` descriptors (fields as
+ * mk_plan_export writes them; slots, tickets and partial indices are
+ * re-derived).  Used by tests that corrupt a plan on purpose; the plan is
+ * then accepted only if mk_plan_validate passes.  Host only. */
+int mk_plan_set_instructions(mk_plan *plan, const mk_instr_desc *descs, size_t n);
+/* Shorten the device watchdog of a context (microseconds) so tests can turn a
+ * wait that cannot be met into MK_ERR_TIMEOUT quickly.  Synchronises stream. */
+int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
+/* Overwrite the host-side step counter of a context.  Setting it ahead of the
+ * device counters makes the next step's dependency waits unsatisfiable, which
+ * (with a short watchdog) exercises the MK_ERR_TIMEOUT path without a hang. */
+int mk_ctx_set_epoch(mk_ctx *ctx, int64_t epoch);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,152 @@
+// Device helpers: bf16 unpacking, wave/block reductions, device-coherent
+// loads/stores and the dependency wait/trigger protocol.
+//
+// Cross-CU data on MI355X: each of the 8 XCDs has its own L2, so data one
+// workgroup writes for another must not sit in a private L2.  Activations
+// and partials are therefore written with device-scope (sc1) stores, which
+// write through to the coherent level, and read with device-scope (sc1)
+// loads.  A producer waits for its own stores to complete before it
+// triggers an event; consumers poll the event and only then read.  This is
+// the counter protocol of the megakernel page, section 2.6 item 3 (fence,
+// then one representative thread bumps the output counter; one thread spins
+// on the input counter with a sleep, then the block synchronises), with the
+// fence replaced by completion of write-through stores so that no whole-L2
+// writeback or invalidate is needed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_program.h"
+
+#define MKD __device__ __forceinline__
+
+typedef uint32_t mk_u32x4 __attribute__((ext_vector_type(4)));
+
+#define MK_E_TIMEOUT (-7)
+#define MK_E_INPUT (-8)
+
+MKD float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+MKD float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+MKD float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// fp32 -> bf16, round to nearest even (NaN stays NaN)
+MKD uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// device-coherent accesses (sc1): visible across XCDs without cache maintenance
+MKD float ldc(const float *p) { return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stc(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD int32_t ldci(const int32_t *p) { return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stci(int32_t *p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD uint32_t ldcu(const uint32_t *p) { return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stcu(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD uint32_t addcu(uint32_t *p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// wait until this wave's outstanding memory operations (stores included) completed
+MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+MKD float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+MKD float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// sum over the workgroup; red: LDS scratch of MK_NWAVES floats
+MKD float block_sum(float v, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < MK_NWAVES; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// record the first device error and raise the abort flag every wait checks
+MKD void mk_raise(const MkProgram &P, int code, int detail) {
+  int32_t *err = P.err;
+  if (atomicCAS(err, 0, code) == 0) stci(err + 1, detail);
+  stci(err + 2, 1);
+}
+MKD bool mk_aborted(const MkProgram &P) { return ldci(P.err + 2) != 0; }
+
+// Wait for event `ev` of this step.  Counter mode: one lane polls the
+// monotonic counter until it reaches (epoch+1) * triggers.  Flag mode: one
+// wave polls all trigger flags of the event (each holds the epoch+1 of the
+// last step its producer finished).  Bounded by the watchdog; returns false
+// (uniformly) when the step is being aborted.
+MKD bool mk_wait(const MkProgram &P, const MkStep &S, int ev, int *s_flag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (P.sync_mode == 0) {
+    if (threadIdx.x == 0) {
+      const uint32_t need = (S.epoch + 1u) * (uint32_t)P.ev_count[ev];
+      int ok = 1;
+      if ((int32_t)(ldcu(P.ctr + ev) - need) < 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        uint32_t spins = 0;
+        while ((int32_t)(ldcu(P.ctr + ev) - need) < 0) {
+          __builtin_amdgcn_s_sleep(1);
+          if ((++spins & 31u) == 0) {
+            if (mk_aborted(P)) { ok = 0; break; }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)P.watchdog_ticks) {
+              mk_raise(P, MK_E_TIMEOUT, ev);
+              ok = 0;
+              break;
+            }
+          }
+        }
+      }
+      *s_flag = ok;
+    }
+  } else if (wave == 0) {
+    const uint32_t want = S.epoch + 1u;
+    const int n = P.ev_count[ev];
+    const uint32_t *f = P.flags + P.ev_flag_base[ev];
+    int ok = 1;
+    uint64_t t0 = 0;
+    uint32_t spins = 0;
+    while (true) {
+      bool mine = true;
+      for (int k = lane; k < n; k += 64) mine = mine && ((int32_t)(ldcu(f + k) - want) >= 0);
+      if (__all(mine)) break;
+      if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+      __builtin_amdgcn_s_sleep(1);
+      if ((++spins & 31u) == 0) {
+        if (mk_aborted(P)) { ok = 0; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)P.watchdog_ticks) {
+          if (lane == 0) mk_raise(P, MK_E_TIMEOUT, ev);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    if (lane == 0) *s_flag = ok;
+  }
+  __syncthreads();
+  const int ok = *s_flag;
+  __syncthreads();
+  return ok != 0;
+}
+
+// Trigger event `ev`: every wave's stores complete, then one lane bumps the
+// counter (counter mode) or stores epoch+1 into its own flag slot (flag mode).
+MKD void mk_signal(const MkProgram &P, const MkStep &S, int ev, int slot) {
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (P.sync_mode == 0)
+      addcu(P.ctr + ev, 1u);
+    else
+      stcu(P.flags + P.ev_flag_base[ev] + slot, S.epoch + 1u);
+  }
+}

@@ -1,0 +1,80 @@
+// The persistent decode megakernel, the multi-launch build of the same ops,
+// and their host-side launchers.
+//
+// Megakernel (megakernel page, section 2.1: one launch, persistent blocks,
+// dependencies in global memory, internal dispatch; section 2.6 items 1-3
+// and 5): one workgroup per CU walks its static instruction list; before an
+// instruction it waits for the instruction's input event, dispatches on the
+// (workgroup-uniform) opcode, and triggers the output event when done.
+// The multi-launch build runs one kernel per dependency level instead, so
+// kernel boundaries replace the events (the contrast the executive-summary
+// page draws between a sequence of kernels and one persistent launch).
+#include <hip/hip_runtime.h>
+
+#include "mk_launch.h"
+#include "mk_ops.h"
+
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag;
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const int cu = blockIdx.x;
+  const int i0 = P.cu_begin[cu], i1 = P.cu_begin[cu + 1];
+  for (int i = i0; i < i1; ++i) {
+    const MkInstr in = P.instr[i];
+    if (in.wait_ev >= 0 && !mk_wait(P, S, in.wait_ev, &s_flag)) return;
+    const int st = run_instr(P, S, in, smem, &s_flag);
+    if (st == MK_ST_ABORT) return;
+    if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
+    __syncthreads();
+  }
+}
+
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_level_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag;
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const int idx = P.level_list[P.level_begin[S.level] + blockIdx.x];
+  const MkInstr in = P.instr[idx];
+  run_instr(P, S, in, smem, &s_flag);
+}
+
+extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+static hipError_t set_lds(const void *fn, int lds) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
+
+int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
+  if (set_lds((const void *)mk_mega_kernel, lds) != hipSuccess) return -1;
+  hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s) {
+  if (n_blocks <= 0) return 0;
+  if (set_lds((const void *)mk_level_kernel, lds) != hipSuccess) return -1;
+  hipLaunchKernelGGL(mk_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s) {
+  if (n_words == 0) return 0;
+  size_t blocks = (n_words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(mk_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, v, n_words);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_occupancy_mega(int lds, int *blocks_per_cu) {
+  if (set_lds((const void *)mk_mega_kernel, lds) != hipSuccess) return -1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void *)mk_mega_kernel, MK_BLOCK, lds) != hipSuccess)
+    return -1;
+  *blocks_per_cu = nb;
+  return 0;
+}

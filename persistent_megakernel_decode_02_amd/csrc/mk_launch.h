@@ -1,0 +1,17 @@
+// Host launchers of the device code (internal to libmk.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mk_program.h"
+
+int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
+int mk_launch_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
+int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s);
+int mk_occupancy_mega(int lds, int *blocks_per_cu);
+
+// measurement kernels (mk_measure.hip)
+size_t mk_gridsync_scratch(int n_blocks);
+int mk_launch_gridsync(int variant, int n_barriers, int n_blocks, void *d_scratch, int32_t *d_result, hipStream_t s);
+int mk_launch_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int n_blocks, hipStream_t s);

@@ -1,0 +1,93 @@
+// Device-visible program layout shared by the host planner and the kernels.
+//
+// A plan is a set of per-CU instruction lists (megakernel page, section 2.5:
+// the host builds the lists, each compute unit runs its own; section 2.6
+// items 2, 3 and 5: opcode dispatch, dependency counters, static lists).
+// Everything the kernels need lives in one MkProgram record inside the
+// caller's workspace; per-step values travel in MkStep by value.
+#pragma once
+#include <stdint.h>
+
+#define MK_MAX_BATCH 16
+#define MK_MAX_GROUP 8     // q heads per kv head
+#define MK_BLOCK 512       // threads per workgroup (8 wave64)
+#define MK_NWAVES (MK_BLOCK / 64)
+
+enum MkOp : int32_t {
+  MKOP_QKV = 1,
+  MKOP_ATTN = 2,
+  MKOP_OPROJ = 3,
+  MKOP_GATEUP = 4,
+  MKOP_DOWN = 5,
+  MKOP_LMHEAD = 6,
+};
+
+// One instruction: 48 bytes, read with scalar loads (uniform per workgroup).
+struct MkInstr {
+  int32_t op, layer;
+  int32_t r0, r1;        // GEMV: output rows [r0, r1).  ATTN: r0 = sequence, r1 = kv head
+  int32_t split, nsplit; // ATTN: key-range split s of S
+  int32_t wait_ev;       // event waited for before starting (-1: none)
+  int32_t sig_ev;        // event triggered when done (-1: none)
+  int32_t sig_slot;      // flag slot inside sig_ev (flag mode)
+  int32_t ticket;        // ATTN: merge ticket index; LMHEAD: argmax ticket index; else -1
+  int32_t part;          // LMHEAD: slot of this instruction's argmax partial
+  int32_t level;
+};
+
+struct MkLayerW {
+  const uint16_t *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *wg, *wu, *wd;
+};
+
+struct MkProgram {
+  // model shape
+  int32_t L, H, nq, nkv, d, I, V, G;  // G = nq / nkv
+  int32_t B_max, max_ctx, S;          // S = attention splits per (sequence, kv head)
+  float eps;
+  int32_t tied;
+  int32_t sync_mode;                  // 0 counters, 1 flags
+  int32_t n_cu, n_instr, n_levels, n_events, n_lm_parts;
+  uint32_t watchdog_ticks;            // s_memrealtime ticks (100 MHz) before a wait gives up
+
+  // lists (device pointers into the workspace)
+  const MkInstr *instr;        // CU-major
+  const int32_t *cu_begin;     // [n_cu + 1]
+  const int32_t *level_begin;  // [n_levels + 1] into level_list (multi-launch)
+  const int32_t *level_list;   // instruction indices grouped by level
+  const int32_t *ev_count;     // [n_events] triggers per step
+  const int32_t *ev_flag_base; // [n_events] first flag slot
+
+  // tables and weights
+  const float *rope;           // [max_ctx][d/2][2] (cos, sin), fp32
+  MkLayerW *layers;            // [L]
+  const uint16_t *embed, *lm_head, *final_norm;
+
+  // activations (fp32), one buffer per layer so no slot is rewritten in a step
+  float *qkv;    // [L][B][(nq + 2 nkv) d]
+  float *attn;   // [L][B][nq d]
+  float *xmid;   // [L][B][H]
+  float *hbuf;   // [L][B][I]
+  float *xout;   // [L][B][H]
+  float *part;   // [L][B][nkv][S][G][d + 2]   (m, l, o[d]) per split and q head
+  float *lm_val; // [n_lm_parts][B]
+  int32_t *lm_idx;
+
+  // synchronisation
+  uint32_t *ctr;     // [n_events] monotonic counters
+  uint32_t *flags;   // [sum ev_count] epoch flags
+  uint32_t *tickets; // [n_tickets] monotonic last-arriver tickets
+  int32_t *err;      // [4]: code, detail, abort flag, spare
+};
+
+struct MkStep {
+  int32_t *tokens;
+  int32_t *positions;
+  uint16_t *kv;    // [L][2][B_max][nkv][max_ctx][d] bf16
+  float *logits;   // [B][V]
+  int32_t *next;   // [B] or null
+  int32_t batch;
+  uint32_t epoch;  // steps completed on this context before this one
+  uint32_t flags;  // MK_ADVANCE
+  int32_t multi;   // 1: launched per level (no waits/signals)
+  int32_t level;   // multi-launch: level this launch runs
+};

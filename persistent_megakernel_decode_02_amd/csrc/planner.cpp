@@ -1,0 +1,722 @@
+// Host planner, plan validator and schedule simulator.
+//
+// The megakernel page ("2 . Definition et genealogie") has the host build
+// the instruction lists (section 2.5), gives every instruction an input
+// counter, a target value and an output counter (section 2.6 item 3) and
+// runs static per-unit lists (section 2.6 item 5).  Its Q&A explains why the
+// grid must be fully resident: a block waiting on a counter that a
+// not-yet-resident block must bump never finishes.  The planner therefore
+// orders every CU's list by dependency level; under co-residency this is
+// deadlock-free by induction on the level, and mk_plan_check verifies it
+// together with read-after-write coverage of every activation slice.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <random>
+
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Events {
+  int L, nkv;
+  int per() const { return nkv + 4; }
+  int qkv(int l, int g) const { return l * per() + g; }
+  int attn(int l) const { return l * per() + nkv; }
+  int o(int l) const { return l * per() + nkv + 1; }
+  int gu(int l) const { return l * per() + nkv + 2; }
+  int down(int l) const { return l * per() + nkv + 3; }
+  int count() const { return L * per(); }
+};
+
+enum { LV_QKV = 0, LV_ATTN = 1, LV_O = 2, LV_GU = 3, LV_DOWN = 4, LV_PER_LAYER = 5 };
+
+struct Pending {
+  MkInstr in;
+  double bytes;
+};
+
+}  // namespace
+
+static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
+  if (!s || !o) return MK_ERR_INVALID_ARG;
+  if (s->n_layers < 1 || s->hidden < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->ffn < 1 ||
+      s->vocab < 1)
+    return MK_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return MK_ERR_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads) return MK_ERR_SHAPE;
+  if (s->n_q_heads / s->n_kv_heads > MK_MAX_GROUP) return MK_ERR_SHAPE;
+  if (s->hidden % 256 || s->ffn % 256 || (s->n_q_heads * s->head_dim) % 256) return MK_ERR_SHAPE;
+  if (!(s->rms_eps > 0) || !(s->rope_theta > 1)) return MK_ERR_SHAPE;
+  if (o->max_batch < 1 || o->max_batch > MK_MAX_BATCH) return MK_ERR_INVALID_ARG;
+  if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
+  if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
+  if (o->sync_mode != MK_SYNC_COUNTER && o->sync_mode != MK_SYNC_FLAG) return MK_ERR_INVALID_ARG;
+  if (o->exec_mode != MK_EXEC_MEGA && o->exec_mode != MK_EXEC_MULTI) return MK_ERR_INVALID_ARG;
+  return MK_OK;
+}
+
+static int lds_requirement(const mk_plan *p) {
+  const mk_model_shape &s = p->shape;
+  const int B = p->B, d = s.head_dim, G = p->G;
+  int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * d, (int64_t)s.ffn});
+  // GEMV ops stage one sequence's input vector at a time
+  int64_t gemv = kmax * 4 + (int64_t)MK_NWAVES * 16 + 256;
+  (void)B;
+  int64_t chunk = ceil_div(p->max_ctx, p->S);
+  int64_t attn = (int64_t)G * d * 4 + 2 * d * 4 + 2 * d * 2 + (int64_t)G * chunk * 4 + MK_BLOCK * 4 +
+                 (int64_t)G * 16 + 256;
+  return (int)std::max(gemv, attn);
+}
+
+void mk_plan_finalize_lists(mk_plan *p) {
+  // stable sort instructions by (cu, slot order as given), recompute cu_begin and level lists
+  const int n = (int)p->instr.size();
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return p->instr_cu[a] < p->instr_cu[b]; });
+  std::vector<MkInstr> in2(n);
+  std::vector<int32_t> cu2(n);
+  for (int i = 0; i < n; ++i) {
+    in2[i] = p->instr[order[i]];
+    cu2[i] = p->instr_cu[order[i]];
+  }
+  p->instr.swap(in2);
+  p->instr_cu.swap(cu2);
+  p->cu_begin.assign(p->n_cu + 1, 0);
+  for (int i = 0; i < n; ++i) p->cu_begin[p->instr_cu[i] + 1]++;
+  for (int c = 0; c < p->n_cu; ++c) p->cu_begin[c + 1] += p->cu_begin[c];
+  p->level_begin.assign(p->n_levels + 1, 0);
+  for (int i = 0; i < n; ++i) {
+    int lv = p->instr[i].level;
+    if (lv >= 0 && lv < p->n_levels) p->level_begin[lv + 1]++;
+  }
+  for (int l = 0; l < p->n_levels; ++l) p->level_begin[l + 1] += p->level_begin[l];
+  p->level_list.assign(n, 0);
+  std::vector<int32_t> fill(p->level_begin.begin(), p->level_begin.end() - 1);
+  for (int i = 0; i < n; ++i) {
+    int lv = p->instr[i].level;
+    if (lv >= 0 && lv < p->n_levels) p->level_list[fill[lv]++] = i;
+  }
+}
+
+void mk_plan_compute_layout(mk_plan *p) {
+  const mk_model_shape &s = p->shape;
+  const size_t L = s.n_layers, B = p->B, H = s.hidden, d = s.head_dim, nq = s.n_q_heads,
+               nkv = s.n_kv_heads, I = s.ffn, R = (nq + 2 * nkv) * d;
+  MkLayout &y = p->lay;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  y.prog = take(sizeof(MkProgram));
+  y.instr = take(sizeof(MkInstr) * std::max<size_t>(p->instr.size(), 1));
+  y.cu_begin = take(4 * (p->n_cu + 1));
+  y.level_begin = take(4 * (p->n_levels + 1));
+  y.level_list = take(4 * std::max<size_t>(p->instr.size(), 1));
+  y.ev_count = take(4 * std::max(p->n_events, 1));
+  y.ev_flag_base = take(4 * std::max(p->n_events, 1));
+  y.rope = take(4 * (size_t)p->max_ctx * d);
+  y.layers = take(sizeof(MkLayerW) * L);
+  y.qkv = take(4 * L * B * R);
+  y.attn = take(4 * L * B * nq * d);
+  y.xmid = take(4 * L * B * H);
+  y.hbuf = take(4 * L * B * I);
+  y.xout = take(4 * L * B * H);
+  y.part = take(4 * L * B * nkv * p->S * p->G * (d + 2));
+  y.lm_val = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
+  y.lm_idx = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
+  y.sync_begin = o;
+  y.ctr = take(4 * std::max(p->n_events, 1));
+  y.flags = take(4 * std::max(p->n_flags, 1));
+  y.tickets = take(4 * std::max(p->n_tickets, 1));
+  y.err = take(16);
+  y.sync_end = o;
+  y.total = o;
+}
+
+int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan **out) {
+  if (!out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = check_shape(shape, opts);
+  if (rc) return rc;
+  if (n_cu < 1 || n_cu > 4096) return MK_ERR_INVALID_ARG;
+
+  mk_plan *p = new (std::nothrow) mk_plan();
+  if (!p) return MK_ERR_INVALID_ARG;
+  p->shape = *shape;
+  p->opts = *opts;
+  p->n_cu = n_cu;
+  p->B = opts->max_batch;
+  p->max_ctx = opts->max_ctx;
+  const mk_model_shape &s = *shape;
+  const int L = s.n_layers, H = s.hidden, d = s.head_dim, nq = s.n_q_heads, nkv = s.n_kv_heads,
+            I = s.ffn, V = s.vocab, B = p->B;
+  p->G = nq / nkv;
+  const int R = (nq + 2 * nkv) * d;
+
+  // attention splits: enough key-range pieces to keep one split's scores in
+  // LDS (<= 1024 positions) and, when contexts are long, to spread the key
+  // stream over the CUs
+  int S = opts->kv_splits;
+  if (S == 0) {
+    int64_t s1 = ceil_div(p->max_ctx, 256);
+    int64_t cap = std::max<int64_t>(1, n_cu / (B * nkv));
+    S = (int)std::min(s1, cap);
+    S = (int)std::max<int64_t>(S, ceil_div(p->max_ctx, 1024));
+    S = std::max(S, 1);
+  }
+  if (ceil_div(p->max_ctx, S) > 1024) {
+    delete p;
+    return MK_ERR_UNSUPPORTED;
+  }
+  p->S = S;
+
+  Events ev{L, nkv};
+  p->n_events = ev.count();
+  p->n_levels = LV_PER_LAYER * L + 1;
+
+  // rows per instruction
+  int rq = d;
+  while (rq > 8 && (R / (rq / 2)) <= n_cu) rq /= 2;
+  const int ro = (int)ceil_div(H, n_cu), rg = (int)ceil_div(I, n_cu), rd = (int)ceil_div(H, n_cu),
+            rl = (int)ceil_div(V, n_cu);
+  p->n_lm_parts = (int)ceil_div(V, rl);
+  p->n_tickets = (S > 1 ? L * B * nkv : 0) + 1;
+  const int lm_ticket = p->n_tickets - 1;
+
+  // event trigger counts and flag slots
+  p->ev_count.assign(p->n_events, 0);
+  auto blank = [](int op, int layer, int level) {
+    MkInstr in;
+    std::memset(&in, 0, sizeof in);
+    in.op = op;
+    in.layer = layer;
+    in.level = level;
+    in.wait_ev = -1;
+    in.sig_ev = -1;
+    in.sig_slot = 0;
+    in.ticket = -1;
+    in.part = -1;
+    in.nsplit = 1;
+    return in;
+  };
+
+  std::vector<double> load(n_cu, 0.0);
+  auto assign = [&](std::vector<Pending> &lvl) {
+    // spread a level evenly (each CU gets floor or ceil of n / n_cu slices);
+    // the CUs with the least bytes so far take the first and largest slices
+    std::stable_sort(lvl.begin(), lvl.end(), [](const Pending &a, const Pending &b) { return a.bytes > b.bytes; });
+    std::vector<int> order(n_cu);
+    for (int c = 0; c < n_cu; ++c) order[c] = c;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return load[a] < load[b]; });
+    for (size_t k = 0; k < lvl.size(); ++k) {
+      const int c = order[k % n_cu];
+      p->instr.push_back(lvl[k].in);
+      p->instr_cu.push_back(c);
+      load[c] += lvl[k].bytes;
+    }
+    lvl.clear();
+  };
+
+  double wbytes = 0;
+  std::vector<Pending> lvl;
+  for (int l = 0; l < L; ++l) {
+    const int base = l * LV_PER_LAYER;
+    // QKV row slices (each inside one head, hence one kv group)
+    {
+      std::vector<int> slot(nkv, 0);
+      for (int r0 = 0; r0 < R; r0 += rq) {
+        MkInstr in = blank(MKOP_QKV, l, base + LV_QKV);
+        in.r0 = r0;
+        in.r1 = std::min(R, r0 + rq);
+        int g;
+        if (r0 < nq * d)
+          g = (r0 / d) / p->G;
+        else if (r0 < (nq + nkv) * d)
+          g = (r0 - nq * d) / d;
+        else
+          g = (r0 - (nq + nkv) * d) / d;
+        in.wait_ev = l > 0 ? ev.down(l - 1) : -1;
+        in.sig_ev = ev.qkv(l, g);
+        in.sig_slot = slot[g]++;
+        p->ev_count[in.sig_ev]++;
+        lvl.push_back({in, 2.0 * (in.r1 - in.r0) * H});
+        wbytes += 2.0 * (in.r1 - in.r0) * H;
+      }
+      assign(lvl);
+    }
+    // attention splits
+    {
+      for (int b = 0; b < B; ++b)
+        for (int g = 0; g < nkv; ++g)
+          for (int sp = 0; sp < S; ++sp) {
+            MkInstr in = blank(MKOP_ATTN, l, base + LV_ATTN);
+            in.r0 = b;
+            in.r1 = g;
+            in.split = sp;
+            in.nsplit = S;
+            in.wait_ev = ev.qkv(l, g);
+            in.sig_ev = ev.attn(l);
+            in.sig_slot = b * nkv + g;
+            in.ticket = S > 1 ? (l * B + b) * nkv + g : -1;
+            lvl.push_back({in, 4.0 * d * (double)ceil_div(p->max_ctx, S)});
+          }
+      p->ev_count[ev.attn(l)] = B * nkv;
+      assign(lvl);
+    }
+    // O projection + residual
+    {
+      int k = 0;
+      for (int r0 = 0; r0 < H; r0 += ro, ++k) {
+        MkInstr in = blank(MKOP_OPROJ, l, base + LV_O);
+        in.r0 = r0;
+        in.r1 = std::min(H, r0 + ro);
+        in.wait_ev = ev.attn(l);
+        in.sig_ev = ev.o(l);
+        in.sig_slot = k;
+        p->ev_count[in.sig_ev]++;
+        lvl.push_back({in, 2.0 * (in.r1 - in.r0) * nq * d});
+        wbytes += 2.0 * (in.r1 - in.r0) * nq * d;
+      }
+      assign(lvl);
+    }
+    // gate/up + SiLU (RMSNorm prologue)
+    {
+      int k = 0;
+      for (int r0 = 0; r0 < I; r0 += rg, ++k) {
+        MkInstr in = blank(MKOP_GATEUP, l, base + LV_GU);
+        in.r0 = r0;
+        in.r1 = std::min(I, r0 + rg);
+        in.wait_ev = ev.o(l);
+        in.sig_ev = ev.gu(l);
+        in.sig_slot = k;
+        p->ev_count[in.sig_ev]++;
+        lvl.push_back({in, 4.0 * (in.r1 - in.r0) * H});
+        wbytes += 4.0 * (in.r1 - in.r0) * H;
+      }
+      assign(lvl);
+    }
+    // down projection + residual
+    {
+      int k = 0;
+      for (int r0 = 0; r0 < H; r0 += rd, ++k) {
+        MkInstr in = blank(MKOP_DOWN, l, base + LV_DOWN);
+        in.r0 = r0;
+        in.r1 = std::min(H, r0 + rd);
+        in.wait_ev = ev.gu(l);
+        in.sig_ev = ev.down(l);
+        in.sig_slot = k;
+        p->ev_count[in.sig_ev]++;
+        lvl.push_back({in, 2.0 * (in.r1 - in.r0) * I});
+        wbytes += 2.0 * (in.r1 - in.r0) * I;
+      }
+      assign(lvl);
+    }
+    wbytes += 4.0 * H;  // two norm gains
+  }
+  // LM head + argmax
+  {
+    int k = 0;
+    for (int r0 = 0; r0 < V; r0 += rl, ++k) {
+      MkInstr in = blank(MKOP_LMHEAD, L, LV_PER_LAYER * L);
+      in.r0 = r0;
+      in.r1 = std::min(V, r0 + rl);
+      in.wait_ev = ev.down(L - 1);
+      in.ticket = lm_ticket;
+      in.part = k;
+      lvl.push_back({in, 2.0 * (in.r1 - in.r0) * H});
+      wbytes += 2.0 * (in.r1 - in.r0) * H;
+    }
+    assign(lvl);
+    wbytes += 2.0 * H;  // final norm gain
+  }
+  p->weight_bytes = wbytes;
+
+  // flag slots
+  p->ev_flag_base.assign(p->n_events, 0);
+  int acc = 0;
+  for (int e = 0; e < p->n_events; ++e) {
+    p->ev_flag_base[e] = acc;
+    acc += p->ev_count[e];
+  }
+  p->n_flags = acc;
+
+  // per-CU lists in level order (stable)
+  {
+    const int n = (int)p->instr.size();
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      if (p->instr_cu[a] != p->instr_cu[b]) return p->instr_cu[a] < p->instr_cu[b];
+      return p->instr[a].level < p->instr[b].level;
+    });
+    std::vector<MkInstr> in2(n);
+    std::vector<int32_t> cu2(n);
+    for (int i = 0; i < n; ++i) {
+      in2[i] = p->instr[order[i]];
+      cu2[i] = p->instr_cu[order[i]];
+    }
+    p->instr.swap(in2);
+    p->instr_cu.swap(cu2);
+  }
+  mk_plan_finalize_lists(p);
+  p->lds_bytes = lds_requirement(p);
+  if (p->lds_bytes > 160 * 1024) {
+    delete p;
+    return MK_ERR_UNSUPPORTED;
+  }
+  mk_plan_compute_layout(p);
+  rc = mk_plan_check(p, false, 0, 0);
+  if (rc) {
+    delete p;
+    return rc;
+  }
+  p->validated = true;
+  *out = p;
+  return MK_OK;
+}
+
+// ------------------------------------------------------------------ checks
+
+namespace {
+
+enum BufKind { BK_XOUT = 0, BK_QKV = 1, BK_ATTN = 2, BK_XMID = 3, BK_H = 4, BK_N = 5 };
+
+struct Access {
+  int buf;  // kind * L + layer
+  int64_t lo, hi;
+};
+
+struct Checker {
+  const mk_plan *p;
+  int L, H, d, nq, nkv, I, V, R, B, G, S;
+  explicit Checker(const mk_plan *pp) : p(pp) {
+    const mk_model_shape &s = p->shape;
+    L = s.n_layers;
+    H = s.hidden;
+    d = s.head_dim;
+    nq = s.n_q_heads;
+    nkv = s.n_kv_heads;
+    I = s.ffn;
+    V = s.vocab;
+    R = (nq + 2 * nkv) * d;
+    B = p->B;
+    G = p->G;
+    S = p->S;
+  }
+  int buf(int kind, int layer) const { return kind * L + layer; }
+
+  void accesses(const MkInstr &in, std::vector<Access> &rd, std::vector<Access> &wr) const {
+    rd.clear();
+    wr.clear();
+    const int l = in.layer;
+    switch (in.op) {
+      case MKOP_QKV:
+        if (l > 0) rd.push_back({buf(BK_XOUT, l - 1), 0, (int64_t)B * H});
+        for (int b = 0; b < B; ++b) wr.push_back({buf(BK_QKV, l), (int64_t)b * R + in.r0, (int64_t)b * R + in.r1});
+        break;
+      case MKOP_ATTN: {
+        const int b = in.r0, g = in.r1;
+        const int64_t o = (int64_t)b * R;
+        rd.push_back({buf(BK_QKV, l), o + (int64_t)g * G * d, o + (int64_t)(g + 1) * G * d});
+        rd.push_back({buf(BK_QKV, l), o + (int64_t)nq * d + g * d, o + (int64_t)nq * d + (g + 1) * d});
+        rd.push_back({buf(BK_QKV, l), o + (int64_t)(nq + nkv) * d + g * d, o + (int64_t)(nq + nkv) * d + (g + 1) * d});
+        const int64_t a = (int64_t)b * nq * d + (int64_t)g * G * d;
+        wr.push_back({buf(BK_ATTN, l), a, a + (int64_t)G * d});
+        break;
+      }
+      case MKOP_OPROJ:
+        rd.push_back({buf(BK_ATTN, l), 0, (int64_t)B * nq * d});
+        for (int b = 0; b < B; ++b) {
+          if (l > 0) rd.push_back({buf(BK_XOUT, l - 1), (int64_t)b * H + in.r0, (int64_t)b * H + in.r1});
+          wr.push_back({buf(BK_XMID, l), (int64_t)b * H + in.r0, (int64_t)b * H + in.r1});
+        }
+        break;
+      case MKOP_GATEUP:
+        rd.push_back({buf(BK_XMID, l), 0, (int64_t)B * H});
+        for (int b = 0; b < B; ++b) wr.push_back({buf(BK_H, l), (int64_t)b * I + in.r0, (int64_t)b * I + in.r1});
+        break;
+      case MKOP_DOWN:
+        rd.push_back({buf(BK_H, l), 0, (int64_t)B * I});
+        for (int b = 0; b < B; ++b) {
+          rd.push_back({buf(BK_XMID, l), (int64_t)b * H + in.r0, (int64_t)b * H + in.r1});
+          wr.push_back({buf(BK_XOUT, l), (int64_t)b * H + in.r0, (int64_t)b * H + in.r1});
+        }
+        break;
+      case MKOP_LMHEAD:
+        rd.push_back({buf(BK_XOUT, L - 1), 0, (int64_t)B * H});
+        break;
+      default:
+        break;
+    }
+  }
+};
+
+struct Writer {
+  int64_t lo, hi;
+  int instr;
+};
+
+}  // namespace
+
+int mk_plan_check(const mk_plan *p, bool simulate, int trials, uint64_t seed) {
+  if (!p) return MK_ERR_INVALID_ARG;
+  Checker ck(p);
+  const int n = (int)p->instr.size();
+  const int L = ck.L;
+  Events ev{L, ck.nkv};
+  if ((int)p->instr_cu.size() != n) return MK_ERR_PLAN;
+  if ((int)p->cu_begin.size() != p->n_cu + 1 || p->cu_begin[p->n_cu] != n) return MK_ERR_PLAN;
+  if (p->n_events != ev.count()) return MK_ERR_PLAN;
+
+  // 1. structure: fields in range, lists level-sorted
+  for (int i = 0; i < n; ++i) {
+    const MkInstr &in = p->instr[i];
+    if (p->instr_cu[i] < 0 || p->instr_cu[i] >= p->n_cu) return MK_ERR_PLAN;
+    if (in.level < 0 || in.level >= p->n_levels) return MK_ERR_PLAN;
+    if (in.wait_ev < -1 || in.wait_ev >= p->n_events) return MK_ERR_PLAN;
+    if (in.sig_ev < -1 || in.sig_ev >= p->n_events) return MK_ERR_PLAN;
+    if (in.sig_ev >= 0 && (in.sig_slot < 0 || in.sig_slot >= p->ev_count[in.sig_ev])) return MK_ERR_PLAN;
+    if (in.ticket < -1 || in.ticket >= p->n_tickets) return MK_ERR_PLAN;
+    const int l = in.layer;
+    switch (in.op) {
+      case MKOP_QKV:
+        if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.R || in.r0 >= in.r1) return MK_ERR_PLAN;
+        break;
+      case MKOP_ATTN:
+        if (l < 0 || l >= L || in.r0 < 0 || in.r0 >= ck.B || in.r1 < 0 || in.r1 >= ck.nkv) return MK_ERR_PLAN;
+        if (in.nsplit != p->S || in.split < 0 || in.split >= in.nsplit) return MK_ERR_PLAN;
+        if ((p->S > 1) != (in.ticket >= 0)) return MK_ERR_PLAN;
+        break;
+      case MKOP_OPROJ:
+      case MKOP_DOWN:
+        if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.H || in.r0 >= in.r1) return MK_ERR_PLAN;
+        break;
+      case MKOP_GATEUP:
+        if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.I || in.r0 >= in.r1) return MK_ERR_PLAN;
+        break;
+      case MKOP_LMHEAD:
+        if (in.r0 < 0 || in.r1 > ck.V || in.r0 >= in.r1 || in.ticket < 0) return MK_ERR_PLAN;
+        if (in.part < 0 || in.part >= p->n_lm_parts) return MK_ERR_PLAN;
+        break;
+      default:
+        return MK_ERR_PLAN;
+    }
+  }
+  for (int c = 0; c < p->n_cu; ++c)
+    for (int i = p->cu_begin[c] + 1; i < p->cu_begin[c + 1]; ++i)
+      if (p->instr[i].level < p->instr[i - 1].level) return MK_ERR_PLAN;
+
+  // 2. events: trigger counts match, flag slots distinct, triggers strictly
+  //    below every waiter's level (otherwise a wait could never be met)
+  std::vector<int> trig(p->n_events, 0), min_wait(p->n_events, 1 << 30), max_trig(p->n_events, -1);
+  std::vector<std::vector<char>> slot_used(p->n_events);
+  for (int e = 0; e < p->n_events; ++e) slot_used[e].assign(std::max(p->ev_count[e], 1), 0);
+  std::vector<int> attn_units(p->n_events, 0);
+  for (int i = 0; i < n; ++i) {
+    const MkInstr &in = p->instr[i];
+    if (in.wait_ev >= 0) min_wait[in.wait_ev] = std::min(min_wait[in.wait_ev], in.level);
+    if (in.sig_ev >= 0) {
+      max_trig[in.sig_ev] = std::max(max_trig[in.sig_ev], in.level);
+      if (in.op == MKOP_ATTN) {
+        if (in.split == 0) attn_units[in.sig_ev]++;  // one trigger per (sequence, kv head)
+      } else {
+        if (slot_used[in.sig_ev][in.sig_slot]) return MK_ERR_PLAN;
+        slot_used[in.sig_ev][in.sig_slot] = 1;
+        trig[in.sig_ev]++;
+      }
+    }
+  }
+  for (int e = 0; e < p->n_events; ++e) {
+    int t = trig[e] + attn_units[e];
+    if (t != p->ev_count[e]) return MK_ERR_PLAN;
+    if (min_wait[e] < (1 << 30) && max_trig[e] >= min_wait[e]) return MK_ERR_PLAN;
+    if (min_wait[e] < (1 << 30) && t == 0) return MK_ERR_PLAN;
+  }
+  // every attention unit has all S splits
+  {
+    std::vector<int> cnt((size_t)L * ck.B * ck.nkv, 0);
+    for (int i = 0; i < n; ++i) {
+      const MkInstr &in = p->instr[i];
+      if (in.op == MKOP_ATTN) cnt[((size_t)in.layer * ck.B + in.r0) * ck.nkv + in.r1] |= (1 << std::min(in.split, 30));
+    }
+    int full = p->S >= 31 ? -1 : (1 << p->S) - 1;
+    if (p->S < 31)
+      for (int v : cnt)
+        if (v != full) return MK_ERR_PLAN;
+  }
+
+  // 3. writes: every output slice written exactly once per step
+  std::vector<std::vector<Writer>> writers(BK_N * L);
+  std::vector<Access> rd, wr;
+  for (int i = 0; i < n; ++i) {
+    ck.accesses(p->instr[i], rd, wr);
+    for (auto &a : wr) writers[a.buf].push_back({a.lo, a.hi, i});
+  }
+  for (int k = 0; k < BK_N; ++k)
+    for (int l = 0; l < L; ++l) {
+      auto &w = writers[k * L + l];
+      std::sort(w.begin(), w.end(), [](const Writer &a, const Writer &b) {
+        return a.lo != b.lo ? a.lo < b.lo : a.instr < b.instr;
+      });
+      int64_t size = 0;
+      switch (k) {
+        case BK_XOUT: size = (int64_t)ck.B * ck.H; break;
+        case BK_QKV: size = (int64_t)ck.B * ck.R; break;
+        case BK_ATTN: size = (int64_t)ck.B * ck.nq * ck.d; break;
+        case BK_XMID: size = (int64_t)ck.B * ck.H; break;
+        case BK_H: size = (int64_t)ck.B * ck.I; break;
+      }
+      int64_t covered = 0;
+      for (size_t j = 0; j < w.size(); ++j) {
+        if (k == BK_ATTN) {  // all splits of one unit share the unit's slice
+          if (w[j].lo < covered && !(j > 0 && w[j].lo == w[j - 1].lo && w[j].hi == w[j - 1].hi)) return MK_ERR_PLAN;
+          covered = std::max(covered, w[j].hi);
+          continue;
+        }
+        if (w[j].lo != covered) return MK_ERR_PLAN;  // gap or overlap
+        covered = w[j].hi;
+      }
+      if (covered != size) return MK_ERR_PLAN;
+    }
+  // LM rows covered exactly once
+  {
+    std::vector<std::pair<int, int>> lm;
+    for (int i = 0; i < n; ++i)
+      if (p->instr[i].op == MKOP_LMHEAD) lm.push_back({p->instr[i].r0, p->instr[i].r1});
+    std::sort(lm.begin(), lm.end());
+    int c = 0;
+    for (auto &r : lm) {
+      if (r.first != c) return MK_ERR_PLAN;
+      c = r.second;
+    }
+    if (c != ck.V) return MK_ERR_PLAN;
+  }
+
+  // 4. read-after-write: every writer of a slice an instruction reads
+  //    happens-before it (program order on a CU + event edges)
+  std::vector<int> topo(n);
+  for (int i = 0; i < n; ++i) topo[i] = i;
+  std::stable_sort(topo.begin(), topo.end(), [&](int a, int b) {
+    if (p->instr[a].level != p->instr[b].level) return p->instr[a].level < p->instr[b].level;
+    return a < b;
+  });
+  const size_t words = ((size_t)n + 63) / 64;
+  std::vector<uint64_t> anc((size_t)n * words, 0), evanc((size_t)p->n_events * words, 0);
+  std::vector<int> prev_on_cu(n, -1);
+  for (int c = 0; c < p->n_cu; ++c)
+    for (int i = p->cu_begin[c] + 1; i < p->cu_begin[c + 1]; ++i) prev_on_cu[i] = i - 1;
+  // process level by level: event ancestor sets of a level are complete before
+  // any waiter (strictly higher level) reads them
+  size_t t = 0;
+  while (t < topo.size()) {
+    const int lv = p->instr[topo[t]].level;
+    size_t t1 = t;
+    while (t1 < topo.size() && p->instr[topo[t1]].level == lv) ++t1;
+    // within a level, program order predecessors may be in the same level:
+    // visit in CU-list order (index order) which topo preserves
+    for (size_t k = t; k < t1; ++k) {
+      int i = topo[k];
+      uint64_t *a = &anc[(size_t)i * words];
+      int pr = prev_on_cu[i];
+      if (pr >= 0) {
+        const uint64_t *b = &anc[(size_t)pr * words];
+        for (size_t w = 0; w < words; ++w) a[w] |= b[w];
+        a[pr / 64] |= 1ull << (pr % 64);
+      }
+      int e = p->instr[i].wait_ev;
+      if (e >= 0) {
+        const uint64_t *b = &evanc[(size_t)e * words];
+        for (size_t w = 0; w < words; ++w) a[w] |= b[w];
+      }
+    }
+    for (size_t k = t; k < t1; ++k) {
+      int i = topo[k];
+      int e = p->instr[i].sig_ev;
+      if (e >= 0) {
+        uint64_t *b = &evanc[(size_t)e * words];
+        const uint64_t *a = &anc[(size_t)i * words];
+        for (size_t w = 0; w < words; ++w) b[w] |= a[w];
+        b[i / 64] |= 1ull << (i % 64);
+      }
+    }
+    t = t1;
+  }
+  std::vector<std::vector<int>> producers(simulate ? n : 0);
+  for (int i = 0; i < n; ++i) {
+    ck.accesses(p->instr[i], rd, wr);
+    const uint64_t *a = &anc[(size_t)i * words];
+    for (auto &r : rd) {
+      auto &w = writers[r.buf];
+      // writers sorted by lo; scan those overlapping [r.lo, r.hi)
+      auto it = std::lower_bound(w.begin(), w.end(), r.lo, [](const Writer &x, int64_t v) { return x.hi <= v; });
+      // lower_bound on hi requires hi sorted, which holds for disjoint slices and
+      // for the shared attention slices (equal ranges are adjacent)
+      for (; it != w.end() && it->lo < r.hi; ++it) {
+        if (it->hi <= r.lo) continue;
+        int wi = it->instr;
+        if (!((a[wi / 64] >> (wi % 64)) & 1)) return MK_ERR_PLAN;
+        if (simulate) producers[i].push_back(wi);
+      }
+    }
+  }
+
+  // 5. optional: random interleavings of the lists with counters, tickets and
+  //    producer checks, no arithmetic
+  if (simulate) {
+    std::mt19937_64 rng(seed);
+    for (int tr = 0; tr < trials; ++tr) {
+      std::vector<int> pc(p->n_cu), ctr(p->n_events, 0), tick(std::max(p->n_tickets, 1), 0);
+      std::vector<char> done(n, 0);
+      std::vector<std::vector<int>> waiting(p->n_events);
+      std::vector<int> ready;
+      for (int c = 0; c < p->n_cu; ++c) pc[c] = p->cu_begin[c];
+      auto park_or_ready = [&](int c) {
+        if (pc[c] >= p->cu_begin[c + 1]) return;
+        const MkInstr &in = p->instr[pc[c]];
+        if (in.wait_ev < 0 || ctr[in.wait_ev] >= p->ev_count[in.wait_ev])
+          ready.push_back(c);
+        else
+          waiting[in.wait_ev].push_back(c);
+      };
+      for (int c = 0; c < p->n_cu; ++c) park_or_ready(c);
+      int executed = 0;
+      while (!ready.empty()) {
+        size_t k = rng() % ready.size();
+        int c = ready[k];
+        ready[k] = ready.back();
+        ready.pop_back();
+        int i = pc[c];
+        for (int pi : producers[i])
+          if (!done[pi]) return MK_ERR_PLAN;
+        done[i] = 1;
+        ++executed;
+        const MkInstr &in = p->instr[i];
+        int fire = -1;
+        if (in.op == MKOP_ATTN && in.ticket >= 0) {
+          if (++tick[in.ticket] == p->S) fire = in.sig_ev;
+        } else {
+          fire = in.sig_ev;
+        }
+        if (fire >= 0) {
+          if (++ctr[fire] == p->ev_count[fire]) {
+            for (int wc : waiting[fire]) ready.push_back(wc);
+            waiting[fire].clear();
+          }
+        }
+        pc[c]++;
+        park_or_ready(c);
+      }
+      if (executed != n) return MK_ERR_PLAN;  // some CU never got past a wait: deadlock
+    }
+  }
+  return MK_OK;
+}

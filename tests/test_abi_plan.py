@@ -1,0 +1,202 @@
+"""Host-side checks of libmk.so (no GPU): every symbol include/mk.h declares
+is exported, the planner builds valid plans for all workload shapes and CU
+counts, the validator and the schedule simulator accept them, and they
+reject plans corrupted on purpose (missing wait, wrong event, broken level
+order, dropped instruction)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import synth_inputs as si
+from persistent_megakernel_decode_02_amd import mk
+from persistent_megakernel_decode_02_amd.engine import plan_opts, shape_struct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "mk.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = mk.load_library()
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in mk.SIGNATURES, n
+    assert set(mk.SIGNATURES) == set(names)
+
+
+def test_strerror_texts():
+    for code in range(0, -12, -1):
+        assert mk.mk_strerror(code) != "unknown error"
+    assert mk.mk_strerror(-99) == "unknown error"
+
+
+SHAPES = {k: (wl.shape, wl.batch, wl.max_ctx) for k, wl in si.WORKLOADS.items()}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("n_cu", [8, 80, 256, 304])
+def test_plan_builds_and_validates(name, n_cu):
+    shape, batch, max_ctx = SHAPES[name]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=n_cu))
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        info = mk.mk_plan_get_info(plan)
+        assert info.num_cus == n_cu and info.n_levels == 5 * shape.n_layers + 1
+        assert info.lds_bytes <= 160 * 1024
+        descs = mk.mk_plan_export(plan)
+        assert len(descs) == info.n_instructions
+        # lists are level-sorted per CU and every CU index is in range
+        last = {}
+        for d in descs:
+            assert 0 <= d.cu < n_cu
+            assert d.level >= last.get(d.cu, -1)
+            last[d.cu] = d.level
+        # weights streamed once per pass: matches the parameter count
+        d, L, H = shape.head_dim, shape.n_layers, shape.hidden
+        P = L * (H * (shape.n_q_heads + 2 * shape.n_kv_heads) * d + shape.n_q_heads * d * H + 3 * H * shape.ffn
+                 + 2 * H) + shape.vocab * H + H
+        assert info.weight_bytes == 2 * P
+        if n_cu <= 80 or name == "tiny":
+            assert mk.mk_plan_simulate(plan, 20, 1) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_plan_llama1b_one_gemv_slice_per_cu():
+    shape, batch, max_ctx = SHAPES["llama1b_pos1024"]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256))
+    try:
+        descs = mk.mk_plan_export(plan)
+        for op in (mk.MK_OP_OPROJ, mk.MK_OP_GATEUP, mk.MK_OP_DOWN, mk.MK_OP_LMHEAD):
+            cus = [d.cu for d in descs if d.op == op and d.layer in (0, shape.n_layers)]
+            assert len(cus) == 256 and len(set(cus)) == 256
+        assert mk.mk_plan_simulate(plan, 3, 7) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def _tiny_plan(n_cu=8, **kw):
+    shape, batch, max_ctx = SHAPES["tiny"]
+    return mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=n_cu, **kw))
+
+
+def _mutated(mutate):
+    plan = _tiny_plan()
+    descs = mk.mk_plan_export(plan)
+    mutate(descs)
+    assert mk.mk_plan_set_instructions(plan, descs) == mk.MK_OK
+    return plan
+
+
+def test_unmodified_roundtrip_stays_valid():
+    plan = _mutated(lambda d: None)
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        assert mk.mk_plan_simulate(plan, 200, 3) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_missing_wait_is_a_race():
+    def m(descs):
+        for d in descs:
+            if d.op == mk.MK_OP_GATEUP and d.layer == 1:
+                d.wait_event = -1
+                return
+    plan = _mutated(m)
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+        assert mk.mk_plan_simulate(plan, 5, 1) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_wait_on_wrong_event_is_rejected():
+    def m(descs):
+        for d in descs:
+            if d.op == mk.MK_OP_DOWN and d.layer == 0:
+                # wait for the O-projection instead of gate/up: reads h too early
+                d.wait_event = d.wait_event - 1
+                return
+    plan = _mutated(m)
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_level_order_violation_is_rejected():
+    def m(descs):
+        # put a layer-1 QKV slice at the head of a CU list
+        for d in descs:
+            if d.op == mk.MK_OP_QKV and d.layer == 1:
+                d.slot = -1
+                return
+    plan = _mutated(m)
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_dropped_instruction_is_rejected():
+    plan = _tiny_plan()
+    try:
+        descs = mk.mk_plan_export(plan)
+        idx = next(i for i, d in enumerate(descs) if d.op == mk.MK_OP_OPROJ)
+        del descs[idx]
+        assert mk.mk_plan_set_instructions(plan, descs) == mk.MK_OK
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_trigger_in_wrong_event_is_rejected():
+    def m(descs):
+        for d in descs:
+            if d.op == mk.MK_OP_OPROJ and d.layer == 0:
+                d.signal_event = d.signal_event + 1  # counts toward gate/up's event instead
+                return
+    plan = _mutated(m)
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_bad_shapes_and_options():
+    base = si.TINY
+    bad = [dict(head_dim=96), dict(n_kv_heads=3), dict(hidden=300)]
+    for kw in bad:
+        d = dict(base.__dict__)
+        d.update(kw)
+        s = si.ModelShape(**d)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_plan_create(shape_struct(s), plan_opts(1, 128, num_cus=8))
+        assert e.value.code == mk.MK_ERR_SHAPE
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_create(shape_struct(base), plan_opts(17, 128, num_cus=8))
+    assert e.value.code == mk.MK_ERR_INVALID_ARG
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_create(shape_struct(base), plan_opts(1, 4096, kv_splits=1, num_cus=8))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED
+
+
+def test_sizes_match_layouts():
+    shape, batch, max_ctx = SHAPES["llama1b_pos1024"]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256))
+    try:
+        ws, kv, lg, n = mk.mk_plan_sizes(plan)
+        assert kv == 2 * 16 * 2 * 1 * 8 * max_ctx * 64
+        assert lg == 4 * 128256
+        assert ws < 64 << 20
+    finally:
+        mk.mk_plan_destroy(plan)

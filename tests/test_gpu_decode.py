@@ -1,0 +1,176 @@
+"""GPU parity of the decode path against the CPU oracle, through the C ABI.
+
+Tiny model: all 47 passes (16 teacher-forced prompt tokens, then greedy),
+in every execution and synchronisation mode, plus forced key-range splits.
+Llama-1B shape at position 1024 and 8192: full-logit parity on the first
+passes of the benchmarked configuration (same plan and launch shape as
+bench.py).  Modes must agree bit for bit with each other (same ops, same
+reduction orders)."""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from decode_harness import LOGIT_TOL, check_kv, run_decode
+from oracle import oracle as orc
+from persistent_megakernel_decode_02_amd import engine, mk
+
+pytestmark = pytest.mark.gpu
+
+TINY = si.WORKLOADS["tiny"]
+
+
+@pytest.fixture(scope="module")
+def tiny_setup():
+    w = si.make_weights(TINY.shape, master=0)
+    return w, engine.to_gpu(w), orc.Model(TINY.shape, w)
+
+
+def _run_tiny(tiny_setup, **kw):
+    w, gw, model = tiny_setup
+    return run_decode(TINY, TINY.steps, weights=w, gpu_weights=gw, model=model, **kw)
+
+
+def test_device_is_mi355x():
+    info = mk.mk_device_query(0)
+    print(f"device {info.arch.decode()} cus={info.num_cus} lds/block={info.lds_per_block} "
+          f"lds/cu={info.lds_per_cu} clock={info.clock_khz}kHz mega_blocks_per_cu={info.mega_blocks_per_cu}")
+    assert info.arch.decode().startswith("gfx950")
+    assert info.num_cus >= 1
+
+
+@pytest.mark.parametrize("mode", [(mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
+                                  (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER)],
+                         ids=["mega-counter", "mega-flag", "multi"])
+def test_tiny_decode_matches_oracle(tiny_setup, mode):
+    res = _run_tiny(tiny_setup, exec_mode=mode[0], sync_mode=mode[1])
+    print(f"tiny {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}, "
+          f"tokens {[t[0] for t in res.tokens]}")
+    assert res.max_rel_err <= LOGIT_TOL
+    assert res.max_rel_err <= 1e-4  # fp32 accumulation is far tighter than the bound
+    assert res.near_ties == 0
+    exact = check_kv(res)
+    print(f"kv exact fraction {exact:.6f}")
+
+
+def test_tiny_modes_bit_identical(tiny_setup):
+    a = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MEGA, sync_mode=mk.MK_SYNC_COUNTER)
+    b = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MEGA, sync_mode=mk.MK_SYNC_FLAG)
+    c = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MULTI, sync_mode=mk.MK_SYNC_COUNTER)
+    assert a.tokens == b.tokens == c.tokens
+    assert np.array_equal(a.logits_last, b.logits_last) and np.array_equal(a.logits_last, c.logits_last)
+    assert np.array_equal(a.kv_gpu, b.kv_gpu) and np.array_equal(a.kv_gpu, c.kv_gpu)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 16])
+def test_tiny_split_attention_matches_oracle(tiny_setup, splits):
+    res = _run_tiny(tiny_setup, kv_splits=splits)
+    assert res.max_rel_err <= 1e-4, res.max_rel_err
+    assert res.near_ties == 0
+    check_kv(res)
+
+
+def test_tiny_host_driven_positions(tiny_setup):
+    # without MK_ADVANCE the host feeds tokens and positions itself
+    res = _run_tiny(tiny_setup, advance=False)
+    assert res.max_rel_err <= 1e-4
+    check_kv(res)
+
+
+@pytest.fixture(scope="module")
+def llama1b():
+    wl = si.WORKLOADS["llama1b_pos1024"]
+    w = si.make_weights(wl.shape, master=0)
+    return w, engine.to_gpu(w), orc.Model(wl.shape, w)
+
+
+def test_llama1b_pos1024_first_passes(llama1b):
+    wl = si.WORKLOADS["llama1b_pos1024"]
+    w, gw, model = llama1b
+    res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model)
+    print(f"llama1b@1024: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
+    assert res.max_rel_err <= LOGIT_TOL
+    assert res.max_rel_err <= 1e-3
+    check_kv(res)
+
+
+def test_llama1b_pos8192_split_attention(llama1b):
+    wl = si.WORKLOADS["llama1b_pos8192"]
+    w, gw, model = llama1b
+    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model)
+    print(f"llama1b@8192: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
+    assert res.max_rel_err <= 1e-3
+    check_kv(res)
+
+
+def test_invalid_token_reports_input_error_and_poisons(tiny_setup):
+    w, gw, model = tiny_setup
+    s = TINY.shape
+    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx)
+    try:
+        kv = eng.kv_cache()
+        logits = torch.empty((1, s.vocab), dtype=torch.float32, device="cuda:0")
+        pos = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        bad = torch.tensor([s.vocab + 5], dtype=torch.int32, device="cuda:0")
+        eng.step(bad, pos, kv, logits)
+        rc, _ = eng.device_error()
+        assert rc == mk.MK_ERR_INPUT
+        with pytest.raises(mk.MkError) as e:
+            eng.step(bad, pos, kv, logits)
+        assert e.value.code == mk.MK_ERR_STATE
+        eng.reset()
+        good = torch.tensor([3], dtype=torch.int32, device="cuda:0")
+        eng.step(good, pos, kv, logits)
+        assert eng.device_error()[0] == 0
+        bad_pos = torch.tensor([TINY.max_ctx], dtype=torch.int32, device="cuda:0")
+        eng.step(good, bad_pos, kv, logits)
+        assert eng.device_error()[0] == mk.MK_ERR_INPUT
+    finally:
+        eng.close()
+
+
+def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup):
+    # the host claims more steps ran than the device counted, so the first
+    # dependency wait can never be met; a 2 ms watchdog ends the step cleanly
+    w, gw, model = tiny_setup
+    s = TINY.shape
+    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx)
+    try:
+        kv = eng.kv_cache()
+        logits = torch.empty((1, s.vocab), dtype=torch.float32, device="cuda:0")
+        pos = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        tok = torch.tensor([3], dtype=torch.int32, device="cuda:0")
+        mk.mk_ctx_set_watchdog_us(eng.ctx, 2000, eng.stream.cuda_stream)
+        mk.mk_ctx_set_epoch(eng.ctx, 5)
+        eng.step(tok, pos, kv, logits)
+        rc, detail = eng.device_error()
+        assert rc == mk.MK_ERR_TIMEOUT, rc
+        eng.reset()
+        mk.mk_ctx_set_watchdog_us(eng.ctx, 2_000_000, eng.stream.cuda_stream)
+        eng.step(tok, pos, kv, logits)
+        assert eng.device_error()[0] == 0
+    finally:
+        eng.close()
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+def test_gridsync_variants_are_correct(variant):
+    info = mk.mk_device_query(0)
+    n = info.num_cus
+    scratch = torch.empty(mk.mk_gridsync_scratch_bytes(n) + 256, dtype=torch.uint8, device="cuda:0")
+    base = (scratch.data_ptr() + 255) // 256 * 256
+    res = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nb = 2000
+    mk.mk_gridsync_bench(variant, 10, n, base, res.data_ptr(), st.cuda_stream)
+    e0.record(st)
+    mk.mk_gridsync_bench(variant, nb, n, base, res.data_ptr(), st.cuda_stream)
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / nb
+    r = res.cpu().tolist()
+    print(f"gridsync {mk.GRIDSYNC_VARIANTS[variant]}: {us:.2f} us/barrier at {n} blocks, errors {r[0]}, "
+          f"timeouts {r[1]}")
+    assert r[1] == 0
+    assert r[0] == 0
