@@ -48,8 +48,10 @@ def main():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
-    ap.add_argument("--mode", default="mega", choices=["mega", "multi", "mega-flag"],
-                    help="what to time for the headline (profiling runs)")
+    ap.add_argument("--mode", default="mega-sentinel",
+                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter"],
+                    help="execution / synchronisation scheme of the headline number")
+    ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -117,12 +119,23 @@ def main():
             if rc != 0:
                 raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
             ms = e0.elapsed_time(e1)
+            if args.trace and (exec_mode, sync_mode) == modes[args.mode]:
+                tr = torch.zeros(eng.n_instr * 4 + 16, dtype=torch.int64, device=dev)
+                mk.mk_ctx_set_trace(eng.ctx, tr.data_ptr(), eng.n_instr, stream.cuda_stream)
+                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+                torch.cuda.synchronize()
+                mk.mk_ctx_set_trace(eng.ctx, None, 0, stream.cuda_stream)
+                descs = mk.mk_plan_export(eng.plan)
+                arr = np.array([(d.cu, d.slot, d.op, d.layer, d.level, d.r0, d.r1, d.split) for d in descs])
+                np.savez(args.trace, desc=arr, t=tr[: eng.n_instr * 4].cpu().numpy().reshape(-1, 4))
             return ms, eng.info
         finally:
             eng.close()
 
-    modes = {"mega": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
-             "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG)}
+    modes = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
+             "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL),
+             "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
+             "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER)}
     ms, info = timed(*modes[args.mode], K, W)
     log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
     ms_per = ms / K
@@ -132,7 +145,8 @@ def main():
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "mk_mega_kernel" if args.mode != "multi" else "mk_level_kernel",
+            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel"}.get(
+                args.mode, "mk_role_mega_kernel"),
             "bytes_per_launch": bpp if args.mode != "multi" else None}
 
     extras = {"plan": {"cus": info.num_cus, "instructions": info.n_instructions, "levels": info.n_levels,
@@ -144,7 +158,7 @@ def main():
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[bench] {name}: {K} passes in {ms2:.3f} ms")
-        if "multi" in extras:
+        if "multi" in extras and args.mode.startswith("mega"):
             extras["bubble_us_per_pass"] = round((extras["multi"]["ms_per_pass"] - ms_per) * 1000.0, 2)
             extras["launches_per_pass_multi"] = info.n_levels
         # grid-barrier microbenchmark

@@ -65,12 +65,19 @@ typedef struct {
 
 /* ------------------------------------------------------------ plan options */
 enum { MK_SYNC_COUNTER = 0, /* one monotonic counter per event, atomic add */
-       MK_SYNC_FLAG = 1     /* one epoch flag per producer, plain stores */ };
-enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step */
-       MK_EXEC_MULTI = 1    /* one launch per op level (kernel boundaries) */ };
+       MK_SYNC_FLAG = 1,    /* one epoch flag per producer, plain stores */
+       MK_SYNC_SENTINEL = 2 /* the data is the signal: activation words start as a
+                               NaN sentinel pattern each step and consumers poll
+                               the data itself (MK_EXEC_MEGA only) */ };
+enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step, loader /
+                               sync-storer / compute wavefronts, LDS page ring */
+       MK_EXEC_MULTI = 1,   /* the same role-specialised ops, one launch per
+                               dependency level (kernel boundaries) */
+       MK_EXEC_FLAT = 2     /* one persistent launch with homogeneous waves: all
+                               waves load, wait and compute each instruction */ };
 
 typedef struct {
-  int32_t max_batch;   /* sequences per step, 1..16 */
+  int32_t max_batch;   /* sequences per step: 1..16 (MK_EXEC_FLAT), 1..4 otherwise */
   int32_t max_ctx;     /* KV slots per sequence */
   int32_t kv_splits;   /* attention splits per (sequence, kv head); 0 = auto */
   int32_t sync_mode;   /* MK_SYNC_* */
@@ -235,9 +242,21 @@ int mk_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_b
  * re-derived).  Used by tests that corrupt a plan on purpose; the plan is
  * then accepted only if mk_plan_validate passes.  Host only. */
 int mk_plan_set_instructions(mk_plan *plan, const mk_instr_desc *descs, size_t n);
+/* Byte offsets of the activation buffers inside the workspace, for tests
+ * and debugging: out[0..7] = qkv, attn, xmid, hbuf, xout, end of the
+ * activation block, attention partials, parity stride (bytes; 0 unless
+ * sentinel mode).  Each activation buffer is fp32 [n_layers][max_batch][n]
+ * with n = (n_q + 2 n_kv) head_dim, n_q head_dim, hidden, ffn, hidden. */
+int mk_plan_get_layout(const mk_plan *plan, uint64_t out[8]);
 /* Shorten the device watchdog of a context (microseconds) so tests can turn a
  * wait that cannot be met into MK_ERR_TIMEOUT quickly.  Synchronises stream. */
 int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
+/* Instruction trace of the megakernel: when d_trace is not NULL every
+ * instruction i of later steps stores 4 uint64 at d_trace[4*i]: the
+ * 100 MHz real-time counter when its wait began, when its work began and
+ * when it finished, and (cu << 32 | step epoch).  n_records must cover the
+ * plan's instruction count.  NULL switches tracing off.  Synchronises stream. */
+int mk_ctx_set_trace(mk_ctx *ctx, void *d_trace, size_t n_records, void *stream);
 /* Overwrite the host-side step counter of a context.  Setting it ahead of the
  * device counters makes the next step's dependency waits unsatisfiable, which
  * (with a short watchdog) exercises the MK_ERR_TIMEOUT path without a hang. */

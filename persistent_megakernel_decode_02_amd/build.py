@@ -26,7 +26,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else []) + ["-c", path, "-o", obj]
+    # host-only sources are still compiled by hipcc (HIP runtime headers) for gfx950 only
+    cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else [f"--offload-arch={ARCH}"]) + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -9,7 +9,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_launch.h"
 #include "planner.h"
 
@@ -208,6 +208,11 @@ static int zero_sync(mk_ctx *c, hipStream_t st) {
   const MkLayout &y = c->plan.lay;
   size_t words = (y.sync_end - y.sync_begin) / 4;
   if (mk_launch_fill(c->ws + y.sync_begin, 0u, words, st)) return MK_ERR_HIP;
+  if (c->plan.opts.sync_mode == MK_SYNC_SENTINEL) {
+    // both step parities of the activations start as "not produced yet"
+    const size_t act_words = 2 * (y.act_end - y.qkv) / 4;
+    if (mk_launch_fill(c->ws + y.qkv, 0x7FBADBADu, act_words, st)) return MK_ERR_HIP;
+  }
   return MK_OK;
 }
 
@@ -220,10 +225,12 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MK_ERR_HIP;
-  if (plan->opts.exec_mode == MK_EXEC_MEGA) {
+  if (plan->opts.exec_mode != MK_EXEC_MULTI) {
     int n_dev_cu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&n_dev_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_ERR_HIP;
-    if (mk_occupancy_mega(mega_lds(plan), &per_cu)) return MK_ERR_HIP;
+    const int occ = plan->opts.exec_mode == MK_EXEC_MEGA ? mk_occupancy_role(plan->lds_bytes, &per_cu)
+                                                          : mk_occupancy_mega(mega_lds(plan), &per_cu);
+    if (occ) return MK_ERR_HIP;
     // persistence: every workgroup of the grid must be resident at once
     if (per_cu < 1 || (int64_t)plan->n_cu > (int64_t)per_cu * n_dev_cu) return MK_ERR_NOT_RESIDENT;
   }
@@ -258,6 +265,13 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   P.n_events = p.n_events;
   P.n_lm_parts = p.n_lm_parts;
   P.watchdog_ticks = 200000000u;  // 2 s
+  P.lds_x = p.lds_x;
+  P.lds_resid = p.lds_resid;
+  P.lds_wsc = p.lds_wsc;
+  P.lds_ring = p.lds_ring;
+  P.n_pages = p.n_pages;
+  P.lds_total = p.lds_bytes;
+  P.par_stride = (int64_t)((y.act_end - y.qkv) / 4);
   char *w = c->ws;
   P.instr = (const MkInstr *)(w + y.instr);
   P.cu_begin = (const int32_t *)(w + y.cu_begin);
@@ -364,7 +378,11 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
   S.flags = flags;
   hipStream_t st = (hipStream_t)stream;
   const MkProgram *dp = (const MkProgram *)(c->ws + c->plan.lay.prog);
-  if (c->plan.opts.exec_mode == MK_EXEC_MEGA) {
+  const int mode = c->plan.opts.exec_mode;
+  if (mode == MK_EXEC_MEGA) {
+    S.multi = 0;
+    if (mk_launch_role_mega(dp, S, c->plan.n_cu, c->plan.lds_bytes, st)) return MK_ERR_HIP;
+  } else if (mode == MK_EXEC_FLAT) {
     S.multi = 0;
     if (mk_launch_mega(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
   } else {
@@ -372,7 +390,7 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
     for (int lv = 0; lv < c->plan.n_levels; ++lv) {
       S.level = lv;
       int nb = c->plan.level_begin[lv + 1] - c->plan.level_begin[lv];
-      if (mk_launch_level(dp, S, nb, c->plan.lds_bytes, st)) return MK_ERR_HIP;
+      if (mk_launch_role_level(dp, S, nb, c->plan.lds_bytes, st)) return MK_ERR_HIP;
     }
   }
   c->epoch++;
@@ -414,6 +432,31 @@ int mk_ctx_set_watchdog_us(mk_ctx *c, uint32_t us, void *stream) {
   if (!c || us == 0) return MK_ERR_INVALID_ARG;
   uint64_t ticks = (uint64_t)us * 100u;  // 100 MHz real-time counter
   c->prog.watchdog_ticks = ticks > 0xffffffffu ? 0xffffffffu : (uint32_t)ticks;
+  hipStream_t st = (hipStream_t)stream;
+  int rc = upload_prog(c, st);
+  if (rc == MK_OK && hipStreamSynchronize(st) != hipSuccess) rc = MK_ERR_HIP;
+  return rc;
+}
+
+int mk_plan_get_layout(const mk_plan *p, uint64_t out[8]) {
+  if (!p || !out) return MK_ERR_INVALID_ARG;
+  const MkLayout &y = p->lay;
+  out[0] = y.qkv;
+  out[1] = y.attn;
+  out[2] = y.xmid;
+  out[3] = y.hbuf;
+  out[4] = y.xout;
+  out[5] = y.act_end;
+  out[6] = y.part;
+  out[7] = p->opts.sync_mode == MK_SYNC_SENTINEL ? (y.act_end - y.qkv) : 0;
+  return MK_OK;
+}
+
+int mk_ctx_set_trace(mk_ctx *c, void *d_trace, size_t n_records, void *stream) {
+  if (!c) return MK_ERR_INVALID_ARG;
+  if (d_trace && n_records < c->plan.instr.size()) return MK_ERR_CTX_OVERFLOW;
+  if (d_trace && !aligned16(d_trace)) return MK_ERR_ALIGN;
+  c->prog.trace = (uint64_t *)d_trace;
   hipStream_t st = (hipStream_t)stream;
   int rc = upload_prog(c, st);
   if (rc == MK_OK && hipStreamSynchronize(st) != hipSuccess) rc = MK_ERR_HIP;

@@ -72,6 +72,15 @@ MKD float block_sum(float v, float *red) {
   return t;
 }
 
+// element offset of cache row block [l][plane][b][g][0][0] in the
+// [L][2][B_max][nkv][max_ctx][d] bf16 KV cache
+MKD size_t kv_off(const MkProgram &P, int l, int plane, int b, int g) {
+  return ((((size_t)l * 2 + plane) * P.B_max + b) * P.nkv + g) * (size_t)P.max_ctx * P.d;
+}
+
+// greedy order: larger value wins, equal values go to the smaller index
+MKD bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
 // record the first device error and raise the abort flag every wait checks
 MKD void mk_raise(const MkProgram &P, int code, int detail) {
   int32_t *err = P.err;

@@ -13,6 +13,28 @@
 
 #include "mk_launch.h"
 #include "mk_ops.h"
+#include "mk_roles_ops.h"
+
+// Role-specialised persistent kernel: one workgroup per CU runs the CU's
+// instruction list with loader / sync-storer / compute waves.
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_role_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const int cu = blockIdx.x;
+  const int i0 = P.cu_begin[cu], i1 = P.cu_begin[cu + 1];
+  role_run(P, S, nullptr, i0, i1 - i0, lds);
+}
+
+// The same role-specialised ops, one launch per dependency level: block i
+// runs instruction i of the level.
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_role_level_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const int idx = P.level_list[P.level_begin[S.level] + blockIdx.x];
+  role_run(P, S, nullptr, idx, 1, lds);
+}
 
 extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -21,13 +43,23 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
   if (mk_aborted(P)) return;
   const int cu = blockIdx.x;
   const int i0 = P.cu_begin[cu], i1 = P.cu_begin[cu + 1];
+  uint64_t *const trace = P.trace;
   for (int i = i0; i < i1; ++i) {
     const MkInstr in = P.instr[i];
+    const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
     if (in.wait_ev >= 0 && !mk_wait(P, S, in.wait_ev, &s_flag)) return;
+    const uint64_t ts = trace ? __builtin_amdgcn_s_memrealtime() : 0;
     const int st = run_instr(P, S, in, smem, &s_flag);
     if (st == MK_ST_ABORT) return;
     if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
+    if (trace && threadIdx.x == 0) {
+      uint64_t *r = trace + (size_t)i * 4;
+      r[0] = tw;
+      r[1] = ts;
+      r[2] = __builtin_amdgcn_s_memrealtime();
+      r[3] = ((uint64_t)cu << 32) | S.epoch;
+    }
   }
 }
 
@@ -60,6 +92,28 @@ int mk_launch_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int
   if (set_lds((const void *)mk_level_kernel, lds) != hipSuccess) return -1;
   hipLaunchKernelGGL(mk_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
+  if (set_lds((const void *)mk_role_mega_kernel, lds) != hipSuccess) return -1;
+  hipLaunchKernelGGL(mk_role_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s) {
+  if (n_blocks <= 0) return 0;
+  if (set_lds((const void *)mk_role_level_kernel, lds) != hipSuccess) return -1;
+  hipLaunchKernelGGL(mk_role_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_occupancy_role(int lds, int *blocks_per_cu) {
+  if (set_lds((const void *)mk_role_mega_kernel, lds) != hipSuccess) return -1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void *)mk_role_mega_kernel, MK_BLOCK, lds) != hipSuccess)
+    return -1;
+  *blocks_per_cu = nb;
+  return 0;
 }
 
 int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s) {

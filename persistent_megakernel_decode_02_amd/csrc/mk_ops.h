@@ -64,9 +64,6 @@ MKD void rmsnorm_lds(float *xs, int K, const uint16_t *gain, float eps, float *r
   __syncthreads();
 }
 
-MKD size_t kv_off(const MkProgram &P, int l, int plane, int b, int g) {
-  return ((((size_t)l * 2 + plane) * P.B_max + b) * P.nkv + g) * (size_t)P.max_ctx * P.d;
-}
 
 // Residual-stream input of layer l for sequence b, element i: the embedding
 // row of the token for layer 0, else the previous layer's output.
@@ -370,7 +367,6 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
 }
 
 // ------------------------------------------ LM head + greedy argmax
-MKD bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
 MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag) {
   const int H = P.H, L = P.L, V = P.V;

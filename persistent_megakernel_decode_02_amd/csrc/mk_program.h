@@ -9,9 +9,22 @@
 #include <stdint.h>
 
 #define MK_MAX_BATCH 16
-#define MK_MAX_GROUP 8     // q heads per kv head
+#define MK_MAX_GROUP 4     // q heads per kv head
 #define MK_BLOCK 512       // threads per workgroup (8 wave64)
 #define MK_NWAVES (MK_BLOCK / 64)
+
+// role engine
+#define MK_PAGE 4096                      // bytes per LDS page
+#define MK_MAXNP 64                       // most pages in the ring
+#define MK_NLW 2                          // loader waves
+#define MK_NCW (MK_NWAVES - MK_NLW - 1)   // compute waves (one more wave syncs and stores)
+#define MK_RB_MAXB 4                      // sequences the role engine stages per instruction
+#define MK_CTL_BYTES 1024                 // LDS control block
+#define MK_WSC (32 * MK_MAX_GROUP)        // floats of per-compute-wave scratch
+#define MK_LDS_TOTAL (160 * 1024)         // LDS of one gfx950 workgroup
+
+enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
+enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2 };
 
 enum MkOp : int32_t {
   MKOP_QKV = 1,
@@ -45,9 +58,14 @@ struct MkProgram {
   int32_t B_max, max_ctx, S;          // S = attention splits per (sequence, kv head)
   float eps;
   int32_t tied;
-  int32_t sync_mode;                  // 0 counters, 1 flags
+  int32_t sync_mode;                  // 0 counters, 1 flags, 2 data sentinels
   int32_t n_cu, n_instr, n_levels, n_events, n_lm_parts;
   uint32_t watchdog_ticks;            // s_memrealtime ticks (100 MHz) before a wait gives up
+  // role-engine LDS layout (byte offsets into dynamic LDS) and ring size
+  int32_t lds_x, lds_resid, lds_wsc, lds_ring, n_pages, lds_total;
+  // activations occupy one contiguous block starting at qkv; in sentinel
+  // mode a second copy (the other step parity) follows at +par_stride floats
+  int64_t par_stride;
 
   // lists (device pointers into the workspace)
   const MkInstr *instr;        // CU-major
@@ -77,6 +95,7 @@ struct MkProgram {
   uint32_t *flags;   // [sum ev_count] epoch flags
   uint32_t *tickets; // [n_tickets] monotonic last-arriver tickets
   int32_t *err;      // [4]: code, detail, abort flag, spare
+  uint64_t *trace;   // optional: [n_instr][4] wait-begin, start, end (100 MHz ticks), cu
 };
 
 struct MkStep {

@@ -55,8 +55,37 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (o->max_batch < 1 || o->max_batch > MK_MAX_BATCH) return MK_ERR_INVALID_ARG;
   if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
-  if (o->sync_mode != MK_SYNC_COUNTER && o->sync_mode != MK_SYNC_FLAG) return MK_ERR_INVALID_ARG;
-  if (o->exec_mode != MK_EXEC_MEGA && o->exec_mode != MK_EXEC_MULTI) return MK_ERR_INVALID_ARG;
+  if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
+  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_FLAT) return MK_ERR_INVALID_ARG;
+  // data sentinels replace the events only inside one persistent launch
+  if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA) return MK_ERR_UNSUPPORTED;
+  return MK_OK;
+}
+
+// Role-engine LDS: control block | per-compute-wave scratch | residual rows |
+// staged input vectors | page ring (the rest of the workgroup's 160 KiB).
+static int role_lds_layout(mk_plan *p) {
+  const mk_model_shape &s = p->shape;
+  const int B = p->B, d = s.head_dim, G = p->G;
+  if (B > MK_RB_MAXB) return MK_ERR_UNSUPPORTED;
+  int max_rows = 1;
+  for (const MkInstr &in : p->instr)
+    if (in.op == MKOP_OPROJ || in.op == MKOP_DOWN) max_rows = std::max(max_rows, in.r1 - in.r0);
+  int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * d, (int64_t)s.ffn});
+  int64_t x_floats = std::max<int64_t>((int64_t)B * kmax, (int64_t)(G + 2) * d + (int64_t)MK_NCW * G * (d + 2));
+  int64_t o = MK_CTL_BYTES;
+  p->lds_wsc = (int)o;
+  o += (int64_t)MK_NCW * MK_WSC * 4;
+  p->lds_resid = (int)o;
+  o += ((int64_t)B * max_rows * 4 + 15) / 16 * 16;
+  p->lds_x = (int)o;
+  o += (x_floats * 4 + 255) / 256 * 256;
+  p->lds_ring = (int)o;
+  int64_t pages = (MK_LDS_TOTAL - o) / MK_PAGE;
+  if (pages > MK_MAXNP) pages = MK_MAXNP;
+  if (pages < 4) return MK_ERR_UNSUPPORTED;
+  p->n_pages = (int)pages;
+  p->lds_bytes = MK_LDS_TOTAL;
   return MK_OK;
 }
 
@@ -130,6 +159,8 @@ void mk_plan_compute_layout(mk_plan *p) {
   y.xmid = take(4 * L * B * H);
   y.hbuf = take(4 * L * B * I);
   y.xout = take(4 * L * B * H);
+  y.act_end = o;
+  if (p->opts.sync_mode == MK_SYNC_SENTINEL) o += y.act_end - y.qkv;  // second parity
   y.part = take(4 * L * B * nkv * p->S * p->G * (d + 2));
   y.lm_val = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.lm_idx = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
@@ -173,7 +204,7 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     S = (int)std::max<int64_t>(S, ceil_div(p->max_ctx, 1024));
     S = std::max(S, 1);
   }
-  if (ceil_div(p->max_ctx, S) > 1024) {
+  if (opts->exec_mode == MK_EXEC_FLAT && ceil_div(p->max_ctx, S) > 1024) {
     delete p;
     return MK_ERR_UNSUPPORTED;
   }
@@ -368,10 +399,18 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     p->instr_cu.swap(cu2);
   }
   mk_plan_finalize_lists(p);
-  p->lds_bytes = lds_requirement(p);
-  if (p->lds_bytes > 160 * 1024) {
-    delete p;
-    return MK_ERR_UNSUPPORTED;
+  if (opts->exec_mode == MK_EXEC_FLAT) {
+    p->lds_bytes = lds_requirement(p);
+    if (p->lds_bytes > MK_LDS_TOTAL) {
+      delete p;
+      return MK_ERR_UNSUPPORTED;
+    }
+  } else {
+    rc = role_lds_layout(p);
+    if (rc) {
+      delete p;
+      return rc;
+    }
   }
   mk_plan_compute_layout(p);
   rc = mk_plan_check(p, false, 0, 0);

@@ -6,12 +6,12 @@
 
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_program.h"
 
 struct MkLayout {  // byte offsets inside the caller's workspace
   size_t prog, instr, cu_begin, level_begin, level_list, ev_count, ev_flag_base, rope, layers;
-  size_t qkv, attn, xmid, hbuf, xout, part, lm_val, lm_idx, ctr, flags, tickets, err;
+  size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, err;
   size_t sync_begin, sync_end;  // [ctr .. err] zeroed on create/reset
   size_t total;
 };
@@ -22,6 +22,7 @@ struct mk_plan {
   int n_cu = 0, S = 1, B = 1, max_ctx = 0, G = 1;
   int n_levels = 0, n_events = 0, n_flags = 0, n_tickets = 0, n_lm_parts = 0;
   int lds_bytes = 0;
+  int lds_x = 0, lds_resid = 0, lds_wsc = 0, lds_ring = 0, n_pages = 0;  // role engine
   std::vector<MkInstr> instr;  // CU-major
   std::vector<int32_t> instr_cu;
   std::vector<int32_t> cu_begin, level_begin, level_list, ev_count, ev_flag_base;

@@ -27,8 +27,8 @@ MK_ERR_PLAN = -9
 MK_ERR_STATE = -10
 MK_ERR_UNSUPPORTED = -11
 
-MK_SYNC_COUNTER, MK_SYNC_FLAG = 0, 1
-MK_EXEC_MEGA, MK_EXEC_MULTI = 0, 1
+MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
+MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT = 0, 1, 2
 MK_ADVANCE = 1
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6
 
@@ -107,6 +107,8 @@ SIGNATURES = {
     "mk_ctx_epoch": (C.c_int64, [C.c_void_p]),
     "mk_ctx_destroy": (None, [C.c_void_p]),
     "mk_ctx_set_watchdog_us": (C.c_int, [C.c_void_p, C.c_uint32, C.c_void_p]),
+    "mk_plan_get_layout": (C.c_int, [C.c_void_p, C.POINTER(C.c_uint64)]),
+    "mk_ctx_set_trace": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "mk_ctx_set_epoch": (C.c_int, [C.c_void_p, C.c_int64]),
     "mk_device_query": (C.c_int, [C.c_int32, C.POINTER(mk_device_info)]),
     "mk_gridsync_scratch_bytes": (C.c_size_t, [C.c_int32]),
@@ -181,6 +183,12 @@ def mk_plan_set_instructions(plan, descs: Sequence[mk_instr_desc]) -> int:
     return load_library().mk_plan_set_instructions(plan, arr, len(descs))
 
 
+def mk_plan_get_layout(plan):
+    out = (C.c_uint64 * 8)()
+    _check(load_library().mk_plan_get_layout(plan, out), "mk_plan_get_layout")
+    return list(out)
+
+
 def mk_plan_destroy(plan):
     if plan:
         load_library().mk_plan_destroy(plan)
@@ -222,6 +230,11 @@ def mk_ctx_epoch(ctx) -> int:
 
 def mk_ctx_set_watchdog_us(ctx, us: int, stream: int):
     _check(load_library().mk_ctx_set_watchdog_us(ctx, us, C.c_void_p(stream)), "mk_ctx_set_watchdog_us")
+
+
+def mk_ctx_set_trace(ctx, d_trace: Optional[int], n_records: int, stream: int):
+    _check(load_library().mk_ctx_set_trace(ctx, C.c_void_p(d_trace) if d_trace else None, n_records,
+                                           C.c_void_p(stream)), "mk_ctx_set_trace")
 
 
 def mk_ctx_set_epoch(ctx, epoch: int):

@@ -10,10 +10,11 @@ Comparison rules (written here once, used by every GPU test):
     cascade.  The GPU token must equal the oracle's argmax unless the oracle
     logit of the GPU token is within the step's measured logit error of the
     oracle's maximum (a near tie), which is counted and reported;
-  * KV cache: after the run, slots the steps wrote hold bf16 values equal to
-    the oracle's, allowing one bf16 unit in the last place for at most 0.1 %
-    of them (fp32 vs fp64 rounding of the same real value); every other byte
-    of the cache is unchanged.
+  * KV cache: the bytes that changed are exactly the slots of the decoded
+    positions (indexing is bit-exact); written bf16 values equal the oracle's
+    except for at most 1 % of them, which differ by the rounding of an fp32
+    versus an fp64 value (bound in check_kv); every other byte of the cache
+    is unchanged.
 """
 from __future__ import annotations
 
@@ -40,6 +41,7 @@ class RunResult:
     kv_ref: np.ndarray
     kv_written: np.ndarray          # bool mask of slots written by the steps
     logits_last: np.ndarray
+    kv_before: np.ndarray
 
 
 def ulp_diff_bf16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -62,7 +64,7 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
     prefill = pos0 if wl.start_pos != 0 else [0] * B
     kv_cpu = si.make_kv_cache(s, B, wl.max_ctx, prefill, master=master)
     kv_ref = si.bf16_bits(kv_cpu).reshape(kv_cpu.shape).copy()
-    kv0 = kv_ref.copy()
+    kv0 = kv_ref.copy()  # cache before the run, for the changed-slot check
     eng = engine.Engine(s, gw, max_batch=B, max_ctx=wl.max_ctx, kv_splits=kv_splits, sync_mode=sync_mode,
                         exec_mode=exec_mode)
     try:
@@ -116,18 +118,40 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
         torch.cuda.synchronize()
         kv_gpu = kv.view(torch.int16).cpu().numpy().view(np.uint16)
         return RunResult(out_tokens, max(errs), errs, near, kv_gpu, kv_ref, written,
-                         logits.cpu().numpy())
+                         logits.cpu().numpy(), kv0)
     finally:
         eng.close()
 
 
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def check_kv(res: RunResult, kv_before: Optional[np.ndarray] = None):
-    """Written slots agree with the oracle to 1 bf16 ulp (>= 99.9 % exact);
-    untouched bytes are identical."""
+    """Cache indexing is exact: the bytes that changed are exactly the slots
+    the steps were meant to write, on both sides, and nothing else moved.
+
+    Values: the GPU rounds an fp32 result to bf16, the oracle an fp64 one.
+    The fp32 value carries an absolute error |delta| of order 1e-6 times the
+    vector's scale (2048-term dot products, grown through the layers), so the
+    two roundings differ by at most one bf16 ulp of the value plus |delta|:
+    required |gpu - oracle| <= ulp(|oracle|) + 1e-4 * max|oracle| (the second
+    term covers values near zero, where |delta| spans many ulps), and at least
+    99 % bit-identical (straddling probability ~ 2 * 1e-5 / 2^-8 ~ 0.5 %)."""
     m = res.kv_written
     g, r = res.kv_gpu[m], res.kv_ref[m]
     exact = float(np.mean(g == r))
-    assert exact >= 0.999, exact
-    assert ulp_diff_bf16(g, r).max() <= 1
+    assert exact >= 0.99, exact
+    gf, rf = bf16_to_f64(g), bf16_to_f64(r)
+    mag = np.abs(rf)
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
+    bound = ulp + 1e-4 * mag.max()
+    worst = float(np.max(np.abs(gf - rf) / bound))
+    assert worst <= 1.0, worst
     assert np.array_equal(res.kv_gpu[~m], res.kv_ref[~m])
+    before = res.kv_before if kv_before is None else kv_before
+    changed_gpu, changed_ref = res.kv_gpu != before, res.kv_ref != before
+    assert not changed_gpu[~m].any() and not changed_ref[~m].any()
+    # a written value may coincide with the prefill by chance; nearly all differ
+    assert changed_gpu[m].mean() > 0.99 and changed_ref[m].mean() > 0.99
     return exact

@@ -45,7 +45,9 @@ SHAPES = {k: (wl.shape, wl.batch, wl.max_ctx) for k, wl in si.WORKLOADS.items()}
 @pytest.mark.parametrize("n_cu", [8, 80, 256, 304])
 def test_plan_builds_and_validates(name, n_cu):
     shape, batch, max_ctx = SHAPES[name]
-    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=n_cu))
+    # the role engine stages up to 4 sequences; larger batches run the flat kernel
+    exec_mode = mk.MK_EXEC_MEGA if batch <= 4 else mk.MK_EXEC_FLAT
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=n_cu, exec_mode=exec_mode))
     try:
         assert mk.mk_plan_validate(plan) == mk.MK_OK
         info = mk.mk_plan_get_info(plan)
@@ -186,8 +188,36 @@ def test_bad_shapes_and_options():
         mk.mk_plan_create(shape_struct(base), plan_opts(17, 128, num_cus=8))
     assert e.value.code == mk.MK_ERR_INVALID_ARG
     with pytest.raises(mk.MkError) as e:
-        mk.mk_plan_create(shape_struct(base), plan_opts(1, 4096, kv_splits=1, num_cus=8))
+        # the flat kernel keeps one split's scores in LDS: at most 1024 positions
+        mk.mk_plan_create(shape_struct(base), plan_opts(1, 4096, kv_splits=1, num_cus=8, exec_mode=mk.MK_EXEC_FLAT))
     assert e.value.code == mk.MK_ERR_UNSUPPORTED
+
+
+def test_role_engine_limits():
+    s16 = SHAPES["llama1b_b16"][0]
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_create(shape_struct(s16), plan_opts(16, 4160, num_cus=256))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED
+    # sentinel synchronisation exists only inside one persistent launch
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_plan_create(shape_struct(si.TINY), plan_opts(1, 128, num_cus=8, sync_mode=mk.MK_SYNC_SENTINEL,
+                                                            exec_mode=mk.MK_EXEC_MULTI))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED
+    for name in ("llama1b_pos1024", "llama8b_pos2048"):
+        shape, batch, max_ctx = SHAPES[name]
+        plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256,
+                                                                sync_mode=mk.MK_SYNC_SENTINEL))
+        try:
+            info = mk.mk_plan_get_info(plan)
+            assert info.lds_bytes == 160 * 1024
+            ws_sent = mk.mk_plan_sizes(plan)[0]
+        finally:
+            mk.mk_plan_destroy(plan)
+        plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256))
+        try:
+            assert mk.mk_plan_sizes(plan)[0] < ws_sent  # sentinel mode keeps two step parities
+        finally:
+            mk.mk_plan_destroy(plan)
 
 
 def test_sizes_match_layouts():

@@ -33,15 +33,20 @@ def _run_tiny(tiny_setup, **kw):
 
 def test_device_is_mi355x():
     info = mk.mk_device_query(0)
+    import sys
     print(f"device {info.arch.decode()} cus={info.num_cus} lds/block={info.lds_per_block} "
-          f"lds/cu={info.lds_per_cu} clock={info.clock_khz}kHz mega_blocks_per_cu={info.mega_blocks_per_cu}")
+          f"lds/cu={info.lds_per_cu} clock={info.clock_khz}kHz mega_blocks_per_cu={info.mega_blocks_per_cu}",
+          file=sys.stderr)
     assert info.arch.decode().startswith("gfx950")
     assert info.num_cus >= 1
 
 
-@pytest.mark.parametrize("mode", [(mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
-                                  (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER)],
-                         ids=["mega-counter", "mega-flag", "multi"])
+MODES = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
+         "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
+         "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG)}
+
+
+@pytest.mark.parametrize("mode", list(MODES.values()), ids=list(MODES))
 def test_tiny_decode_matches_oracle(tiny_setup, mode):
     res = _run_tiny(tiny_setup, exec_mode=mode[0], sync_mode=mode[1])
     print(f"tiny {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}, "
@@ -53,13 +58,15 @@ def test_tiny_decode_matches_oracle(tiny_setup, mode):
     print(f"kv exact fraction {exact:.6f}")
 
 
-def test_tiny_modes_bit_identical(tiny_setup):
-    a = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MEGA, sync_mode=mk.MK_SYNC_COUNTER)
-    b = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MEGA, sync_mode=mk.MK_SYNC_FLAG)
-    c = _run_tiny(tiny_setup, exec_mode=mk.MK_EXEC_MULTI, sync_mode=mk.MK_SYNC_COUNTER)
-    assert a.tokens == b.tokens == c.tokens
-    assert np.array_equal(a.logits_last, b.logits_last) and np.array_equal(a.logits_last, c.logits_last)
-    assert np.array_equal(a.kv_gpu, b.kv_gpu) and np.array_equal(a.kv_gpu, c.kv_gpu)
+@pytest.mark.parametrize("group", [("mega-counter", "mega-flag", "mega-sentinel", "multi"),
+                                   ("flat-counter", "flat-flag")], ids=["roles", "flat"])
+def test_tiny_modes_bit_identical(tiny_setup, group):
+    # the same ops under different synchronisation / launch schemes give the same bits
+    runs = [_run_tiny(tiny_setup, exec_mode=MODES[m][0], sync_mode=MODES[m][1]) for m in group]
+    for r in runs[1:]:
+        assert r.tokens == runs[0].tokens
+        assert np.array_equal(r.logits_last, runs[0].logits_last)
+        assert np.array_equal(r.kv_gpu, runs[0].kv_gpu)
 
 
 @pytest.mark.parametrize("splits", [2, 5, 16])
@@ -84,29 +91,35 @@ def llama1b():
     return w, engine.to_gpu(w), orc.Model(wl.shape, w)
 
 
-def test_llama1b_pos1024_first_passes(llama1b):
+@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "flat-counter"])
+def test_llama1b_pos1024_first_passes(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
     w, gw, model = llama1b
-    res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model)
-    print(f"llama1b@1024: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
+    res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                     sync_mode=MODES[mode][1])
+    print(f"llama1b@1024 {mode}: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
     assert res.max_rel_err <= LOGIT_TOL
     assert res.max_rel_err <= 1e-3
     check_kv(res)
 
 
-def test_llama1b_pos8192_split_attention(llama1b):
+@pytest.mark.parametrize("mode", ["mega-sentinel", "flat-counter"])
+def test_llama1b_pos8192_split_attention(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos8192"]
     w, gw, model = llama1b
-    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model)
+    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                     sync_mode=MODES[mode][1])
     print(f"llama1b@8192: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
     assert res.max_rel_err <= 1e-3
     check_kv(res)
 
 
-def test_invalid_token_reports_input_error_and_poisons(tiny_setup):
+@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter"])
+def test_invalid_token_reports_input_error_and_poisons(tiny_setup, mode):
     w, gw, model = tiny_setup
     s = TINY.shape
-    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx)
+    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx, exec_mode=MODES[mode][0],
+                        sync_mode=MODES[mode][1])
     try:
         kv = eng.kv_cache()
         logits = torch.empty((1, s.vocab), dtype=torch.float32, device="cuda:0")
@@ -129,12 +142,16 @@ def test_invalid_token_reports_input_error_and_poisons(tiny_setup):
         eng.close()
 
 
-def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup):
+@pytest.mark.parametrize("mode", ["mega-counter", "flat-counter"])
+def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup, mode):
     # the host claims more steps ran than the device counted, so the first
-    # dependency wait can never be met; a 2 ms watchdog ends the step cleanly
+    # counter wait can never be met; a 2 ms watchdog ends the step cleanly.
+    # (Flag and sentinel waits compare against what this step's producers
+    # write, so a skipped host epoch cannot starve them.)
     w, gw, model = tiny_setup
     s = TINY.shape
-    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx)
+    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx, exec_mode=MODES[mode][0],
+                        sync_mode=MODES[mode][1])
     try:
         kv = eng.kv_cache()
         logits = torch.empty((1, s.vocab), dtype=torch.float32, device="cuda:0")
