@@ -120,14 +120,14 @@ def main():
                 raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
             ms = e0.elapsed_time(e1)
             if args.trace and (exec_mode, sync_mode) == modes[args.mode]:
-                tr = torch.zeros(eng.n_instr * 4 + 16, dtype=torch.int64, device=dev)
+                tr = torch.zeros(eng.n_instr * 8 + 16, dtype=torch.int64, device=dev)
                 mk.mk_ctx_set_trace(eng.ctx, tr.data_ptr(), eng.n_instr, stream.cuda_stream)
                 eng.step(tokens, positions, kv, logits, nxt, advance=True)
                 torch.cuda.synchronize()
                 mk.mk_ctx_set_trace(eng.ctx, None, 0, stream.cuda_stream)
                 descs = mk.mk_plan_export(eng.plan)
                 arr = np.array([(d.cu, d.slot, d.op, d.layer, d.level, d.r0, d.r1, d.split) for d in descs])
-                np.savez(args.trace, desc=arr, t=tr[: eng.n_instr * 4].cpu().numpy().reshape(-1, 4))
+                np.savez(args.trace, desc=arr, t=tr[: eng.n_instr * 8].cpu().numpy().reshape(-1, 8))
             return ms, eng.info
         finally:
             eng.close()

@@ -236,6 +236,13 @@ int mk_gridsync_bench(int32_t variant, int32_t n_barriers, int32_t n_blocks, voi
  * block to d_out (uint32[n_blocks]).  Gives the achievable HBM read rate. */
 int mk_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_blocks, void *stream);
 
+/* Streaming-read probe through LDS: n_waves (1..8) waves per workgroup stream
+ * `bytes` (multiple of 1024) of d_buf into a 64 KiB LDS ring with direct
+ * global->LDS loads, as the megakernel's loader waves do.  d_out: uint32
+ * [n_blocks]. */
+int mk_lds_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_blocks, int32_t n_waves,
+                       void *stream);
+
 /* ------------------------------------------------------------ test hooks */
 /* Replace a plan's instruction list with `n` descriptors (fields as
  * mk_plan_export writes them; slots, tickets and partial indices are
@@ -251,11 +258,14 @@ int mk_plan_get_layout(const mk_plan *plan, uint64_t out[8]);
 /* Shorten the device watchdog of a context (microseconds) so tests can turn a
  * wait that cannot be met into MK_ERR_TIMEOUT quickly.  Synchronises stream. */
 int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
-/* Instruction trace of the megakernel: when d_trace is not NULL every
- * instruction i of later steps stores 4 uint64 at d_trace[4*i]: the
- * 100 MHz real-time counter when its wait began, when its work began and
- * when it finished, and (cu << 32 | step epoch).  n_records must cover the
- * plan's instruction count.  NULL switches tracing off.  Synchronises stream. */
+/* Instruction trace of the persistent kernels: when d_trace is not NULL
+ * every instruction i of later steps stores 8 uint64 at d_trace[8*i]: the
+ * 100 MHz real-time counter when its wait began, when its inputs were
+ * staged (work began) and when it finished; (cu << 32 | step epoch); for the
+ * role-specialised kernel the CU's cumulative ticks of loader waves blocked
+ * on a free page and of compute waves waiting for a landed page, and the
+ * instruction's page count (else 0).  n_records must cover the plan's
+ * instruction count.  NULL switches tracing off.  Synchronises stream. */
 int mk_ctx_set_trace(mk_ctx *ctx, void *d_trace, size_t n_records, void *stream);
 /* Overwrite the host-side step counter of a context.  Setting it ahead of the
  * device counters makes the next step's dependency waits unsatisfiable, which

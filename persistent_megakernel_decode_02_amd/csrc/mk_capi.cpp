@@ -506,4 +506,11 @@ int mk_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_b
   return mk_launch_stream_read(d_buf, bytes, d_out, n_blocks, (hipStream_t)stream) ? MK_ERR_HIP : MK_OK;
 }
 
+int mk_lds_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t n_blocks, int32_t n_waves,
+                       void *stream) {
+  if (!d_buf || !d_out || n_blocks < 1 || n_waves < 1 || n_waves > 8 || (bytes & 1023u)) return MK_ERR_INVALID_ARG;
+  if (!aligned16(d_buf)) return MK_ERR_ALIGN;
+  return mk_launch_lds_stream(d_buf, bytes, d_out, n_blocks, n_waves, (hipStream_t)stream) ? MK_ERR_HIP : MK_OK;
+}
+
 }  // extern "C"

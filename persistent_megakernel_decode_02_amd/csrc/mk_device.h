@@ -36,14 +36,22 @@ MKD uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// device-coherent accesses (sc1): visible across XCDs without cache maintenance
-MKD float ldc(const float *p) { return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD void stc(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD int32_t ldci(const int32_t *p) { return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD void stci(int32_t *p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD uint32_t ldcu(const uint32_t *p) { return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD void stcu(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MKD uint32_t addcu(uint32_t *p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Device-coherent accesses (sc1): visible across XCDs without cache
+// maintenance.  The pointers are cast to the global address space so the
+// compiler emits global_* instructions; a generic (flat) access would also
+// count against the LDS counter and make every later LDS fence wait for the
+// memory round trip.
+#define MK_G(T) __attribute__((address_space(1))) T
+MKD float ldc(const float *p) { return __hip_atomic_load((MK_G(float) *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stc(float *p, float v) { __hip_atomic_store((MK_G(float) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD int32_t ldci(const int32_t *p) { return __hip_atomic_load((MK_G(int32_t) *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stci(int32_t *p, int32_t v) { __hip_atomic_store((MK_G(int32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD uint32_t ldcu(const uint32_t *p) { return __hip_atomic_load((MK_G(uint32_t) *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stcu(uint32_t *p, uint32_t v) { __hip_atomic_store((MK_G(uint32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD uint32_t addcu(uint32_t *p, uint32_t v) { return __hip_atomic_fetch_add((MK_G(uint32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// plain global store / load (no coherence requirement)
+template <class T> MKD void gst(T *p, T v) { *(MK_G(T) *)p = v; }
+template <class T> MKD T gld(const T *p) { return *(const MK_G(T) *)p; }
 
 // wait until this wave's outstanding memory operations (stores included) completed
 MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -57,6 +65,23 @@ MKD float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Wave-wide sum with DPP lane moves (no LDS traffic): quad swaps, half-row
+// and row mirrors give every lane its 16-lane row sum, two row broadcasts
+// accumulate the four rows into lane 63, which is then read as a scalar.
+template <int CTRL, int ROWMASK>
+MKD float dpp_term(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+MKD float wave_total(float v) {
+  v += dpp_term<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_term<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_term<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_term<0x140, 0xF>(v);  // row_mirror
+  v += dpp_term<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // sum over the workgroup; red: LDS scratch of MK_NWAVES floats
@@ -84,7 +109,10 @@ MKD bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv &&
 // record the first device error and raise the abort flag every wait checks
 MKD void mk_raise(const MkProgram &P, int code, int detail) {
   int32_t *err = P.err;
-  if (atomicCAS(err, 0, code) == 0) stci(err + 1, detail);
+  int32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong((MK_G(int32_t) *)err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+    stci(err + 1, detail);
   stci(err + 2, 1);
 }
 MKD bool mk_aborted(const MkProgram &P) { return ldci(P.err + 2) != 0; }

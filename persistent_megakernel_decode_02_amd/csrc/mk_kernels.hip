@@ -54,11 +54,12 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
     if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
     if (trace && threadIdx.x == 0) {
-      uint64_t *r = trace + (size_t)i * 4;
+      uint64_t *r = trace + (size_t)i * 8;
       r[0] = tw;
       r[1] = ts;
       r[2] = __builtin_amdgcn_s_memrealtime();
       r[3] = ((uint64_t)cu << 32) | S.epoch;
+      r[4] = r[5] = r[6] = r[7] = 0;
     }
   }
 }

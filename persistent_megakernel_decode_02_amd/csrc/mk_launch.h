@@ -17,4 +17,5 @@ int mk_occupancy_mega(int lds, int *blocks_per_cu);
 // measurement kernels (mk_measure.hip)
 size_t mk_gridsync_scratch(int n_blocks);
 int mk_launch_gridsync(int variant, int n_barriers, int n_blocks, void *d_scratch, int32_t *d_result, hipStream_t s);
+int mk_launch_lds_stream(const void *d_buf, size_t bytes, uint32_t *d_out, int n_blocks, int nw, hipStream_t s);
 int mk_launch_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int n_blocks, hipStream_t s);

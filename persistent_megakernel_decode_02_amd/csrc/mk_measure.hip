@@ -268,6 +268,39 @@ extern "C" __global__ void __launch_bounds__(SR_BLOCK) mk_stream_read_kernel(con
   }
 }
 
+// Streaming through LDS with direct global->LDS loads: `nw` waves of each
+// block issue 16-byte-per-lane loads into a 64 KiB LDS ring (1 KiB per
+// instruction), keeping up to 60 loads in flight per wave, the way the
+// megakernel's loader waves feed their page ring.
+typedef __attribute__((address_space(3))) void mk_lds_v;
+extern "C" __global__ void __launch_bounds__(SR_BLOCK) mk_lds_stream_kernel(const char *buf, size_t nbytes, uint32_t *out, int nw) {
+  extern __shared__ __attribute__((aligned(16))) char ring[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t n1k = nbytes / 1024;
+  const size_t per = (n1k + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n1k ? lo + per : n1k;
+  if (wave < nw) {
+    uint32_t issued = 0;
+    for (size_t i = lo + wave; i < hi; i += nw) {
+      __builtin_amdgcn_global_load_lds((const void *)(buf + i * 1024 + lane * 16),
+                                       (mk_lds_v *)(ring + ((i * 1024) & 65535)), 16, 0, 0);
+      if ((++issued & 3u) == 0) asm volatile("s_waitcnt vmcnt(60)" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = *(const uint32_t *)(ring + (blockIdx.x * 64) % 65536);
+}
+
+int mk_launch_lds_stream(const void *d_buf, size_t bytes, uint32_t *d_out, int n_blocks, int nw, hipStream_t st) {
+  if (hipFuncSetAttribute((const void *)mk_lds_stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 65536) !=
+      hipSuccess)
+    return -1;
+  hipLaunchKernelGGL(mk_lds_stream_kernel, dim3(n_blocks), dim3(SR_BLOCK), 65536, st, (const char *)d_buf, bytes, d_out, nw);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int mk_launch_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int n_blocks, hipStream_t st) {
   hipLaunchKernelGGL(mk_stream_read_kernel, dim3(n_blocks), dim3(SR_BLOCK), 0, st, (const mk_u32x4 *)d_buf, bytes / 16, d_out);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -44,6 +44,10 @@ struct MkCtl {
   uint32_t cw_done;             // compute-wave instruction completions
   uint32_t abort;               // a role gave up: everyone leaves
   uint32_t pad0;
+  int32_t pos[MK_RB_MAXB];      // positions of this step, read once at kernel start
+  uint32_t st_load_block;       // trace only: 100 MHz ticks the loaders spent waiting for a free page
+  uint32_t st_page_wait;        // trace only: ticks compute waves spent waiting for a landed page
+  uint32_t st_pages;            // trace only: pages issued
   float lm_v[MK_NCW * MK_RB_MAXB];
   int32_t lm_i[MK_NCW * MK_RB_MAXB];
 };
@@ -64,10 +68,54 @@ static_assert(sizeof(MkCtl) <= MK_CTL_BYTES, "LDS control block");
 
 // ------------------------------------------------------------- LDS sync
 
-MKD uint32_t lds_ld(uint32_t *p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-MKD void lds_st(uint32_t *p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); }
-// executes once per active lane: call it from a single lane
-MKD void lds_add(uint32_t *p, uint32_t v) { __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP); }
+// LDS flags: explicit address space 3 (ds_* instructions, counted by
+// lgkmcnt only, so they never wait for a loader's in-flight global->LDS
+// loads) with workgroup fences restricted to LDS.
+typedef __attribute__((address_space(3))) uint32_t mk_lds_u32;
+MKD uint32_t lds_ld(uint32_t *p) {
+  const uint32_t v = __hip_atomic_load((mk_lds_u32 *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return v;
+}
+MKD void lds_st(uint32_t *p, uint32_t v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store((mk_lds_u32 *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// The loader's own flag accesses are written as ds instructions in inline
+// assembly.  Compiled LDS accesses would make the compiler wait for every
+// global->LDS load still in flight (those write LDS and are counted by
+// vmcnt, and it cannot prove the flag and the pages do not overlap); the
+// loader has already waited for exactly the pages it publishes.
+MKD uint32_t lds_off(const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p; }
+MKD void lds_publish(uint32_t *p, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
+}
+MKD uint32_t lds_peek(uint32_t *p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
+  return v;
+}
+MKD void lds_add(uint32_t *p, uint32_t v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_fetch_add((mk_lds_u32 *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// read-only program data (instruction lists, pointer tables) through the
+// constant address space: scalar loads, counted by lgkmcnt, never by vmcnt
+template <class T>
+MKD T cld(const T *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  T v;
+  const __attribute__((address_space(4))) uint32_t *src = (const __attribute__((address_space(4))) uint32_t *)p;
+  uint32_t *dst = reinterpret_cast<uint32_t *>(&v);
+  static_assert(sizeof(T) % 4 == 0, "word-sized records");
+#pragma unroll
+  for (unsigned i = 0; i < sizeof(T) / 4; ++i) dst[i] = src[i];
+  return v;
+#else
+  return *p;
+#endif
+}
 
 // Spin (one wave, uniform) until *p >= v.  false: the kernel is aborting.
 MKD bool role_wait(const MkRole &R, uint32_t *p, uint32_t v) {
@@ -114,12 +162,14 @@ struct MkGeo {
 
 MKD int role_batch(const MkStep &S) { return S.batch; }
 
-MKD bool mk_geo(const MkProgram &P, const MkStep &S, const MkInstr &in, MkGeo &g) {
+MKD bool mk_geo(const MkProgram &P, const MkStep &S, const MkCtl *ctl, const MkInstr &in, MkGeo &g) {
   g.w1 = nullptr;
   g.d = P.d;
   g.kc = g.vc = nullptr;
   g.p = g.t0 = g.t1 = g.bp = 0;
-  const MkLayerW *LW = in.op != MKOP_LMHEAD ? &P.layers[in.layer] : nullptr;
+  MkLayerW LWv;
+  if (in.op != MKOP_LMHEAD) LWv = cld(&P.layers[in.layer]);
+  const MkLayerW *LW = &LWv;
   switch (in.op) {
     case MKOP_QKV: {
       g.K = P.H;
@@ -154,7 +204,7 @@ MKD bool mk_geo(const MkProgram &P, const MkStep &S, const MkInstr &in, MkGeo &g
       break;
     case MKOP_ATTN: {
       const int b = in.r0, gg = in.r1, NS = in.nsplit;
-      const int p = S.positions[b];
+      const int p = ctl->pos[b];
       if (p < 0 || p >= P.max_ctx) return false;
       const int n = p + 1;
       g.bp = MK_PAGE / (2 * P.d);
@@ -206,7 +256,7 @@ MKD void loader_publish_all(const MkRole &R, LoaderState &L, int lid) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   while (L.pub < L.iss) {
     const uint32_t s = (uint32_t)lid + MK_NLW * L.pub;
-    lds_st(&R.ctl->pg_ready[s % R.np], s + 1u);
+    lds_publish(&R.ctl->pg_ready[s % R.np], s + 1u);
     ++L.pub;
   }
 }
@@ -227,9 +277,12 @@ MKD bool loader_page(const MkRole &R, LoaderState &L, int lid, uint32_t s, const
   const int slot = (int)(s % (uint32_t)R.np);
   if (s >= (uint32_t)R.np) {
     const uint32_t need = s - (uint32_t)R.np + 1u;
-    if ((int32_t)(lds_ld(&R.ctl->pg_done[slot]) - need) < 0) {
+    if ((int32_t)(lds_peek(&R.ctl->pg_done[slot]) - need) < 0) {
       loader_publish_all(R, L, lid);  // never block while holding landed pages
+      const uint64_t t0 = R.P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
       if (!role_wait(R, &R.ctl->pg_done[slot], need)) return false;
+      if (R.P.trace && (threadIdx.x & 63) == 0)
+        lds_add(&R.ctl->st_load_block, (uint32_t)(__builtin_amdgcn_s_memrealtime() - t0));
     }
   }
   loader_issue(R, src, valid, slot);
@@ -237,7 +290,7 @@ MKD bool loader_page(const MkRole &R, LoaderState &L, int lid, uint32_t s, const
   if (L.iss - L.pub > MK_QMAX) {
     asm volatile("s_waitcnt vmcnt(60)" ::: "memory");  // all but the last 15 pages (60 loads) landed
     const uint32_t s0 = (uint32_t)lid + MK_NLW * L.pub;
-    lds_st(&R.ctl->pg_ready[s0 % R.np], s0 + 1u);
+    lds_publish(&R.ctl->pg_ready[s0 % R.np], s0 + 1u);
     ++L.pub;
   }
   return true;
@@ -247,7 +300,13 @@ MKD bool loader_page(const MkRole &R, LoaderState &L, int lid, uint32_t s, const
 
 MKD const char *page_wait(const MkRole &R, uint32_t s, bool *ok) {
   const int slot = (int)(s % (uint32_t)R.np);
-  *ok = role_wait(R, &R.ctl->pg_ready[slot], s + 1u);
+  if (R.P.trace && (int32_t)(lds_ld(&R.ctl->pg_ready[slot]) - (s + 1u)) < 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    *ok = role_wait(R, &R.ctl->pg_ready[slot], s + 1u);
+    if ((threadIdx.x & 63) == 0) lds_add(&R.ctl->st_page_wait, (uint32_t)(__builtin_amdgcn_s_memrealtime() - t0));
+  } else {
+    *ok = role_wait(R, &R.ctl->pg_ready[slot], s + 1u);
+  }
   return R.ring + (size_t)slot * MK_PAGE;
 }
 MKD void page_free(const MkRole &R, uint32_t s) {
@@ -266,13 +325,40 @@ MKD float dot8(const mk_u32x4 w, const float4 xa, const float4 xb, float a) {
   return a;
 }
 
-// Dot products of one weight row (ppr pages starting at page seq s) with the
-// staged vectors X[b][K], b < B.  acc[b] ends with the full sum in every lane.
-MKD bool row_dot(const MkRole &R, const MkGeo &g, uint32_t s, int B, float *acc) {
+// Lane slice of the staged input for one page of a row: chunk q of page kk
+// covers input elements kk*2048 + q*512 + lane*8 .. +8.  For one sequence
+// and rows of one page (K <= 2048) the slice is the same for every row, so
+// compute waves keep it in registers for the whole instruction.
+template <int NB>
+struct XSlice {
+  float4 v[NB][4][2];
+};
+
+template <int NB>
+MKD void load_xslice(const MkRole &R, const MkGeo &g, int B, int kk, XSlice<NB> &xs) {
   const int lane = threadIdx.x & 63;
-  float a[MK_RB_MAXB];
+  const int valid = min(MK_PAGE, g.rb - kk * MK_PAGE);
 #pragma unroll
-  for (int b = 0; b < MK_RB_MAXB; ++b) a[b] = 0.f;
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool on = b < B && q * 1024 + lane * 16 < valid;
+      const float4 *x4 = reinterpret_cast<const float4 *>(R.X + (size_t)b * g.K + kk * 2048 + q * 512 + lane * 8);
+      xs.v[b][q][0] = on ? x4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      xs.v[b][q][1] = on ? x4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// Dot products of one weight row (ppr pages starting at page seq s) with the
+// staged vectors X[b][K], b < B <= NB.  acc[b] ends with the full sum
+// (uniform).  CACHED: the input slice is `xc` (single-page rows); otherwise
+// each page's slice is read from LDS together with the page.
+template <int NB, bool CACHED>
+MKD bool row_dot(const MkRole &R, const MkGeo &g, uint32_t s, int B, const XSlice<NB> &xc, float *acc) {
+  const int lane = threadIdx.x & 63;
+  float a[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) a[b] = 0.f;
   for (int kk = 0; kk < g.ppr; ++kk) {
     bool ok;
     const char *pg = page_wait(R, s + kk, &ok);
@@ -284,22 +370,22 @@ MKD bool row_dot(const MkRole &R, const MkGeo &g, uint32_t s, int B, float *acc)
       const int off = q * 1024 + lane * 16;
       w[q] = off < valid ? *(const mk_u32x4 *)(pg + off) : mk_u32x4{0, 0, 0, 0};
     }
+    if (CACHED) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = kk * 2048 + q * 512 + lane * 8;  // first input element of this chunk
-      if (q * 1024 + lane * 16 < valid) {
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int b = 0; b < MK_RB_MAXB; ++b)
-          if (b < B) {
-            const float4 *x4 = reinterpret_cast<const float4 *>(R.X + (size_t)b * g.K + e);
-            a[b] = dot8(w[q], x4[0], x4[1], a[b]);
-          }
-      }
+        for (int b = 0; b < NB; ++b) a[b] = dot8(w[q], xc.v[b][q][0], xc.v[b][q][1], a[b]);
+    } else {
+      XSlice<NB> xl;
+      load_xslice<NB>(R, g, B, kk, xl);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a[b] = dot8(w[q], xl.v[b][q][0], xl.v[b][q][1], a[b]);
     }
     page_free(R, s + kk);
   }
 #pragma unroll
-  for (int b = 0; b < MK_RB_MAXB; ++b)
-    if (b < B) acc[b] = wave_sum(a[b]);
+  for (int b = 0; b < NB; ++b) acc[b] = wave_total(a[b]);
   return true;
 }

@@ -132,7 +132,7 @@ MKD void wave_rmsnorm(float *x, int K, const uint16_t *gain, float eps) {
   for (int i = lane; i < K; i += 64) ss = fmaf(x[i], x[i], ss);
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)K + eps);
-  for (int i = lane; i < K; i += 64) x[i] = (x[i] * r) * bf2f(gain[i]);
+  for (int i = lane; i < K; i += 64) x[i] = (x[i] * r) * bf2f(gld(gain + i));
 }
 
 // ------------------------------------------------------------ wave barrier
@@ -156,14 +156,14 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       for (int b = 0; b < B; ++b) {
         float *x = R.X + (size_t)b * H;
         if (in.op == MKOP_QKV && l == 0) {
-          const int tok = S.tokens[b];
+          const int tok = gld(S.tokens + b);
           if (tok < 0 || tok >= P.V) {
             if (lane == 0) mk_raise(P, MK_E_INPUT, b);
             role_abort(R);
             return false;
           }
           const uint16_t *e = P.embed + (size_t)tok * H;
-          for (int i = lane; i < H; i += 64) x[i] = bf2f(e[i]);
+          for (int i = lane; i < H; i += 64) x[i] = bf2f(gld(e + i));
         } else {
           const float *src = in.op == MKOP_QKV ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H
                              : in.op == MKOP_GATEUP ? A.xmid + ((size_t)l * P.B_max + b) * H
@@ -183,13 +183,13 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
         if (!stage_vec(R, R.X + (size_t)b * K, src, K, sent)) return false;
         float *rd = R.resid + (size_t)b * nr;
         if (in.op == MKOP_OPROJ && l == 0) {
-          const int tok = S.tokens[b];
+          const int tok = gld(S.tokens + b);
           if (tok < 0 || tok >= P.V) {
             if (lane == 0) mk_raise(P, MK_E_INPUT, b);
             role_abort(R);
             return false;
           }
-          for (int i = lane; i < nr; i += 64) rd[i] = bf2f(P.embed[(size_t)tok * H + in.r0 + i]);
+          for (int i = lane; i < nr; i += 64) rd[i] = bf2f(gld(P.embed + (size_t)tok * H + in.r0 + i));
         } else {
           const float *rs = in.op == MKOP_OPROJ ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H + in.r0
                                                 : A.xmid + ((size_t)l * P.B_max + b) * H + in.r0;
@@ -206,11 +206,11 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       if (!stage_vec(R, q, qkv + (size_t)gg * G * d, G * d, sent)) return false;
       if (!stage_vec(R, kc, qkv + (size_t)P.nq * d + (size_t)gg * d, d, sent)) return false;
       if (!stage_vec(R, vc, qkv + (size_t)(P.nq + P.nkv) * d + (size_t)gg * d, d, sent)) return false;
-      const float *cs = P.rope + (size_t)g.p * d;
+      const float *cs = P.rope + (size_t)g.p * d;  // read below through gld
       for (int e = lane; e < (G + 1) * half; e += 64) {
         const int j = e / half, i = e - j * half;  // j == G is the key
         float *u = j < G ? q + j * d : kc;
-        const float a = u[i], c = u[i + half], co = cs[2 * i], si = cs[2 * i + 1];
+        const float a = u[i], c = u[i + half], co = gld(cs + 2 * i), si = gld(cs + 2 * i + 1);
         float r0 = a * co - c * si, r1 = c * co + a * si;
         if (j == G) {
           r0 = bf2f(f2bf(r0));
@@ -224,8 +224,8 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
         uint16_t *K = S.kv + kv_off(P, l, 0, b, gg) + (size_t)g.p * d;
         uint16_t *V = S.kv + kv_off(P, l, 1, b, gg) + (size_t)g.p * d;
         for (int i = lane; i < d; i += 64) {
-          K[i] = f2bf(kc[i]);
-          V[i] = f2bf(vc[i]);
+          gst(K + i, f2bf(kc[i]));
+          gst(V + i, f2bf(vc[i]));
         }
       }
       return true;
@@ -334,6 +334,82 @@ MKD float *attn_wpart(const MkRole &R, int cw) {
   return R.X + (size_t)(G + 2) * d + (size_t)cw * G * (d + 2);
 }
 
+// projection rows (QKV, O, gate/up, down, LM head) of one instruction for up
+// to NB sequences
+template <int NB>
+MKD bool gemv_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, uint32_t seq0, int cw) {
+  const MkProgram &P = R.P;
+  const MkStep &S = R.S;
+  const int lane = threadIdx.x & 63;
+  const int B = S.batch, l = in.layer;
+  float best_v[NB];
+  int best_i[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    best_v[b] = -INFINITY;
+    best_i[b] = 0x7fffffff;
+  }
+  const int nr = in.r1 - in.r0;
+  // one sequence, rows of one page: the input slice stays in registers
+  XSlice<NB> xc;
+  const bool cached = NB == 1 && g.ppr == 1;
+  if (cached && cw < g.n_units) load_xslice<NB>(R, g, B, 0, xc);
+  for (int u = cw; u < g.n_units; u += MK_NCW) {
+    const uint32_t s = seq0 + (uint32_t)u * (uint32_t)g.ppu;
+    float acc[NB], acc2[NB];
+    if (cached) {
+      if (!row_dot<NB, true>(R, g, s, B, xc, acc)) return false;
+      if (in.op == MKOP_GATEUP && !row_dot<NB, true>(R, g, s + g.ppr, B, xc, acc2)) return false;
+    } else {
+      if (!row_dot<NB, false>(R, g, s, B, xc, acc)) return false;
+      if (in.op == MKOP_GATEUP && !row_dot<NB, false>(R, g, s + g.ppr, B, xc, acc2)) return false;
+    }
+    const int r = in.r0 + u;
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= B) continue;
+        switch (in.op) {
+          case MKOP_QKV:
+            stc(A.qkv + ((size_t)l * P.B_max + b) * ((P.nq + 2 * P.nkv) * P.d) + r, acc[b]);
+            break;
+          case MKOP_OPROJ:
+            stc(A.xmid + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
+            break;
+          case MKOP_GATEUP: {
+            const float a = acc[b];
+            stc(A.hbuf + ((size_t)l * P.B_max + b) * P.I + r, (a / (1.0f + expf(-a))) * acc2[b]);
+            break;
+          }
+          case MKOP_DOWN:
+            stc(A.xout + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
+            break;
+          case MKOP_LMHEAD:
+            gst(S.logits + (size_t)b * P.V + r, acc[b]);
+            break;
+        }
+      }
+    }
+    if (in.op == MKOP_LMHEAD) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (b < B && better(acc[b], r, best_v[b], best_i[b])) {
+          best_v[b] = acc[b];
+          best_i[b] = r;
+        }
+    }
+  }
+  if (in.op == MKOP_LMHEAD && lane == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b >= B) continue;
+      R.ctl->lm_v[cw * MK_RB_MAXB + b] = best_v[b];
+      R.ctl->lm_i[cw * MK_RB_MAXB + b] = best_i[b];
+    }
+  }
+  return true;
+}
+
 MKD bool compute_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, uint32_t seq0, int cw) {
   const MkProgram &P = R.P;
   const MkStep &S = R.S;
@@ -357,7 +433,9 @@ MKD bool compute_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const
     for (int u = cw; u < g.n_units; u += MK_NCW)
       if (!attn_unit(R, g, u, seq0 + (uint32_t)u * 2u, qv, acc, wsc)) return false;
     float *wp = attn_wpart(R, cw);
-    for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int j = 0; j < MK_MAX_GROUP; ++j) {
+      if (j >= G) continue;
       wp[j * (d + 2) + 2 + lane] = acc.o[j][0];
       if (d > 64) wp[j * (d + 2) + 2 + lane + 64] = acc.o[j][1];
       if (lane == 0) {
@@ -367,61 +445,7 @@ MKD bool compute_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const
     }
     return true;
   }
-  float best_v[MK_RB_MAXB];
-  int best_i[MK_RB_MAXB];
-#pragma unroll
-  for (int b = 0; b < MK_RB_MAXB; ++b) {
-    best_v[b] = -INFINITY;
-    best_i[b] = 0x7fffffff;
-  }
-  const int nr = in.r1 - in.r0;
-  for (int u = cw; u < g.n_units; u += MK_NCW) {
-    const uint32_t s = seq0 + (uint32_t)u * (uint32_t)g.ppu;
-    float acc[MK_RB_MAXB], acc2[MK_RB_MAXB];
-    if (!row_dot(R, g, s, B, acc)) return false;
-    if (in.op == MKOP_GATEUP && !row_dot(R, g, s + g.ppr, B, acc2)) return false;
-    const int r = in.r0 + u;
-    if (lane == 0) {
-#pragma unroll
-      for (int b = 0; b < MK_RB_MAXB; ++b) {
-        if (b >= B) continue;
-        switch (in.op) {
-          case MKOP_QKV:
-            stc(A.qkv + ((size_t)l * P.B_max + b) * ((P.nq + 2 * P.nkv) * P.d) + r, acc[b]);
-            break;
-          case MKOP_OPROJ:
-            stc(A.xmid + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
-            break;
-          case MKOP_GATEUP: {
-            const float a = acc[b];
-            stc(A.hbuf + ((size_t)l * P.B_max + b) * P.I + r, (a / (1.0f + expf(-a))) * acc2[b]);
-            break;
-          }
-          case MKOP_DOWN:
-            stc(A.xout + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
-            break;
-          case MKOP_LMHEAD:
-            S.logits[(size_t)b * P.V + r] = acc[b];
-            break;
-        }
-      }
-    }
-    if (in.op == MKOP_LMHEAD) {
-#pragma unroll
-      for (int b = 0; b < MK_RB_MAXB; ++b)
-        if (b < B && better(acc[b], r, best_v[b], best_i[b])) {
-          best_v[b] = acc[b];
-          best_i[b] = r;
-        }
-    }
-  }
-  if (in.op == MKOP_LMHEAD && lane == 0) {
-    for (int b = 0; b < B; ++b) {
-      R.ctl->lm_v[cw * MK_RB_MAXB + b] = best_v[b];
-      R.ctl->lm_i[cw * MK_RB_MAXB + b] = best_i[b];
-    }
-  }
-  return true;
+  return B == 1 ? gemv_instr<1>(R, in, g, A, seq0, cw) : gemv_instr<MK_RB_MAXB>(R, in, g, A, seq0, cw);
 }
 
 // ------------------------------------------------------- sync epilogues
@@ -512,10 +536,10 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
         }
       }
       if (ix == 0x7fffffff) ix = 0;
-      if (S.next) S.next[b] = ix;
+      if (S.next) gst(S.next + b, ix);
       if (S.flags & 1u) {
-        S.tokens[b] = ix;
-        S.positions[b] = S.positions[b] + 1;
+        gst(S.tokens + b, ix);
+        gst(S.positions + b, R.ctl->pos[b] + 1);
       }
     }
     return 0;
@@ -571,13 +595,13 @@ MKD void wave_signal_event(const MkRole &R, int ev, int slot) {
     stcu(P.flags + P.ev_flag_base[ev] + slot, R.S.epoch + 1u);
 }
 
-__device__ __attribute__((noinline)) void role_loader(const MkRole &R, const int32_t *list, int first, int n, int lid) {
+MKD void role_loader(const MkRole &R, const int32_t *list, int first, int n, int lid) {
   LoaderState L{0u, 0u};
   uint32_t seq = 0;
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = R.P.instr[list ? list[k] : first + k];
+    const MkInstr in = cld(&R.P.instr[list ? list[k] : first + k]);
     MkGeo g;
-    if (!mk_geo(R.P, R.S, in, g)) {
+    if (!mk_geo(R.P, R.S, R.ctl, in, g)) {
       role_abort(R);
       break;
     }
@@ -593,13 +617,13 @@ __device__ __attribute__((noinline)) void role_loader(const MkRole &R, const int
   loader_publish_all(R, L, lid);
 }
 
-__device__ __attribute__((noinline)) void role_compute(const MkRole &R, const int32_t *list, int first, int n, int cw, const MkAct &A) {
+MKD void role_compute(const MkRole &R, const int32_t *list, int first, int n, int cw, const MkAct &A) {
   uint32_t seq = 0;
   const bool sent = R.P.sync_mode == MK_SYNC_SENTINEL && !R.S.multi;
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = R.P.instr[list ? list[k] : first + k];
+    const MkInstr in = cld(&R.P.instr[list ? list[k] : first + k]);
     MkGeo g;
-    if (!mk_geo(R.P, R.S, in, g)) {
+    if (!mk_geo(R.P, R.S, R.ctl, in, g)) {
       role_abort(R);
       return;
     }
@@ -611,14 +635,14 @@ __device__ __attribute__((noinline)) void role_compute(const MkRole &R, const in
   }
 }
 
-__device__ __attribute__((noinline)) void role_sync(const MkRole &R, const int32_t *list, int first, int n, const MkAct &A) {
+MKD void role_sync(const MkRole &R, const int32_t *list, int first, int n, const MkAct &A) {
   const MkProgram &P = R.P;
   const MkStep &S = R.S;
   const bool sent = P.sync_mode == MK_SYNC_SENTINEL && !S.multi;
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = P.instr[list ? list[k] : first + k];
+    const MkInstr in = cld(&P.instr[list ? list[k] : first + k]);
     MkGeo g;
-    if (!mk_geo(P, S, in, g)) {
+    if (!mk_geo(P, S, R.ctl, in, g)) {
       if ((threadIdx.x & 63) == 0) mk_raise(P, MK_E_INPUT, 1000 + in.r0);
       role_abort(R);
       return;
@@ -640,11 +664,16 @@ __device__ __attribute__((noinline)) void role_sync(const MkRole &R, const int32
       wave_signal_event(R, in.sig_ev, in.sig_slot);
     }
     if (P.trace && (threadIdx.x & 63) == 0) {
-      uint64_t *r = P.trace + (size_t)(list ? list[k] : first + k) * 4;
+      uint64_t *r = P.trace + (size_t)(list ? list[k] : first + k) * 8;
       r[0] = tw;
       r[1] = ts;
       r[2] = __builtin_amdgcn_s_memrealtime();
       r[3] = ((uint64_t)blockIdx.x << 32) | S.epoch;
+      // stall counters so far in this launch (cumulative over the CU's list)
+      r[4] = lds_ld(&R.ctl->st_load_block);
+      r[5] = lds_ld(&R.ctl->st_page_wait);
+      r[6] = (uint64_t)(g.n_units * g.ppu);
+      r[7] = 0;
     }
   }
 }
@@ -653,6 +682,8 @@ __device__ __attribute__((noinline)) void role_sync(const MkRole &R, const int32
 MKD void role_run(const MkProgram &P, const MkStep &S, const int32_t *list, int first, int n, char *lds) {
   MkCtl *ctl = reinterpret_cast<MkCtl *>(lds);
   for (int i = threadIdx.x; i < (int)(sizeof(MkCtl) / 4); i += MK_BLOCK) reinterpret_cast<uint32_t *>(ctl)[i] = 0;
+  __syncthreads();
+  if (threadIdx.x < S.batch) ctl->pos[threadIdx.x] = gld(S.positions + threadIdx.x);
   __syncthreads();
   const int par = (P.sync_mode == MK_SYNC_SENTINEL && !S.multi) ? (int)(S.epoch & 1u) : 0;
   MkRole R{P, S, ctl, reinterpret_cast<float *>(lds + P.lds_x), reinterpret_cast<float *>(lds + P.lds_resid),

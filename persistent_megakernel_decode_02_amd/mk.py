@@ -113,6 +113,7 @@ SIGNATURES = {
     "mk_device_query": (C.c_int, [C.c_int32, C.POINTER(mk_device_info)]),
     "mk_gridsync_scratch_bytes": (C.c_size_t, [C.c_int32]),
     "mk_gridsync_bench": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "mk_lds_stream_read": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "mk_stream_read": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]),
 }
 
@@ -259,6 +260,11 @@ def mk_gridsync_scratch_bytes(n_blocks: int) -> int:
 def mk_gridsync_bench(variant: int, n_barriers: int, n_blocks: int, d_scratch: int, d_result: int, stream: int):
     _check(load_library().mk_gridsync_bench(variant, n_barriers, n_blocks, C.c_void_p(d_scratch),
                                             C.c_void_p(d_result), C.c_void_p(stream)), "mk_gridsync_bench")
+
+
+def mk_lds_stream_read(d_buf: int, nbytes: int, d_out: int, n_blocks: int, n_waves: int, stream: int):
+    _check(load_library().mk_lds_stream_read(C.c_void_p(d_buf), nbytes, C.c_void_p(d_out), n_blocks, n_waves,
+                                             C.c_void_p(stream)), "mk_lds_stream_read")
 
 
 def mk_stream_read(d_buf: int, nbytes: int, d_out: int, n_blocks: int, stream: int):
