@@ -267,7 +267,8 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   P.watchdog_ticks = 200000000u;  // 2 s
   P.lds_x = p.lds_x;
   P.lds_resid = p.lds_resid;
-  P.lds_wsc = p.lds_wsc;
+  P.lds_out = p.lds_out;
+  P.out_stride = p.out_stride;
   P.lds_ring = p.lds_ring;
   P.n_pages = p.n_pages;
   P.lds_total = p.lds_bytes;

@@ -83,6 +83,21 @@ MKD float wave_total(float v) {
   v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// DPP move where lanes without a source (masked rows) keep their own value
+template <int CTRL, int ROWMASK>
+MKD float dpp_keep(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+// wave-wide maximum with the same lane moves as wave_total
+MKD float wave_max_all(float v) {
+  v = fmaxf(v, dpp_keep<0xB1, 0xF>(v));
+  v = fmaxf(v, dpp_keep<0x4E, 0xF>(v));
+  v = fmaxf(v, dpp_keep<0x141, 0xF>(v));
+  v = fmaxf(v, dpp_keep<0x140, 0xF>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_keep<0x143, 0xC>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 // sum over the workgroup; red: LDS scratch of MK_NWAVES floats
 MKD float block_sum(float v, float *red) {

@@ -17,23 +17,29 @@
 
 // Role-specialised persistent kernel: one workgroup per CU runs the CU's
 // instruction list with loader / sync-storer / compute waves.
+// The step record is the kernel's second argument; role functions read it in
+// place in the kernarg segment, after the 8-byte program pointer.
+static_assert(alignof(MkStep) == 8, "kernarg layout: MkStep follows the program pointer at offset 8");
+MKD const MkStep *kernarg_step() {
+  return (const MkStep *)((const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr() + 8);
+}
+
 extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_role_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   const MkProgram &P = *Pp;
   if (mk_aborted(P)) return;
   const int cu = blockIdx.x;
   const int i0 = P.cu_begin[cu], i1 = P.cu_begin[cu + 1];
-  role_run(P, S, nullptr, i0, i1 - i0, lds);
+  (void)S;
+  role_run(Pp, kernarg_step(), i0, i1 - i0);
 }
 
 // The same role-specialised ops, one launch per dependency level: block i
 // runs instruction i of the level.
 extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_role_level_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   const MkProgram &P = *Pp;
   if (mk_aborted(P)) return;
   const int idx = P.level_list[P.level_begin[S.level] + blockIdx.x];
-  role_run(P, S, nullptr, idx, 1, lds);
+  role_run(Pp, kernarg_step(), idx, 1);
 }
 
 extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {

@@ -20,7 +20,6 @@
 #define MK_NCW (MK_NWAVES - MK_NLW - 1)   // compute waves (one more wave syncs and stores)
 #define MK_RB_MAXB 4                      // sequences the role engine stages per instruction
 #define MK_CTL_BYTES 1024                 // LDS control block
-#define MK_WSC (32 * MK_MAX_GROUP)        // floats of per-compute-wave scratch
 #define MK_LDS_TOTAL (160 * 1024)         // LDS of one gfx950 workgroup
 
 enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
@@ -62,7 +61,8 @@ struct MkProgram {
   int32_t n_cu, n_instr, n_levels, n_events, n_lm_parts;
   uint32_t watchdog_ticks;            // s_memrealtime ticks (100 MHz) before a wait gives up
   // role-engine LDS layout (byte offsets into dynamic LDS) and ring size
-  int32_t lds_x, lds_resid, lds_wsc, lds_ring, n_pages, lds_total;
+  int32_t lds_x, lds_resid, lds_out, lds_ring, n_pages, lds_total;
+  int32_t out_stride;                 // floats per sequence in the per-row result area
   // activations occupy one contiguous block starting at qkv; in sentinel
   // mode a second copy (the other step parity) follows at +par_stride floats
   int64_t par_stride;

@@ -4,6 +4,7 @@
 #include "mk_roles.h"
 
 #define MK_SYNC_SENTINEL MKSYNC_SENTINEL
+#define MK_XCH 16  // 16-byte chunks per lane the sync wave stages in one round (4096 floats)
 
 // ----------------------------------------------- device-coherent vector loads
 
@@ -34,60 +35,67 @@ MKD bool has_sentinel(mk_u32x4 v) {
   return v.x == MK_SENTINEL || v.y == MK_SENTINEL || v.z == MK_SENTINEL || v.w == MK_SENTINEL;
 }
 
-// One wave copies n floats (n % 4 == 0, src 16-byte aligned) from global to
-// LDS with device-coherent 16-byte loads.  With `sentinel`, words still
-// holding the sentinel are re-read until every word has been produced.
-MKD bool stage_vec(const MkRole &R, float *dst, const float *src, int n, bool sentinel) {
+// abort / watchdog check inside a sync-wave poll; false: give up
+MKD bool poll_check(const MkRole &R, uint64_t t0, int code) {
+  if (lds_ld(&R.ctl->abort) || mk_aborted(R.P)) {
+    role_abort(R);
+    return false;
+  }
+  if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)R.P.watchdog_ticks) {
+    if ((threadIdx.x & 63) == 0) mk_raise(R.P, MK_E_TIMEOUT, code);
+    role_abort(R);
+    return false;
+  }
+  return true;
+}
+
+// Load up to MK_XCH 16-byte chunks per lane of the fp32 vector src[0, n)
+// (chunk j of a lane covers elements (j * 64 + lane) * 4 .. + 4) with
+// device-coherent loads, all in flight at once.  With `sentinel`, chunks
+// still holding the sentinel are re-read until every word has been produced.
+MKD bool load_vec(const MkRole &R, const float *src, int n, bool sentinel, mk_u32x4 (&v)[MK_XCH]) {
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t rs = mk_rsrc(src, (uint32_t)n * 4u);
-  constexpr int NB = 4;
-  for (int base = 0; base < n; base += 64 * 4 * NB) {
-    mk_u32x4 v[NB];
+  const int nch = (n + 255) / 256;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int e = base + (j * 64 + lane) * 4;
-      v[j] = ldc16(rs, e * 4);  // out-of-range offsets read 0 (buffer bounds)
-    }
-    if (sentinel) {
-      uint64_t t0 = 0;
-      uint32_t spins = 0;
-      while (true) {
-        bool miss = false;
+  for (int j = 0; j < MK_XCH; ++j)
+    if (j < nch) v[j] = ldc16(rs, (j * 64 + lane) * 16);  // out-of-range offsets read 0 (buffer bounds)
+  if (!sentinel) return true;
+  uint64_t t0 = 0;
+  uint32_t spins = 0;
+  while (true) {
+    bool miss = false;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int e = base + (j * 64 + lane) * 4;
-          miss = miss || (e < n && has_sentinel(v[j]));
-        }
-        if (!__any(miss)) break;
-        if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
-        __builtin_amdgcn_s_sleep(1);
-        if ((++spins & 63u) == 0) {
-          if (lds_ld(&R.ctl->abort) || mk_aborted(R.P)) {
-            role_abort(R);
-            return false;
-          }
-          if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)R.P.watchdog_ticks) {
-            if (lane == 0) mk_raise(R.P, MK_E_TIMEOUT, 0x20000);
-            role_abort(R);
-            return false;
-          }
-        }
+    for (int j = 0; j < MK_XCH; ++j)
+      if (j < nch) miss = miss || ((j * 64 + lane) * 4 < n && has_sentinel(v[j]));
+    if (!__any(miss)) return true;
+    if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_s_sleep(1);
+    if ((++spins & 63u) == 0 && !poll_check(R, t0, 0x20000)) return false;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int e = base + (j * 64 + lane) * 4;
-          if (e < n && has_sentinel(v[j])) v[j] = ldc16(rs, e * 4);
-        }
-      }
-    }
+    for (int j = 0; j < MK_XCH; ++j)
+      if (j < nch && (j * 64 + lane) * 4 < n && has_sentinel(v[j])) v[j] = ldc16(rs, (j * 64 + lane) * 16);
+  }
+}
+
+MKD void store_vec(float *dst, int n, const mk_u32x4 (&v)[MK_XCH]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int e = base + (j * 64 + lane) * 4;
-      if (e < n) {
-        float4 f = make_float4(__uint_as_float(v[j].x), __uint_as_float(v[j].y), __uint_as_float(v[j].z),
-                               __uint_as_float(v[j].w));
-        *reinterpret_cast<float4 *>(dst + e) = f;
-      }
-    }
+  for (int j = 0; j < MK_XCH; ++j) {
+    const int e = (j * 64 + lane) * 4;
+    if (e < n)
+      *reinterpret_cast<float4 *>(dst + e) = make_float4(__uint_as_float(v[j].x), __uint_as_float(v[j].y),
+                                                         __uint_as_float(v[j].z), __uint_as_float(v[j].w));
+  }
+}
+
+// Copy n floats (n % 4 == 0) from global to LDS, MK_XCH chunks per lane per round.
+MKD bool stage_vec(const MkRole &R, float *dst, const float *src, int n, bool sentinel) {
+  for (int base = 0; base < n; base += 256 * MK_XCH) {
+    mk_u32x4 v[MK_XCH];
+    const int m = min(n - base, 256 * MK_XCH);
+    if (!load_vec(R, src + base, m, sentinel, v)) return false;
+    store_vec(dst + base, m, v);
   }
   return true;
 }
@@ -106,17 +114,7 @@ MKD bool stage_scalars(const MkRole &R, float *dst, const float *src, int n, boo
         if (!__any(miss)) break;
         if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
         __builtin_amdgcn_s_sleep(1);
-        if ((++spins & 63u) == 0) {
-          if (lds_ld(&R.ctl->abort) || mk_aborted(R.P)) {
-            role_abort(R);
-            return false;
-          }
-          if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)R.P.watchdog_ticks) {
-            if (lane == 0) mk_raise(R.P, MK_E_TIMEOUT, 0x20001);
-            role_abort(R);
-            return false;
-          }
-        }
+        if ((++spins & 63u) == 0 && !poll_check(R, t0, 0x20001)) return false;
         if (miss) v = ldc(src + i);
       }
     }
@@ -125,24 +123,64 @@ MKD bool stage_scalars(const MkRole &R, float *dst, const float *src, int n, boo
   return true;
 }
 
-// In-place RMSNorm of one staged vector by one wave
-MKD void wave_rmsnorm(float *x, int K, const uint16_t *gain, float eps) {
+// bf16 values of a length-n vector in the lane layout of load_vec (4 per chunk)
+MKD void load_bf16_chunks(const uint16_t *p, int n, uint32_t (&g)[MK_XCH][2]) {
   const int lane = threadIdx.x & 63;
-  float ss = 0.f;
-  for (int i = lane; i < K; i += 64) ss = fmaf(x[i], x[i], ss);
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)K + eps);
-  for (int i = lane; i < K; i += 64) x[i] = (x[i] * r) * bf2f(gld(gain + i));
+#pragma unroll
+  for (int j = 0; j < MK_XCH; ++j) {
+    const int e = (j * 64 + lane) * 4;
+    if (e < n) {
+      const uint64_t w = gld(reinterpret_cast<const uint64_t *>(p + e));
+      g[j][0] = (uint32_t)w;
+      g[j][1] = (uint32_t)(w >> 32);
+    } else {
+      g[j][0] = g[j][1] = 0u;
+    }
+  }
 }
 
-// ------------------------------------------------------------ wave barrier
-// (sync wave waiting on its own earlier LDS writes before publishing: the
-// release store in lds_st orders them)
+// RMSNorm of a vector held in registers (load_vec layout, n <= 256 * MK_XCH),
+// gains g; result written to LDS dst
+MKD void norm_store(float *dst, int n, mk_u32x4 (&v)[MK_XCH], const uint32_t (&g)[MK_XCH][2], float eps) {
+  const int lane = threadIdx.x & 63;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MK_XCH; ++j) {
+    const int e = (j * 64 + lane) * 4;
+    if (e < n) {
+      const float a = __uint_as_float(v[j].x), b = __uint_as_float(v[j].y), c = __uint_as_float(v[j].z),
+                  d = __uint_as_float(v[j].w);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+      ss = fmaf(c, c, ss);
+      ss = fmaf(d, d, ss);
+    }
+  }
+  ss = wave_total(ss);
+  const float r = 1.0f / sqrtf(ss / (float)n + eps);
+#pragma unroll
+  for (int j = 0; j < MK_XCH; ++j) {
+    const int e = (j * 64 + lane) * 4;
+    if (e < n)
+      *reinterpret_cast<float4 *>(dst + e) = make_float4(
+          (__uint_as_float(v[j].x) * r) * bf_lo(g[j][0]), (__uint_as_float(v[j].y) * r) * bf_hi(g[j][0]),
+          (__uint_as_float(v[j].z) * r) * bf_lo(g[j][1]), (__uint_as_float(v[j].w) * r) * bf_hi(g[j][1]));
+  }
+}
 
 // ------------------------------------------------------- sync-wave staging
 
-// returns false on abort (error already raised)
-MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, bool sent) {
+MKD bool normed_op(int op) { return op == MKOP_QKV || op == MKOP_GATEUP || op == MKOP_LMHEAD; }
+
+MKD const uint16_t *norm_gain(const MkProgram &P, const MkInstr &in) {
+  return in.op == MKOP_QKV ? P.layers[in.layer].attn_norm
+                           : in.op == MKOP_GATEUP ? P.layers[in.layer].mlp_norm : P.final_norm;
+}
+
+// returns false on abort (error already raised).  `gain` holds the norm
+// gains of a normed op, loaded before the dependency wait.
+MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, bool sent,
+                    const uint32_t (&gain)[MK_XCH][2]) {
   const MkProgram &P = R.P;
   const MkStep &S = R.S;
   const int lane = threadIdx.x & 63;
@@ -151,10 +189,8 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
     case MKOP_QKV:
     case MKOP_GATEUP:
     case MKOP_LMHEAD: {
-      const uint16_t *gain = in.op == MKOP_QKV ? P.layers[l].attn_norm
-                             : in.op == MKOP_GATEUP ? P.layers[l].mlp_norm : P.final_norm;
       for (int b = 0; b < B; ++b) {
-        float *x = R.X + (size_t)b * H;
+        mk_u32x4 v[MK_XCH];
         if (in.op == MKOP_QKV && l == 0) {
           const int tok = gld(S.tokens + b);
           if (tok < 0 || tok >= P.V) {
@@ -162,15 +198,18 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
             role_abort(R);
             return false;
           }
-          const uint16_t *e = P.embed + (size_t)tok * H;
-          for (int i = lane; i < H; i += 64) x[i] = bf2f(gld(e + i));
+          uint32_t e2[MK_XCH][2];
+          load_bf16_chunks(P.embed + (size_t)tok * H, H, e2);
+#pragma unroll
+          for (int j = 0; j < MK_XCH; ++j) v[j] = mk_u32x4{e2[j][0] << 16, e2[j][0] & 0xffff0000u, e2[j][1] << 16,
+                                                           e2[j][1] & 0xffff0000u};
         } else {
           const float *src = in.op == MKOP_QKV ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H
                              : in.op == MKOP_GATEUP ? A.xmid + ((size_t)l * P.B_max + b) * H
                                                     : A.xout + ((size_t)(P.L - 1) * P.B_max + b) * H;
-          if (!stage_vec(R, x, src, H, sent)) return false;
+          if (!load_vec(R, src, H, sent, v)) return false;
         }
-        wave_rmsnorm(x, H, gain, P.eps);
+        norm_store(R.X + (size_t)b * H, H, v, gain, P.eps);
       }
       return true;
     }
@@ -178,9 +217,6 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
     case MKOP_DOWN: {
       const int K = g.K, nr = in.r1 - in.r0;
       for (int b = 0; b < B; ++b) {
-        const float *src = in.op == MKOP_OPROJ ? A.attn + ((size_t)l * P.B_max + b) * K
-                                               : A.hbuf + ((size_t)l * P.B_max + b) * K;
-        if (!stage_vec(R, R.X + (size_t)b * K, src, K, sent)) return false;
         float *rd = R.resid + (size_t)b * nr;
         if (in.op == MKOP_OPROJ && l == 0) {
           const int tok = gld(S.tokens + b);
@@ -191,10 +227,14 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
           }
           for (int i = lane; i < nr; i += 64) rd[i] = bf2f(gld(P.embed + (size_t)tok * H + in.r0 + i));
         } else {
+          // residual rows first: they were complete before this instruction's input
           const float *rs = in.op == MKOP_OPROJ ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H + in.r0
                                                 : A.xmid + ((size_t)l * P.B_max + b) * H + in.r0;
           if (!stage_scalars(R, rd, rs, nr, sent)) return false;
         }
+        const float *src = in.op == MKOP_OPROJ ? A.attn + ((size_t)l * P.B_max + b) * K
+                                               : A.hbuf + ((size_t)l * P.B_max + b) * K;
+        if (!stage_vec(R, R.X + (size_t)b * K, src, K, sent)) return false;
       }
       return true;
     }
@@ -207,6 +247,8 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       if (!stage_vec(R, kc, qkv + (size_t)P.nq * d + (size_t)gg * d, d, sent)) return false;
       if (!stage_vec(R, vc, qkv + (size_t)(P.nq + P.nkv) * d + (size_t)gg * d, d, sent)) return false;
       const float *cs = P.rope + (size_t)g.p * d;  // read below through gld
+      // queries are pre-scaled by log2(e) / sqrt(d): scores come out in base 2
+      const float qs = 1.4426950408889634f / sqrtf((float)d);
       for (int e = lane; e < (G + 1) * half; e += 64) {
         const int j = e / half, i = e - j * half;  // j == G is the key
         float *u = j < G ? q + j * d : kc;
@@ -215,6 +257,9 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
         if (j == G) {
           r0 = bf2f(f2bf(r0));
           r1 = bf2f(f2bf(r1));
+        } else {
+          r0 *= qs;
+          r1 *= qs;
         }
         u[i] = r0;
         u[i + half] = r1;
@@ -235,96 +280,143 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
   }
 }
 
-// ------------------------------------------------------- compute waves
+// --------------------------------------------------------- compute waves
 
-struct AttnAcc {
-  float m[MK_MAX_GROUP], l[MK_MAX_GROUP];
-  float o[MK_MAX_GROUP][2];  // dims lane and lane + 64
+// results of one wave, one lane per row: lane t holds the wave's t-th row
+// of the current 64-row chunk; written to R.out[b][unit] when full
+struct RowRes {
+  float v[MK_RB_MAXB];
+  int t, ubase;
 };
-
-// One block of bp key positions: scores, online softmax update, values.
-MKD bool attn_unit(const MkRole &R, const MkGeo &g, int u, uint32_t s, const float (*qv)[8], AttnAcc &acc, float *wsc) {
+MKD void rowres_init(RowRes &rr, int cw) {
+#pragma unroll
+  for (int b = 0; b < MK_RB_MAXB; ++b) rr.v[b] = 0.f;
+  rr.t = 0;
+  rr.ubase = cw;
+}
+template <int NB>
+MKD void rowres_put(const MkRole &R, RowRes &rr, const float *r, int B) {
   const int lane = threadIdx.x & 63;
-  const int d = g.d, G = R.P.G, bp = g.bp;
-  const int lpp = d / 8, ppi = 64 / lpp;  // lanes per position, positions per pass
-  const int ta = g.t0 + u * bp;
-  const int npos = min(bp, g.t1 - ta);
-  bool ok;
-  char *kp = const_cast<char *>(page_wait(R, s, &ok));
-  if (!ok) return false;
-  char *vp = const_cast<char *>(page_wait(R, s + 1, &ok));
-  if (!ok) return false;
-  // the page holds the cache's old slot for the current position: use the new key/value
-  if (ta <= g.p && g.p < ta + npos) {
-    const int row = g.p - ta;
-    const float *kc = R.X + G * d, *vc = kc + d;
-    uint16_t *kr = reinterpret_cast<uint16_t *>(kp + (size_t)row * 2 * d);
-    uint16_t *vr = reinterpret_cast<uint16_t *>(vp + (size_t)row * 2 * d);
-    for (int i = lane; i < d; i += 64) {
-      kr[i] = f2bf(kc[i]);
-      vr[i] = f2bf(vc[i]);
-    }
-  }
-  const float scale = 1.0f / sqrtf((float)d);
-  // scores: lpp lanes per position, 8 dims per lane
-  const int c8 = (lane % lpp) * 8, pin = lane / lpp;
-  for (int pass = 0; pass < bp / ppi; ++pass) {
-    const int row = pass * ppi + pin;
-    float sc[MK_MAX_GROUP];
-    const mk_u32x4 w = row < npos ? *reinterpret_cast<const mk_u32x4 *>(kp + (size_t)row * 2 * d + c8 * 2)
-                                  : mk_u32x4{0, 0, 0, 0};
-    const float k8[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
 #pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j) {
+  for (int b = 0; b < NB; ++b) rr.v[b] = lane == rr.t ? r[b] : rr.v[b];
+  if (++rr.t == 64) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < B) R.out[(size_t)b * R.P.out_stride + rr.ubase + MK_NCW * lane] = rr.v[b];
+    rr.t = 0;
+    rr.ubase += 64 * MK_NCW;
+  }
+}
+template <int NB>
+MKD void rowres_flush(const MkRole &R, RowRes &rr, int B) {
+  const int lane = threadIdx.x & 63;
+  if (lane < rr.t) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < B) R.out[(size_t)b * R.P.out_stride + rr.ubase + MK_NCW * lane] = rr.v[b];
+  }
+}
+
+MKD float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+
+// One sequence, whole pages.  ONE: rows are one page, the input slice stays
+// in registers; TWO: gate and up rows, SiLU(gate) * up per unit.
+template <bool ONE, bool TWO>
+MKD bool gemv_fast(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {
+  const int ppr = ONE ? 1 : g.ppr, ppu = ONE ? (TWO ? 2 : 1) : g.ppu;
+  XSlice xc;
+  if (ONE && cw < g.n_units) load_xslice(R.X, 0, xc);
+  RowRes rr;
+  rowres_init(rr, cw);
+  uint32_t s = seq0 + (uint32_t)(cw * ppu);
+  int slot = ring_add(slot0, cw * ppu, R.np);
+  const int ustep = (MK_NCW - 1) * ppu;  // pages of the other waves' units between two of ours
+  for (int u = cw; u < g.n_units; u += MK_NCW) {
+    float tot[2];
+#pragma unroll
+    for (int h = 0; h < (TWO ? 2 : 1); ++h) {
       float a = 0.f;
-      if (j < G) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf(qv[j][e], k8[e], a);
+      for (int kk = 0; kk < ppr; ++kk) {
+        if (!page_wait(R, slot, s)) return false;
+        const char *pg = R.ring + (size_t)slot * MK_PAGE;
+        if (ONE) {
+          a = page_dot(pg, xc, a);
+        } else {
+          XSlice xs;
+          load_xslice(R.X, kk, xs);
+          a = page_dot(pg, xs, a);
+        }
+        page_free(R, slot, s);
+        ++s;
+        if (++slot == R.np) slot = 0;
       }
-      sc[j] = a;
+      tot[h] = wave_total(a);
     }
+    float r = tot[0];
+    if (TWO) r = silu_mul(tot[0], tot[1]);
+    rowres_put<1>(R, rr, &r, 1);
+    s += (uint32_t)ustep;
+    slot = ring_add(slot, ustep, R.np);
+  }
+  rowres_flush<1>(R, rr, 1);
+  return true;
+}
+
+// Any batch (<= MK_RB_MAXB) and partial pages (rows shorter than a page,
+// or not a whole number of pages): bounds-checked reads.
+template <bool TWO>
+MKD bool gemv_general(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw, int B) {
+  const int lane = threadIdx.x & 63;
+  RowRes rr;
+  rowres_init(rr, cw);
+  uint32_t s = seq0 + (uint32_t)(cw * g.ppu);
+  int slot = ring_add(slot0, cw * g.ppu, R.np);
+  const int ustep = (MK_NCW - 1) * g.ppu;
+  for (int u = cw; u < g.n_units; u += MK_NCW) {
+    float tot[2][MK_RB_MAXB];
 #pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j) {
-      if (j < G) {
-        for (int o = 1; o < lpp; o <<= 1) sc[j] += __shfl_xor(sc[j], o, 64);
+    for (int h = 0; h < (TWO ? 2 : 1); ++h) {
+      float a[MK_RB_MAXB];
+#pragma unroll
+      for (int b = 0; b < MK_RB_MAXB; ++b) a[b] = 0.f;
+      for (int kk = 0; kk < g.ppr; ++kk) {
+        if (!page_wait(R, slot, s)) return false;
+        const char *pg = R.ring + (size_t)slot * MK_PAGE;
+        const int valid = g.full ? MK_PAGE : mk_page_valid(g, u, kk);
+        mk_u32x4 w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int off = q * 1024 + lane * 16;
+          w[q] = off < valid ? *reinterpret_cast<const mk_u32x4 *>(pg + off) : mk_u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int b = 0; b < MK_RB_MAXB; ++b) {
+          if (b >= B) continue;
+          const float *x = R.X + (size_t)b * g.K + kk * 2048;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int off = q * 1024 + lane * 16;
+            const bool on = off < valid;
+            const float4 *x4 = reinterpret_cast<const float4 *>(x + q * 512 + lane * 8);
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            a[b] = dot8(w[q], on ? x4[0] : z, on ? x4[1] : z, a[b]);
+          }
+        }
+        page_free(R, slot, s);
+        ++s;
+        if (++slot == R.np) slot = 0;
       }
+#pragma unroll
+      for (int b = 0; b < MK_RB_MAXB; ++b) tot[h][b] = b < B ? wave_total(a[b]) : 0.f;
     }
-    if ((lane % lpp) == 0) {
+    float r[MK_RB_MAXB];
 #pragma unroll
-      for (int j = 0; j < MK_MAX_GROUP; ++j)
-        if (j < G) wsc[j * 32 + row] = row < npos ? sc[j] * scale : -INFINITY;
-    }
+    for (int b = 0; b < MK_RB_MAXB; ++b) r[b] = TWO ? silu_mul(tot[0][b], tot[1][b]) : tot[0][b];
+    rowres_put<MK_RB_MAXB>(R, rr, r, B);
+    s += (uint32_t)ustep;
+    slot = ring_add(slot, ustep, R.np);
   }
-  page_free(R, s);
-  // online softmax update; lane i < npos owns position i
-#pragma unroll
-  for (int j = 0; j < MK_MAX_GROUP; ++j) {
-    if (j >= G) continue;
-    const float sv = lane < npos ? wsc[j * 32 + lane] : -INFINITY;
-    const float mb = wave_max(sv);
-    const float mn = fmaxf(acc.m[j], mb);
-    const float corr = acc.m[j] == -INFINITY ? 0.f : expf(acc.m[j] - mn);
-    const float pv = lane < npos ? expf(sv - mn) : 0.f;
-    acc.l[j] = acc.l[j] * corr + wave_sum(pv);
-    acc.o[j][0] *= corr;
-    acc.o[j][1] *= corr;
-    acc.m[j] = mn;
-    if (lane < bp) wsc[j * 32 + lane] = pv;
-  }
-  // weighted values: lane owns dims lane (and lane + 64 when d = 128)
-  const uint16_t *vr = reinterpret_cast<const uint16_t *>(vp);
-  for (int i = 0; i < npos; ++i) {
-    const float v0 = bf2f(vr[(size_t)i * d + lane]);
-    const float v1 = d > 64 ? bf2f(vr[(size_t)i * d + lane + 64]) : 0.f;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j)
-      if (j < G) {
-        const float pj = wsc[j * 32 + i];
-        acc.o[j][0] = fmaf(pj, v0, acc.o[j][0]);
-        acc.o[j][1] = fmaf(pj, v1, acc.o[j][1]);
-      }
-  }
-  page_free(R, s + 1);
+  rowres_flush<MK_RB_MAXB>(R, rr, B);
   return true;
 }
 
@@ -334,132 +426,162 @@ MKD float *attn_wpart(const MkRole &R, int cw) {
   return R.X + (size_t)(G + 2) * d + (size_t)cw * G * (d + 2);
 }
 
-// projection rows (QKV, O, gate/up, down, LM head) of one instruction for up
-// to NB sequences
-template <int NB>
-MKD bool gemv_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, uint32_t seq0, int cw) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
+// sum over the lpp (8 or 16) consecutive lanes that hold one key position
+MKD float group_sum(float v, int lpp) {
+  v += dpp_term<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_term<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_term<0x141, 0xF>(v);  // row_half_mirror: the other quad of the half row
+  if (lpp == 16) v += dpp_term<0x140, 0xF>(v);  // row_mirror: the other half row
+  return v;
+}
+
+MKD float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Decode attention over this instruction's key blocks (flash-decoding split
+// of the megakernel page, section 2.6's attention instruction).  Lanes come
+// in groups of lpp = d/8, one group per key position, 8 dims per lane; each
+// group keeps its own running max / sum / output for the positions it saw
+// (scores in base 2: the staged queries carry log2(e)/sqrt(d)), and the
+// groups of the wave are merged at the end into one partial per q head.
+MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {
   const int lane = threadIdx.x & 63;
-  const int B = S.batch, l = in.layer;
-  float best_v[NB];
-  int best_i[NB];
+  const int d = g.d, G = R.P.G;
+  const int lpp = d / 8, ppi = 64 / lpp;
+  const int c8 = (lane % lpp) * 8, pin = lane / lpp;
+  float qv[MK_MAX_GROUP][8];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    best_v[b] = -INFINITY;
-    best_i[b] = 0x7fffffff;
+  for (int j = 0; j < MK_MAX_GROUP; ++j) {
+    const float4 *q4 = reinterpret_cast<const float4 *>(R.X + j * d + c8);
+    const float4 a = j < G ? q4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = j < G ? q4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    qv[j][0] = a.x, qv[j][1] = a.y, qv[j][2] = a.z, qv[j][3] = a.w;
+    qv[j][4] = b.x, qv[j][5] = b.y, qv[j][6] = b.z, qv[j][7] = b.w;
   }
-  const int nr = in.r1 - in.r0;
-  // one sequence, rows of one page: the input slice stays in registers
-  XSlice<NB> xc;
-  const bool cached = NB == 1 && g.ppr == 1;
-  if (cached && cw < g.n_units) load_xslice<NB>(R, g, B, 0, xc);
-  for (int u = cw; u < g.n_units; u += MK_NCW) {
-    const uint32_t s = seq0 + (uint32_t)u * (uint32_t)g.ppu;
-    float acc[NB], acc2[NB];
-    if (cached) {
-      if (!row_dot<NB, true>(R, g, s, B, xc, acc)) return false;
-      if (in.op == MKOP_GATEUP && !row_dot<NB, true>(R, g, s + g.ppr, B, xc, acc2)) return false;
-    } else {
-      if (!row_dot<NB, false>(R, g, s, B, xc, acc)) return false;
-      if (in.op == MKOP_GATEUP && !row_dot<NB, false>(R, g, s + g.ppr, B, xc, acc2)) return false;
-    }
-    const int r = in.r0 + u;
-    if (lane == 0) {
+  float m[MK_MAX_GROUP], l[MK_MAX_GROUP], o[MK_MAX_GROUP][8];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= B) continue;
-        switch (in.op) {
-          case MKOP_QKV:
-            stc(A.qkv + ((size_t)l * P.B_max + b) * ((P.nq + 2 * P.nkv) * P.d) + r, acc[b]);
-            break;
-          case MKOP_OPROJ:
-            stc(A.xmid + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
-            break;
-          case MKOP_GATEUP: {
-            const float a = acc[b];
-            stc(A.hbuf + ((size_t)l * P.B_max + b) * P.I + r, (a / (1.0f + expf(-a))) * acc2[b]);
-            break;
-          }
-          case MKOP_DOWN:
-            stc(A.xout + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * nr + u] + acc[b]);
-            break;
-          case MKOP_LMHEAD:
-            gst(S.logits + (size_t)b * P.V + r, acc[b]);
-            break;
-        }
+  for (int j = 0; j < MK_MAX_GROUP; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  }
+  const float *kn = R.X + G * d, *vn = kn + d;  // this step's key and value (bf16-rounded)
+  uint32_t s = seq0 + (uint32_t)(cw * 2);
+  int slot = ring_add(slot0, cw * 2, R.np);
+  for (int u = cw; u < g.n_units; u += MK_NCW) {
+    const int ta = g.t0 + u * g.bp;
+    const int npos = min(g.bp, g.t1 - ta);
+    const bool here = ta <= g.p && g.p < ta + npos;  // the block holds this step's position
+    const int vslot = slot + 1 == R.np ? 0 : slot + 1;
+    if (!page_wait(R, slot, s) || !page_wait(R, vslot, s + 1)) return false;
+    const char *kp = R.ring + (size_t)slot * MK_PAGE, *vp = R.ring + (size_t)vslot * MK_PAGE;
+    float sc[4][MK_MAX_GROUP];
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int row = pass * ppi + pin;
+      const mk_u32x4 kw = row < npos ? *reinterpret_cast<const mk_u32x4 *>(kp + (size_t)row * 2 * d + c8 * 2)
+                                     : mk_u32x4{0, 0, 0, 0};
+      float k8[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
+                     bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
+      if (here && ta + row == g.p) {  // the page holds the slot's previous contents
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k8[e] = kn[c8 + e];
+      }
+#pragma unroll
+      for (int j = 0; j < MK_MAX_GROUP; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(qv[j][e], k8[e], a);
+        a = group_sum(a, lpp);
+        sc[pass][j] = row < npos ? a : -INFINITY;
       }
     }
-    if (in.op == MKOP_LMHEAD) {
+    page_free(R, slot, s);
+    float pr[4][MK_MAX_GROUP];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (b < B && better(acc[b], r, best_v[b], best_i[b])) {
-          best_v[b] = acc[b];
-          best_i[b] = r;
-        }
+    for (int j = 0; j < MK_MAX_GROUP; ++j) {
+      const float mb = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
+      const float mn = fmaxf(m[j], mb);
+      const float c = m[j] == mn ? 1.f : exp2_fast(m[j] - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        pr[pass][j] = sc[pass][j] == -INFINITY ? 0.f : exp2_fast(sc[pass][j] - mn);
+        ls += pr[pass][j];
+      }
+      l[j] = fmaf(l[j], c, ls);
+      m[j] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] *= c;
     }
-  }
-  if (in.op == MKOP_LMHEAD && lane == 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b >= B) continue;
-      R.ctl->lm_v[cw * MK_RB_MAXB + b] = best_v[b];
-      R.ctl->lm_i[cw * MK_RB_MAXB + b] = best_i[b];
+    for (int pass = 0; pass < 4; ++pass) {
+      const int row = pass * ppi + pin;
+      const mk_u32x4 vw = row < npos ? *reinterpret_cast<const mk_u32x4 *>(vp + (size_t)row * 2 * d + c8 * 2)
+                                     : mk_u32x4{0, 0, 0, 0};
+      float v8[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
+                     bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+      if (here && ta + row == g.p) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = vn[c8 + e];
+      }
+#pragma unroll
+      for (int j = 0; j < MK_MAX_GROUP; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pr[pass][j], v8[e], o[j][e]);
+    }
+    page_free(R, vslot, s + 1);
+    s += (uint32_t)(MK_NCW * 2);
+    slot = ring_add(slot, MK_NCW * 2, R.np);
+  }
+  // merge the lane groups: rescale to the wave max, then sum groups lane-wise
+  float *wp = attn_wpart(R, cw);
+#pragma unroll
+  for (int j = 0; j < MK_MAX_GROUP; ++j) {
+    if (j >= G) continue;
+    const float M = wave_max_all(m[j]);
+    const float f = m[j] == -INFINITY ? 0.f : exp2_fast(m[j] - M);
+    const float L = wave_total(l[j] * f) * (1.0f / (float)lpp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[j][e] * f;
+      if (lpp == 8) v += dpp_term<0x128, 0xF>(v);  // row_ror:8: the other 8-lane group of the row
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      o[j][e] = v;
+    }
+    if (lane < lpp) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wp[j * (d + 2) + 2 + c8 + e] = o[j][e];
+    }
+    if (lane == 0) {
+      wp[j * (d + 2)] = M;
+      wp[j * (d + 2) + 1] = L;
     }
   }
   return true;
 }
 
-MKD bool compute_instr(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, uint32_t seq0, int cw) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
-  const int lane = threadIdx.x & 63;
-  const int B = S.batch, l = in.layer;
-  float *wsc = R.wsc + (size_t)cw * MK_WSC;
-  if (in.op == MKOP_ATTN) {
-    const int d = P.d, G = P.G, lpp = d / 8;
-    float qv[MK_MAX_GROUP][8];
-#pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[j][e] = j < G ? R.X[j * d + (lane % lpp) * 8 + e] : 0.f;
-    AttnAcc acc;
-#pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j) {
-      acc.m[j] = -INFINITY;
-      acc.l[j] = 0.f;
-      acc.o[j][0] = acc.o[j][1] = 0.f;
-    }
-    for (int u = cw; u < g.n_units; u += MK_NCW)
-      if (!attn_unit(R, g, u, seq0 + (uint32_t)u * 2u, qv, acc, wsc)) return false;
-    float *wp = attn_wpart(R, cw);
-#pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j) {
-      if (j >= G) continue;
-      wp[j * (d + 2) + 2 + lane] = acc.o[j][0];
-      if (d > 64) wp[j * (d + 2) + 2 + lane + 64] = acc.o[j][1];
-      if (lane == 0) {
-        wp[j * (d + 2)] = acc.m[j];
-        wp[j * (d + 2) + 1] = acc.l[j];
-      }
-    }
-    return true;
-  }
-  return B == 1 ? gemv_instr<1>(R, in, g, A, seq0, cw) : gemv_instr<MK_RB_MAXB>(R, in, g, A, seq0, cw);
-}
-
 // ------------------------------------------------------- sync epilogues
+
+MKD void argmax_merge(float &v, int &i, float ov, int oi) {
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
 
 // returns 1: trigger the event, 0: do not, -1: abort
 MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A) {
   const MkProgram &P = R.P;
   const MkStep &S = R.S;
   const int lane = threadIdx.x & 63;
+  const int B = S.batch, l = in.layer;
   if (in.op == MKOP_ATTN) {
-    const int b = in.r0, gg = in.r1, d = P.d, G = P.G, NS = in.nsplit, l = in.layer;
+    const int b = in.r0, gg = in.r1, d = P.d, G = P.G, NS = in.nsplit;
     float *out = A.attn + ((size_t)l * P.B_max + b) * P.nq * d + (size_t)gg * G * d;
     float *part = P.part + ((((size_t)l * P.B_max + b) * P.nkv + gg) * NS) * G * (d + 2);
-    // merge the compute waves' partials
+    // merge the compute waves' partials (base-2 scores)
     for (int e = lane; e < G * d; e += 64) {
       const int j = e / d, i = e - j * d;
       float mx = -INFINITY;
@@ -467,7 +589,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
       float z = 0.f, o = 0.f;
       for (int w = 0; w < MK_NCW; ++w) {
         const float *wp = attn_wpart(R, w) + j * (d + 2);
-        const float c = wp[0] == -INFINITY ? 0.f : expf(wp[0] - mx);
+        const float c = wp[0] == -INFINITY ? 0.f : exp2_fast(wp[0] - mx);
         z = fmaf(wp[1], c, z);
         o = fmaf(wp[2 + i], c, o);
       }
@@ -496,7 +618,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
       for (int s2 = 0; s2 < NS; ++s2) {
         const float *pp = part + ((size_t)s2 * G + j) * (d + 2);
         const float ms = ldc(pp);
-        const float c = ms == -INFINITY ? 0.f : expf(ms - mx);
+        const float c = ms == -INFINITY ? 0.f : exp2_fast(ms - mx);
         z = fmaf(ldc(pp + 1), c, z);
         o = fmaf(ldc(pp + 2 + i), c, o);
       }
@@ -504,47 +626,71 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
     }
     return 1;
   }
-  if (in.op == MKOP_LMHEAD) {
-    for (int b = 0; b < S.batch; ++b) {
-      float v = -INFINITY;
-      int ix = 0x7fffffff;
-      for (int w = 0; w < MK_NCW; ++w)
-        if (better(R.ctl->lm_v[w * MK_RB_MAXB + b], R.ctl->lm_i[w * MK_RB_MAXB + b], v, ix)) {
-          v = R.ctl->lm_v[w * MK_RB_MAXB + b];
-          ix = R.ctl->lm_i[w * MK_RB_MAXB + b];
-        }
-      if (lane == 0) {
-        stc(P.lm_val + (size_t)in.part * P.B_max + b, v);
-        stci(P.lm_idx + (size_t)in.part * P.B_max + b, ix);
+  // projections: coalesced stores of the compute waves' row results
+  const int n = g.n_units;
+  float lmv[MK_RB_MAXB];
+  int lmi[MK_RB_MAXB];
+  for (int b = 0; b < B; ++b) {
+    const float *ob = R.out + (size_t)b * P.out_stride;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int u = lane; u < n; u += 64) {
+      const float v = ob[u];
+      const int r = in.r0 + u;
+      switch (in.op) {
+        case MKOP_QKV:
+          stc(A.qkv + ((size_t)l * P.B_max + b) * ((P.nq + 2 * P.nkv) * P.d) + r, v);
+          break;
+        case MKOP_OPROJ:
+          stc(A.xmid + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * n + u] + v);
+          break;
+        case MKOP_GATEUP:
+          stc(A.hbuf + ((size_t)l * P.B_max + b) * P.I + r, v);
+          break;
+        case MKOP_DOWN:
+          stc(A.xout + ((size_t)l * P.B_max + b) * P.H + r, R.resid[(size_t)b * n + u] + v);
+          break;
+        case MKOP_LMHEAD:
+          gst(S.logits + (size_t)b * P.V + r, v);
+          argmax_merge(bv, bi, v, r);
+          break;
       }
     }
-    wait_vm();
-    uint32_t old = 0;
-    if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
-    old = __shfl(old, 0, 64);
-    if (old + 1u != (S.epoch + 1u) * (uint32_t)P.n_lm_parts) return 0;
-    if (lane < S.batch) {
-      const int b = lane;
-      float v = -INFINITY;
-      int ix = 0x7fffffff;
-      for (int k = 0; k < P.n_lm_parts; ++k) {
-        const float pv = ldc(P.lm_val + (size_t)k * P.B_max + b);
-        const int pi = ldci(P.lm_idx + (size_t)k * P.B_max + b);
-        if (better(pv, pi, v, ix)) {
-          v = pv;
-          ix = pi;
-        }
-      }
-      if (ix == 0x7fffffff) ix = 0;
-      if (S.next) gst(S.next + b, ix);
-      if (S.flags & 1u) {
-        gst(S.tokens + b, ix);
-        gst(S.positions + b, R.ctl->pos[b] + 1);
+    if (in.op == MKOP_LMHEAD) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+      if (b < MK_RB_MAXB) {
+        lmv[b] = bv;
+        lmi[b] = bi;
       }
     }
-    return 0;
   }
-  return 1;
+  if (in.op != MKOP_LMHEAD) return 1;
+  if (lane == 0) {
+    for (int b = 0; b < B && b < MK_RB_MAXB; ++b) {
+      stc(P.lm_val + (size_t)in.part * P.B_max + b, lmv[b]);
+      stci(P.lm_idx + (size_t)in.part * P.B_max + b, lmi[b]);
+    }
+  }
+  wait_vm();
+  uint32_t old = 0;
+  if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
+  old = __shfl(old, 0, 64);
+  if (old + 1u != (S.epoch + 1u) * (uint32_t)P.n_lm_parts) return 0;
+  if (lane < B) {
+    const int b = lane;
+    float v = -INFINITY;
+    int ix = 0x7fffffff;
+    for (int k = 0; k < P.n_lm_parts; ++k)
+      argmax_merge(v, ix, ldc(P.lm_val + (size_t)k * P.B_max + b), ldci(P.lm_idx + (size_t)k * P.B_max + b));
+    if (ix == 0x7fffffff) ix = 0;
+    if (S.next) gst(S.next + b, ix);
+    if (S.flags & 1u) {
+      gst(S.tokens + b, ix);
+      gst(S.positions + b, R.ctl->pos[b] + 1);
+    }
+  }
+  return 0;
 }
 
 // ------------------------------------------------------- role loops
@@ -572,17 +718,7 @@ MKD bool wave_wait_event(const MkRole &R, int ev) {
     if (ready) return true;
     if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
     __builtin_amdgcn_s_sleep(1);
-    if ((++spins & 31u) == 0) {
-      if (lds_ld(&R.ctl->abort) || mk_aborted(P)) {
-        role_abort(R);
-        return false;
-      }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)P.watchdog_ticks) {
-        if (lane == 0) mk_raise(P, MK_E_TIMEOUT, ev);
-        role_abort(R);
-        return false;
-      }
-    }
+    if ((++spins & 31u) == 0 && !poll_check(R, t0, ev)) return false;
   }
 }
 
@@ -595,52 +731,151 @@ MKD void wave_signal_event(const MkRole &R, int ev, int slot) {
     stcu(P.flags + P.ev_flag_base[ev] + slot, R.S.epoch + 1u);
 }
 
-MKD void role_loader(const MkRole &R, const int32_t *list, int first, int n, int lid) {
-  LoaderState L{0u, 0u};
+template <bool FULL>
+MKD bool loader_instr(const MkRole &R, LoaderState &L, const MkGeo &g, uint32_t seq) {
+  const uint32_t npg = (uint32_t)(g.n_units * g.ppu);
+  uint32_t j = L.s - seq;  // first page of this instruction with the loader's parity
+  if (j >= npg) return true;
+  int u = (int)(j / (uint32_t)g.ppu);
+  const int rem = (int)(j - (uint32_t)u * (uint32_t)g.ppu);
+  int h = rem / g.ppr, kk = rem - h * g.ppr;
+  const char *row0 = g.src0 + (size_t)u * g.ustride;
+  const char *row1 = g.nh > 1 ? g.src1 + (size_t)u * g.ustride : row0;
+  for (; j < npg; j += MK_NLW) {
+    const char *src = (h ? row1 : row0) + (size_t)kk * MK_PAGE;
+    const int valid = FULL ? MK_PAGE : mk_page_valid(g, u, kk);
+    if (!loader_page<FULL>(R, L, src, valid)) return false;
+#pragma unroll
+    for (int i = 0; i < MK_NLW; ++i) {
+      if (++kk == g.ppr) {
+        kk = 0;
+        if (++h == g.nh) {
+          h = 0;
+          ++u;
+          row0 += g.ustride;
+          row1 += g.ustride;
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------- role entries
+//
+// Each role is a separate function (not inlined into the kernel) so that the
+// register allocator sees one role's loop at a time; inlining all three
+// into one body made it spill hundreds of scalar registers into vector
+// lanes, which the hot loops then paid for.  Arguments of a called
+// function arrive in vector registers, so they are made wave-uniform
+// (readfirstlane) again, and the program and step records are read through
+// the constant address space (scalar loads).
+
+extern __shared__ __attribute__((aligned(16))) char mk_role_lds[];
+
+typedef const __attribute__((address_space(4))) MkProgram MkProgramK;
+typedef const __attribute__((address_space(4))) MkStep MkStepK;
+
+MKD int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+MKD const void *uni_ptr(const void *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
+struct RoleCtx {
+  const MkProgram &P;
+  const MkStep &S;
+};
+MKD MkRole make_role(const MkProgram &P, const MkStep &S) {
+  char *lds = mk_role_lds;
+  const int par = (P.sync_mode == MK_SYNC_SENTINEL && !S.multi) ? (int)(S.epoch & 1u) : 0;
+  return MkRole{P,
+                S,
+                reinterpret_cast<MkCtl *>(lds),
+                reinterpret_cast<float *>(lds + P.lds_x),
+                reinterpret_cast<float *>(lds + P.lds_resid),
+                reinterpret_cast<float *>(lds + P.lds_out),
+                lds + P.lds_ring,
+                P.n_pages,
+                par};
+}
+
+__device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n, int lid) {
+  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
+  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+  first = uni(first);
+  n = uni(n);
+  lid = uni(lid);
+  const MkRole R = make_role(P, S);
+  LoaderState L{(uint32_t)lid, lid, 0u, 0, 0};
   uint32_t seq = 0;
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = cld(&R.P.instr[list ? list[k] : first + k]);
+    const MkInstr in = cld(&P.instr[first + k]);
     MkGeo g;
-    if (!mk_geo(R.P, R.S, R.ctl, in, g)) {
+    if (!mk_geo(P, S, R.ctl, in, g)) {
       role_abort(R);
       break;
     }
-    const uint32_t npg = (uint32_t)(g.n_units * g.ppu);
-    for (uint32_t j = (uint32_t)((lid - (int)(seq % MK_NLW) + MK_NLW) % MK_NLW); j < npg; j += MK_NLW) {
-      const int u = (int)(j / (uint32_t)g.ppu), kk = (int)(j % (uint32_t)g.ppu);
-      int valid;
-      const char *src = mk_page_src(g, in.op, u, kk, &valid);
-      if (!loader_page(R, L, lid, seq + j, src, valid)) return;
-    }
-    seq += npg;
+    const bool ok = g.full ? loader_instr<true>(R, L, g, seq) : loader_instr<false>(R, L, g, seq);
+    if (!ok) return;
+    seq += (uint32_t)(g.n_units * g.ppu);
   }
-  loader_publish_all(R, L, lid);
+  while (L.inflight > 0) loader_publish_one(R, L);
 }
 
-MKD void role_compute(const MkRole &R, const int32_t *list, int first, int n, int cw, const MkAct &A) {
+__device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n, int cw) {
+  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
+  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+  first = uni(first);
+  n = uni(n);
+  cw = uni(cw);
+  const MkRole R = make_role(P, S);
   uint32_t seq = 0;
-  const bool sent = R.P.sync_mode == MK_SYNC_SENTINEL && !R.S.multi;
+  int slot0 = 0;
+  const int B = S.batch;
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = cld(&R.P.instr[list ? list[k] : first + k]);
+    const MkInstr in = cld(&P.instr[first + k]);
     MkGeo g;
-    if (!mk_geo(R.P, R.S, R.ctl, in, g)) {
+    if (!mk_geo(P, S, R.ctl, in, g)) {
       role_abort(R);
       return;
     }
-    if (!role_wait(R, &R.ctl->x_ready, (uint32_t)k + 1u)) return;
-    if (!compute_instr(R, in, g, A, seq, cw)) return;
-    if (!sent) wait_vm();  // outputs complete before the storer may trigger the event
+    if (!role_wait(R, &R.ctl->x_ready, (uint32_t)k + 1u, true)) return;
+    bool ok;
+    const bool two = in.op == MKOP_GATEUP;
+    if (in.op == MKOP_ATTN) ok = attn_instr(R, g, seq, slot0, cw);
+    else if (B == 1 && g.full && g.ppr == 1) ok = two ? gemv_fast<true, true>(R, g, seq, slot0, cw)
+                                                      : gemv_fast<true, false>(R, g, seq, slot0, cw);
+    else if (B == 1 && g.full) ok = two ? gemv_fast<false, true>(R, g, seq, slot0, cw)
+                                        : gemv_fast<false, false>(R, g, seq, slot0, cw);
+    else ok = two ? gemv_general<true>(R, g, seq, slot0, cw, B) : gemv_general<false>(R, g, seq, slot0, cw, B);
+    if (!ok) return;
     if ((threadIdx.x & 63) == 0) lds_add(&R.ctl->cw_done, 1u);  // one increment per wave
-    seq += (uint32_t)(g.n_units * g.ppu);
+    const uint32_t npg = (uint32_t)(g.n_units * g.ppu);
+    seq += npg;
+    slot0 = (int)(((uint32_t)slot0 + npg) % (uint32_t)R.np);
   }
 }
 
-MKD void role_sync(const MkRole &R, const int32_t *list, int first, int n, const MkAct &A) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
+__device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n) {
+  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
+  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+  first = uni(first);
+  n = uni(n);
+  const MkRole R = make_role(P, S);
+  const MkAct A = mk_act(P, R.par);
   const bool sent = P.sync_mode == MK_SYNC_SENTINEL && !S.multi;
+  if (sent) {
+    // reset this CU's share of the other parity's activations to the sentinel
+    float *other = P.qkv + (size_t)(R.par ^ 1) * P.par_stride;
+    const size_t per = (P.par_stride + P.n_cu - 1) / P.n_cu;
+    const size_t lo = (size_t)blockIdx.x * per, hi = min(lo + per, (size_t)P.par_stride);
+    for (size_t i = lo + (threadIdx.x & 63); i < hi; i += 64) stcu(reinterpret_cast<uint32_t *>(other) + i, MK_SENTINEL);
+  }
   for (int k = 0; k < n; ++k) {
-    const MkInstr in = cld(&P.instr[list ? list[k] : first + k]);
+    const MkInstr in = cld(&P.instr[first + k]);
     MkGeo g;
     if (!mk_geo(P, S, R.ctl, in, g)) {
       if ((threadIdx.x & 63) == 0) mk_raise(P, MK_E_INPUT, 1000 + in.r0);
@@ -648,12 +883,14 @@ MKD void role_sync(const MkRole &R, const int32_t *list, int first, int n, const
       return;
     }
     const uint64_t tw = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint32_t gain[MK_XCH][2];
+    if (normed_op(in.op)) load_bf16_chunks(norm_gain(P, in), P.H, gain);  // ahead of the wait
     if (!S.multi && !sent && in.wait_ev >= 0 && !wave_wait_event(R, in.wait_ev)) return;
     if (!role_wait(R, &R.ctl->cw_done, (uint32_t)k * MK_NCW)) return;  // X is free again
-    if (!sync_stage(R, in, g, A, sent)) return;
+    if (!sync_stage(R, in, g, A, sent, gain)) return;
     lds_st(&R.ctl->x_ready, (uint32_t)k + 1u);
     const uint64_t ts = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)(k + 1) * MK_NCW)) return;
+    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)(k + 1) * MK_NCW, true)) return;
     const int sig = sync_epilogue(R, in, g, A);
     if (sig < 0) {
       role_abort(R);
@@ -664,7 +901,7 @@ MKD void role_sync(const MkRole &R, const int32_t *list, int first, int n, const
       wave_signal_event(R, in.sig_ev, in.sig_slot);
     }
     if (P.trace && (threadIdx.x & 63) == 0) {
-      uint64_t *r = P.trace + (size_t)(list ? list[k] : first + k) * 8;
+      uint64_t *r = P.trace + (size_t)(first + k) * 8;
       r[0] = tw;
       r[1] = ts;
       r[2] = __builtin_amdgcn_s_memrealtime();
@@ -678,30 +915,17 @@ MKD void role_sync(const MkRole &R, const int32_t *list, int first, int n, const
   }
 }
 
-// Entry used by both kernels: run `n` instructions of `list` with roles.
-MKD void role_run(const MkProgram &P, const MkStep &S, const int32_t *list, int first, int n, char *lds) {
-  MkCtl *ctl = reinterpret_cast<MkCtl *>(lds);
+// Entry used by both kernels: run instructions [first, first + n) of the
+// program with roles.  Sg points at the kernel's step argument in the
+// kernarg segment (valid for the whole launch).
+MKD void role_run(const MkProgram *Pg, const MkStep *Sg, int first, int n) {
+  MkCtl *ctl = reinterpret_cast<MkCtl *>(mk_role_lds);
   for (int i = threadIdx.x; i < (int)(sizeof(MkCtl) / 4); i += MK_BLOCK) reinterpret_cast<uint32_t *>(ctl)[i] = 0;
   __syncthreads();
-  if (threadIdx.x < S.batch) ctl->pos[threadIdx.x] = gld(S.positions + threadIdx.x);
+  if ((int)threadIdx.x < Sg->batch) ctl->pos[threadIdx.x] = gld(Sg->positions + threadIdx.x);
   __syncthreads();
-  const int par = (P.sync_mode == MK_SYNC_SENTINEL && !S.multi) ? (int)(S.epoch & 1u) : 0;
-  MkRole R{P, S, ctl, reinterpret_cast<float *>(lds + P.lds_x), reinterpret_cast<float *>(lds + P.lds_resid),
-           reinterpret_cast<float *>(lds + P.lds_wsc), lds + P.lds_ring, P.n_pages, par};
-  const MkAct A = mk_act(P, par);
   const int wave = threadIdx.x >> 6;
-  if (wave < MK_NLW) {
-    role_loader(R, list, first, n, wave);
-  } else if (wave == MK_SYNCW) {
-    if (P.sync_mode == MK_SYNC_SENTINEL && !S.multi) {
-      // reset this CU's share of the other parity's activations to the sentinel
-      float *other = P.qkv + (size_t)(par ^ 1) * P.par_stride;
-      const size_t per = (P.par_stride + P.n_cu - 1) / P.n_cu;
-      const size_t lo = (size_t)blockIdx.x * per, hi = min(lo + per, (size_t)P.par_stride);
-      for (size_t i = lo + (threadIdx.x & 63); i < hi; i += 64) stcu(reinterpret_cast<uint32_t *>(other) + i, MK_SENTINEL);
-    }
-    role_sync(R, list, first, n, A);
-  } else {
-    role_compute(R, list, first, n, wave - MK_NLW - 1, A);
-  }
+  if (wave < MK_NLW) role_loader_entry(Pg, Sg, first, n, wave);
+  else if (wave == MK_SYNCW) role_sync_entry(Pg, Sg, first, n);
+  else role_compute_entry(Pg, Sg, first, n, wave - MK_NLW - 1);
 }

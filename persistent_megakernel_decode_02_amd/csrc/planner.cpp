@@ -68,14 +68,18 @@ static int role_lds_layout(mk_plan *p) {
   const mk_model_shape &s = p->shape;
   const int B = p->B, d = s.head_dim, G = p->G;
   if (B > MK_RB_MAXB) return MK_ERR_UNSUPPORTED;
-  int max_rows = 1;
-  for (const MkInstr &in : p->instr)
+  int max_rows = 1, max_out = 1;
+  for (const MkInstr &in : p->instr) {
     if (in.op == MKOP_OPROJ || in.op == MKOP_DOWN) max_rows = std::max(max_rows, in.r1 - in.r0);
+    if (in.op != MKOP_ATTN) max_out = std::max(max_out, in.r1 - in.r0);
+  }
   int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * d, (int64_t)s.ffn});
   int64_t x_floats = std::max<int64_t>((int64_t)B * kmax, (int64_t)(G + 2) * d + (int64_t)MK_NCW * G * (d + 2));
   int64_t o = MK_CTL_BYTES;
-  p->lds_wsc = (int)o;
-  o += (int64_t)MK_NCW * MK_WSC * 4;
+  // per-row results of the compute waves: [B][out_stride]
+  p->out_stride = (max_out + 3) / 4 * 4;
+  p->lds_out = (int)o;
+  o += (int64_t)B * p->out_stride * 4;
   p->lds_resid = (int)o;
   o += ((int64_t)B * max_rows * 4 + 15) / 16 * 16;
   p->lds_x = (int)o;

@@ -22,7 +22,7 @@ struct mk_plan {
   int n_cu = 0, S = 1, B = 1, max_ctx = 0, G = 1;
   int n_levels = 0, n_events = 0, n_flags = 0, n_tickets = 0, n_lm_parts = 0;
   int lds_bytes = 0;
-  int lds_x = 0, lds_resid = 0, lds_wsc = 0, lds_ring = 0, n_pages = 0;  // role engine
+  int lds_x = 0, lds_resid = 0, lds_out = 0, lds_ring = 0, n_pages = 0, out_stride = 0;  // role engine
   std::vector<MkInstr> instr;  // CU-major
   std::vector<int32_t> instr_cu;
   std::vector<int32_t> cu_begin, level_begin, level_list, ev_count, ev_flag_base;
