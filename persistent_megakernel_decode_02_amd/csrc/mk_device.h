@@ -114,7 +114,8 @@ MKD float block_sum(float v, float *red) {
 
 // element offset of cache row block [l][plane][b][g][0][0] in the
 // [L][2][B_max][nkv][max_ctx][d] bf16 KV cache
-MKD size_t kv_off(const MkProgram &P, int l, int plane, int b, int g) {
+template <class PT>
+MKD size_t kv_off(const PT &P, int l, int plane, int b, int g) {
   return ((((size_t)l * 2 + plane) * P.B_max + b) * P.nkv + g) * (size_t)P.max_ctx * P.d;
 }
 
@@ -122,7 +123,8 @@ MKD size_t kv_off(const MkProgram &P, int l, int plane, int b, int g) {
 MKD bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
 // record the first device error and raise the abort flag every wait checks
-MKD void mk_raise(const MkProgram &P, int code, int detail) {
+template <class PT>
+MKD void mk_raise(const PT &P, int code, int detail) {
   int32_t *err = P.err;
   int32_t expected = 0;
   if (__hip_atomic_compare_exchange_strong((MK_G(int32_t) *)err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -130,7 +132,8 @@ MKD void mk_raise(const MkProgram &P, int code, int detail) {
     stci(err + 1, detail);
   stci(err + 2, 1);
 }
-MKD bool mk_aborted(const MkProgram &P) { return ldci(P.err + 2) != 0; }
+template <class PT>
+MKD bool mk_aborted(const PT &P) { return __builtin_amdgcn_readfirstlane(ldci(P.err + 2)) != 0; }
 
 // Wait for event `ev` of this step.  Counter mode: one lane polls the
 // monotonic counter until it reaches (epoch+1) * triggers.  Flag mode: one

@@ -110,3 +110,15 @@ struct MkStep {
   int32_t multi;   // 1: launched per level (no waits/signals)
   int32_t level;   // multi-launch: level this launch runs
 };
+
+// Device code of the role engine reads the program and step records through
+// the constant address space (scalar loads that stay valid across the
+// engine's LDS-flag assembly); on the host these are the plain types.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MK_CONST __attribute__((address_space(4)))
+#else
+#define MK_CONST
+#endif
+typedef const MK_CONST MkProgram MkProgC;
+typedef const MK_CONST MkStep MkStepC;
+

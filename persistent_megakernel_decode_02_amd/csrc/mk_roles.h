@@ -42,6 +42,12 @@
 #define MK_SENTINEL 0x7FBADBADu           // quiet NaN payload the arithmetic never produces
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) mk_u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mk_f32x4 lds_f32x4;
 
 // LDS control block (start of dynamic LDS)
 struct MkCtl {
@@ -56,15 +62,16 @@ struct MkCtl {
   uint32_t st_page_wait;        // trace only: ticks compute waves spent waiting for a landed page
   uint32_t st_pages;            // trace only: pages issued
 };
+typedef __attribute__((address_space(3))) MkCtl MkCtl3;
 
 struct MkRole {
-  const MkProgram &P;
-  const MkStep &S;
-  MkCtl *ctl;
-  float *X;           // staged input vector(s) [B][K] (ATTN: q | k | v | wave partials)
-  float *resid;       // residual rows [B][rows]
-  float *out;         // per-row results of the compute waves [B][out_stride]
-  char *ring;         // NP pages
+  MkProgC &P;
+  MkStepC &S;
+  MkCtl3 *ctl;       // control block (LDS address space: flags are ds instructions)
+  lds_float *X;       // staged input vector(s) [B][K] (ATTN: q | k | v | wave partials)
+  lds_float *resid;   // residual rows [B][rows]
+  lds_float *out;     // per-row results of the compute waves [B][out_stride]
+  lds_char *ring;     // NP pages
   int np;
   int par;            // activation parity (sentinel mode)
 };
@@ -83,14 +90,14 @@ static_assert(sizeof(MkCtl) <= MK_CTL_BYTES, "LDS control block");
 // memory round trip on every page a compute wave frees after storing an
 // output.  Ordering against global memory is made explicit where it matters
 // (a vmcnt wait before a wave reports results that other CUs will read).
-MKD uint32_t lds_off(const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p; }
-MKD uint32_t lds_ld(uint32_t *p) {
+MKD uint32_t lds_off(const lds_u32 *p) { return (uint32_t)(size_t)p; }
+MKD uint32_t lds_ld(lds_u32 *p) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
-  return v;
+  return __builtin_amdgcn_readfirstlane(v);  // one address for the wave: the value is uniform
 }
-MKD void lds_st(uint32_t *p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
-MKD void lds_add(uint32_t *p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
+MKD void lds_st(lds_u32 *p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
+MKD void lds_add(lds_u32 *p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
 
 // read-only program data (instruction lists, pointer tables) through the
 // constant address space: scalar loads, counted by lgkmcnt, never by vmcnt
@@ -112,7 +119,7 @@ MKD T cld(const T *p) {
 // Spin (one wave, uniform) until *p >= v.  false: the kernel is aborting.
 // Long waits (`nap`) sleep 4 x 64 clocks per poll so the spinning wave
 // leaves issue slots to the waves doing work.
-MKD bool role_wait(const MkRole &R, uint32_t *p, uint32_t v, bool nap = false) {
+MKD bool role_wait(const MkRole &R, lds_u32 *p, uint32_t v, bool nap = false) {
   if ((int32_t)(lds_ld(p) - v) >= 0) return true;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   uint32_t n = 0;
@@ -126,7 +133,7 @@ MKD bool role_wait(const MkRole &R, uint32_t *p, uint32_t v, bool nap = false) {
         return false;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)R.P.watchdog_ticks) {
-        if ((threadIdx.x & 63) == 0) mk_raise(R.P, MK_E_TIMEOUT, 0x10000 + (int)(p - (uint32_t *)R.ctl));
+        if ((threadIdx.x & 63) == 0) mk_raise(R.P, MK_E_TIMEOUT, 0x10000 + (int)(p - (lds_u32 *)R.ctl));
         lds_st(&R.ctl->abort, 1u);
         return false;
       }
@@ -155,7 +162,7 @@ struct MkGeo {
   int d, p, t0, t1, bp;  // head_dim, current position, key range [t0, t1), positions per page
 };
 
-MKD bool mk_geo(const MkProgram &P, const MkStep &S, const MkCtl *ctl, const MkInstr &in, MkGeo &g) {
+MKD bool mk_geo(MkProgC &P, MkStepC &S, const MkCtl3 *ctl, const MkInstr &in, MkGeo &g) {
   g.d = P.d;
   g.p = g.t0 = g.t1 = g.bp = 0;
   g.nh = 1;
@@ -193,7 +200,7 @@ MKD bool mk_geo(const MkProgram &P, const MkStep &S, const MkCtl *ctl, const MkI
       break;
     case MKOP_ATTN: {
       const int b = in.r0, gg = in.r1, NS = in.nsplit;
-      const int p = ctl->pos[b];
+      const int p = __builtin_amdgcn_readfirstlane(ctl->pos[b]);
       if (p < 0 || p >= P.max_ctx) return false;
       const int n = p + 1;
       g.bp = MK_PAGE / (2 * P.d);
@@ -293,7 +300,7 @@ MKD bool loader_page(const MkRole &R, LoaderState &L, const char *src, int valid
     }
   }
   const int lane = threadIdx.x & 63;
-  char *dst = R.ring + (size_t)L.slot * MK_PAGE;
+  lds_char *dst = R.ring + (size_t)L.slot * MK_PAGE;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int off = q * 1024 + lane * 16;
@@ -335,7 +342,7 @@ MKD int ring_add(int slot, int k, int np) {
   return slot;
 }
 
-MKD float dot8(const mk_u32x4 w, const float4 xa, const float4 xb, float a) {
+MKD float dot8(const mk_u32x4 w, const mk_f32x4 xa, const mk_f32x4 xb, float a) {
   a = fmaf(bf_lo(w.x), xa.x, a);
   a = fmaf(bf_hi(w.x), xa.y, a);
   a = fmaf(bf_lo(w.y), xa.z, a);
@@ -350,22 +357,22 @@ MKD float dot8(const mk_u32x4 w, const float4 xa, const float4 xb, float a) {
 // Lane slice of a staged input for one page of a row: chunk q of page kk
 // covers input elements kk*2048 + q*512 + lane*8 .. +8.
 struct XSlice {
-  float4 v[4][2];
+  mk_f32x4 v[4][2];
 };
-MKD void load_xslice(const float *x, int kk, XSlice &xs) {
+MKD void load_xslice(const lds_float *x, int kk, XSlice &xs) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float4 *x4 = reinterpret_cast<const float4 *>(x + kk * 2048 + q * 512 + lane * 8);
+    const lds_f32x4 *x4 = reinterpret_cast<const lds_f32x4 *>(x + kk * 2048 + q * 512 + lane * 8);
     xs.v[q][0] = x4[0];
     xs.v[q][1] = x4[1];
   }
 }
-MKD float page_dot(const char *pg, const XSlice &xs, float a) {
+MKD float page_dot(const lds_char *pg, const XSlice &xs, float a) {
   const int lane = threadIdx.x & 63;
   mk_u32x4 w[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const mk_u32x4 *>(pg + q * 1024 + lane * 16);
+  for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const lds_u32x4 *>(pg + q * 1024 + lane * 16);
 #pragma unroll
   for (int q = 0; q < 4; ++q) a = dot8(w[q], xs.v[q][0], xs.v[q][1], a);
   return a;

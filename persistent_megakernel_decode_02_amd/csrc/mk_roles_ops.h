@@ -20,7 +20,7 @@ MKD mk_u32x4 ldc16(__amdgpu_buffer_rsrc_t r, int byte_off) {
 struct MkAct {
   float *qkv, *attn, *xmid, *hbuf, *xout;
 };
-MKD MkAct mk_act(const MkProgram &P, int par) {
+MKD MkAct mk_act(MkProgC &P, int par) {
   const size_t o = (size_t)par * P.par_stride;
   MkAct a;
   a.qkv = P.qkv + o;
@@ -78,19 +78,19 @@ MKD bool load_vec(const MkRole &R, const float *src, int n, bool sentinel, mk_u3
   }
 }
 
-MKD void store_vec(float *dst, int n, const mk_u32x4 (&v)[MK_XCH]) {
+MKD void store_vec(lds_float *dst, int n, const mk_u32x4 (&v)[MK_XCH]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < MK_XCH; ++j) {
     const int e = (j * 64 + lane) * 4;
     if (e < n)
-      *reinterpret_cast<float4 *>(dst + e) = make_float4(__uint_as_float(v[j].x), __uint_as_float(v[j].y),
-                                                         __uint_as_float(v[j].z), __uint_as_float(v[j].w));
+      *reinterpret_cast<lds_f32x4 *>(dst + e) = mk_f32x4{__uint_as_float(v[j].x), __uint_as_float(v[j].y),
+                                                         __uint_as_float(v[j].z), __uint_as_float(v[j].w)};
   }
 }
 
 // Copy n floats (n % 4 == 0) from global to LDS, MK_XCH chunks per lane per round.
-MKD bool stage_vec(const MkRole &R, float *dst, const float *src, int n, bool sentinel) {
+MKD bool stage_vec(const MkRole &R, lds_float *dst, const float *src, int n, bool sentinel) {
   for (int base = 0; base < n; base += 256 * MK_XCH) {
     mk_u32x4 v[MK_XCH];
     const int m = min(n - base, 256 * MK_XCH);
@@ -101,7 +101,7 @@ MKD bool stage_vec(const MkRole &R, float *dst, const float *src, int n, bool se
 }
 
 // n scalar floats (any alignment), device-coherent, sentinel-checked
-MKD bool stage_scalars(const MkRole &R, float *dst, const float *src, int n, bool sentinel) {
+MKD bool stage_scalars(const MkRole &R, lds_float *dst, const float *src, int n, bool sentinel) {
   const int lane = threadIdx.x & 63;
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
@@ -141,7 +141,7 @@ MKD void load_bf16_chunks(const uint16_t *p, int n, uint32_t (&g)[MK_XCH][2]) {
 
 // RMSNorm of a vector held in registers (load_vec layout, n <= 256 * MK_XCH),
 // gains g; result written to LDS dst
-MKD void norm_store(float *dst, int n, mk_u32x4 (&v)[MK_XCH], const uint32_t (&g)[MK_XCH][2], float eps) {
+MKD void norm_store(lds_float *dst, int n, mk_u32x4 (&v)[MK_XCH], const uint32_t (&g)[MK_XCH][2], float eps) {
   const int lane = threadIdx.x & 63;
   float ss = 0.f;
 #pragma unroll
@@ -162,9 +162,9 @@ MKD void norm_store(float *dst, int n, mk_u32x4 (&v)[MK_XCH], const uint32_t (&g
   for (int j = 0; j < MK_XCH; ++j) {
     const int e = (j * 64 + lane) * 4;
     if (e < n)
-      *reinterpret_cast<float4 *>(dst + e) = make_float4(
+      *reinterpret_cast<lds_f32x4 *>(dst + e) = mk_f32x4{
           (__uint_as_float(v[j].x) * r) * bf_lo(g[j][0]), (__uint_as_float(v[j].y) * r) * bf_hi(g[j][0]),
-          (__uint_as_float(v[j].z) * r) * bf_lo(g[j][1]), (__uint_as_float(v[j].w) * r) * bf_hi(g[j][1]));
+          (__uint_as_float(v[j].z) * r) * bf_lo(g[j][1]), (__uint_as_float(v[j].w) * r) * bf_hi(g[j][1])};
   }
 }
 
@@ -172,7 +172,7 @@ MKD void norm_store(float *dst, int n, mk_u32x4 (&v)[MK_XCH], const uint32_t (&g
 
 MKD bool normed_op(int op) { return op == MKOP_QKV || op == MKOP_GATEUP || op == MKOP_LMHEAD; }
 
-MKD const uint16_t *norm_gain(const MkProgram &P, const MkInstr &in) {
+MKD const uint16_t *norm_gain(MkProgC &P, const MkInstr &in) {
   return in.op == MKOP_QKV ? P.layers[in.layer].attn_norm
                            : in.op == MKOP_GATEUP ? P.layers[in.layer].mlp_norm : P.final_norm;
 }
@@ -181,8 +181,8 @@ MKD const uint16_t *norm_gain(const MkProgram &P, const MkInstr &in) {
 // gains of a normed op, loaded before the dependency wait.
 MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, bool sent,
                     const uint32_t (&gain)[MK_XCH][2]) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
+  MkProgC &P = R.P;
+  MkStepC &S = R.S;
   const int lane = threadIdx.x & 63;
   const int B = S.batch, H = P.H, l = in.layer;
   switch (in.op) {
@@ -217,7 +217,7 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
     case MKOP_DOWN: {
       const int K = g.K, nr = in.r1 - in.r0;
       for (int b = 0; b < B; ++b) {
-        float *rd = R.resid + (size_t)b * nr;
+        lds_float *rd = R.resid + (size_t)b * nr;
         if (in.op == MKOP_OPROJ && l == 0) {
           const int tok = gld(S.tokens + b);
           if (tok < 0 || tok >= P.V) {
@@ -242,7 +242,7 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       const int b = in.r0, gg = in.r1, d = P.d, G = P.G, half = d / 2;
       const int R0 = (P.nq + 2 * P.nkv) * d;
       const float *qkv = A.qkv + ((size_t)l * P.B_max + b) * R0;
-      float *q = R.X, *kc = R.X + G * d, *vc = kc + d;
+      lds_float *q = R.X, *kc = R.X + G * d, *vc = kc + d;
       if (!stage_vec(R, q, qkv + (size_t)gg * G * d, G * d, sent)) return false;
       if (!stage_vec(R, kc, qkv + (size_t)P.nq * d + (size_t)gg * d, d, sent)) return false;
       if (!stage_vec(R, vc, qkv + (size_t)(P.nq + P.nkv) * d + (size_t)gg * d, d, sent)) return false;
@@ -251,7 +251,7 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       const float qs = 1.4426950408889634f / sqrtf((float)d);
       for (int e = lane; e < (G + 1) * half; e += 64) {
         const int j = e / half, i = e - j * half;  // j == G is the key
-        float *u = j < G ? q + j * d : kc;
+        lds_float *u = j < G ? q + j * d : kc;
         const float a = u[i], c = u[i + half], co = gld(cs + 2 * i), si = gld(cs + 2 * i + 1);
         float r0 = a * co - c * si, r1 = c * co + a * si;
         if (j == G) {
@@ -338,7 +338,7 @@ MKD bool gemv_fast(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, in
       float a = 0.f;
       for (int kk = 0; kk < ppr; ++kk) {
         if (!page_wait(R, slot, s)) return false;
-        const char *pg = R.ring + (size_t)slot * MK_PAGE;
+        const lds_char *pg = R.ring + (size_t)slot * MK_PAGE;
         if (ONE) {
           a = page_dot(pg, xc, a);
         } else {
@@ -381,24 +381,24 @@ MKD bool gemv_general(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0,
       for (int b = 0; b < MK_RB_MAXB; ++b) a[b] = 0.f;
       for (int kk = 0; kk < g.ppr; ++kk) {
         if (!page_wait(R, slot, s)) return false;
-        const char *pg = R.ring + (size_t)slot * MK_PAGE;
+        const lds_char *pg = R.ring + (size_t)slot * MK_PAGE;
         const int valid = g.full ? MK_PAGE : mk_page_valid(g, u, kk);
         mk_u32x4 w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int off = q * 1024 + lane * 16;
-          w[q] = off < valid ? *reinterpret_cast<const mk_u32x4 *>(pg + off) : mk_u32x4{0, 0, 0, 0};
+          w[q] = off < valid ? *reinterpret_cast<const lds_u32x4 *>(pg + off) : mk_u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int b = 0; b < MK_RB_MAXB; ++b) {
           if (b >= B) continue;
-          const float *x = R.X + (size_t)b * g.K + kk * 2048;
+          const lds_float *x = R.X + (size_t)b * g.K + kk * 2048;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int off = q * 1024 + lane * 16;
             const bool on = off < valid;
-            const float4 *x4 = reinterpret_cast<const float4 *>(x + q * 512 + lane * 8);
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            const lds_f32x4 *x4 = reinterpret_cast<const lds_f32x4 *>(x + q * 512 + lane * 8);
+            const mk_f32x4 z = {0.f, 0.f, 0.f, 0.f};
             a[b] = dot8(w[q], on ? x4[0] : z, on ? x4[1] : z, a[b]);
           }
         }
@@ -421,7 +421,7 @@ MKD bool gemv_general(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0,
 }
 
 // wave partials of attention live after q | k | v in X: [NCW][G][d + 2]
-MKD float *attn_wpart(const MkRole &R, int cw) {
+MKD lds_float *attn_wpart(const MkRole &R, int cw) {
   const int d = R.P.d, G = R.P.G;
   return R.X + (size_t)(G + 2) * d + (size_t)cw * G * (d + 2);
 }
@@ -451,9 +451,10 @@ MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, i
   float qv[MK_MAX_GROUP][8];
 #pragma unroll
   for (int j = 0; j < MK_MAX_GROUP; ++j) {
-    const float4 *q4 = reinterpret_cast<const float4 *>(R.X + j * d + c8);
-    const float4 a = j < G ? q4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 b = j < G ? q4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const lds_f32x4 *q4 = reinterpret_cast<const lds_f32x4 *>(R.X + j * d + c8);
+    const mk_f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const mk_f32x4 a = j < G ? q4[0] : z;
+    const mk_f32x4 b = j < G ? q4[1] : z;
     qv[j][0] = a.x, qv[j][1] = a.y, qv[j][2] = a.z, qv[j][3] = a.w;
     qv[j][4] = b.x, qv[j][5] = b.y, qv[j][6] = b.z, qv[j][7] = b.w;
   }
@@ -465,7 +466,7 @@ MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
   }
-  const float *kn = R.X + G * d, *vn = kn + d;  // this step's key and value (bf16-rounded)
+  const lds_float *kn = R.X + G * d, *vn = kn + d;  // this step's key and value (bf16-rounded)
   uint32_t s = seq0 + (uint32_t)(cw * 2);
   int slot = ring_add(slot0, cw * 2, R.np);
   for (int u = cw; u < g.n_units; u += MK_NCW) {
@@ -474,12 +475,12 @@ MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, i
     const bool here = ta <= g.p && g.p < ta + npos;  // the block holds this step's position
     const int vslot = slot + 1 == R.np ? 0 : slot + 1;
     if (!page_wait(R, slot, s) || !page_wait(R, vslot, s + 1)) return false;
-    const char *kp = R.ring + (size_t)slot * MK_PAGE, *vp = R.ring + (size_t)vslot * MK_PAGE;
+    const lds_char *kp = R.ring + (size_t)slot * MK_PAGE, *vp = R.ring + (size_t)vslot * MK_PAGE;
     float sc[4][MK_MAX_GROUP];
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int row = pass * ppi + pin;
-      const mk_u32x4 kw = row < npos ? *reinterpret_cast<const mk_u32x4 *>(kp + (size_t)row * 2 * d + c8 * 2)
+      const mk_u32x4 kw = row < npos ? *reinterpret_cast<const lds_u32x4 *>(kp + (size_t)row * 2 * d + c8 * 2)
                                      : mk_u32x4{0, 0, 0, 0};
       float k8[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
                      bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
@@ -517,7 +518,7 @@ MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, i
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int row = pass * ppi + pin;
-      const mk_u32x4 vw = row < npos ? *reinterpret_cast<const mk_u32x4 *>(vp + (size_t)row * 2 * d + c8 * 2)
+      const mk_u32x4 vw = row < npos ? *reinterpret_cast<const lds_u32x4 *>(vp + (size_t)row * 2 * d + c8 * 2)
                                      : mk_u32x4{0, 0, 0, 0};
       float v8[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
                      bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
@@ -535,7 +536,7 @@ MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, i
     slot = ring_add(slot, MK_NCW * 2, R.np);
   }
   // merge the lane groups: rescale to the wave max, then sum groups lane-wise
-  float *wp = attn_wpart(R, cw);
+  lds_float *wp = attn_wpart(R, cw);
 #pragma unroll
   for (int j = 0; j < MK_MAX_GROUP; ++j) {
     if (j >= G) continue;
@@ -573,8 +574,8 @@ MKD void argmax_merge(float &v, int &i, float ov, int oi) {
 
 // returns 1: trigger the event, 0: do not, -1: abort
 MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
+  MkProgC &P = R.P;
+  MkStepC &S = R.S;
   const int lane = threadIdx.x & 63;
   const int B = S.batch, l = in.layer;
   if (in.op == MKOP_ATTN) {
@@ -588,7 +589,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
       for (int w = 0; w < MK_NCW; ++w) mx = fmaxf(mx, attn_wpart(R, w)[j * (d + 2)]);
       float z = 0.f, o = 0.f;
       for (int w = 0; w < MK_NCW; ++w) {
-        const float *wp = attn_wpart(R, w) + j * (d + 2);
+        const lds_float *wp = attn_wpart(R, w) + j * (d + 2);
         const float c = wp[0] == -INFINITY ? 0.f : exp2_fast(wp[0] - mx);
         z = fmaf(wp[1], c, z);
         o = fmaf(wp[2 + i], c, o);
@@ -608,7 +609,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
     wait_vm();
     uint32_t old = 0;
     if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
-    old = __shfl(old, 0, 64);
+    old = __builtin_amdgcn_readfirstlane(old);
     if (old + 1u != (S.epoch + 1u) * (uint32_t)NS) return 0;
     for (int e = lane; e < G * d; e += 64) {
       const int j = e / d, i = e - j * d;
@@ -631,7 +632,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
   float lmv[MK_RB_MAXB];
   int lmi[MK_RB_MAXB];
   for (int b = 0; b < B; ++b) {
-    const float *ob = R.out + (size_t)b * P.out_stride;
+    const lds_float *ob = R.out + (size_t)b * P.out_stride;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int u = lane; u < n; u += 64) {
@@ -675,7 +676,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
   wait_vm();
   uint32_t old = 0;
   if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
-  old = __shfl(old, 0, 64);
+  old = __builtin_amdgcn_readfirstlane(old);
   if (old + 1u != (S.epoch + 1u) * (uint32_t)P.n_lm_parts) return 0;
   if (lane < B) {
     const int b = lane;
@@ -697,8 +698,8 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
 
 // wave-level dependency wait (counter or flag mode)
 MKD bool wave_wait_event(const MkRole &R, int ev) {
-  const MkProgram &P = R.P;
-  const MkStep &S = R.S;
+  MkProgC &P = R.P;
+  MkStepC &S = R.S;
   const int lane = threadIdx.x & 63;
   uint64_t t0 = 0;
   uint32_t spins = 0;
@@ -706,7 +707,7 @@ MKD bool wave_wait_event(const MkRole &R, int ev) {
     bool ready;
     if (P.sync_mode == 0) {
       const uint32_t need = (S.epoch + 1u) * (uint32_t)P.ev_count[ev];
-      ready = (int32_t)(ldcu(P.ctr + ev) - need) >= 0;
+      ready = (int32_t)(__builtin_amdgcn_readfirstlane(ldcu(P.ctr + ev)) - need) >= 0;
     } else {
       const uint32_t want = S.epoch + 1u;
       const int n = P.ev_count[ev];
@@ -723,7 +724,7 @@ MKD bool wave_wait_event(const MkRole &R, int ev) {
 }
 
 MKD void wave_signal_event(const MkRole &R, int ev, int slot) {
-  const MkProgram &P = R.P;
+  MkProgC &P = R.P;
   if ((threadIdx.x & 63) != 0) return;
   if (P.sync_mode == 0)
     addcu(P.ctr + ev, 1u);
@@ -773,9 +774,6 @@ MKD bool loader_instr(const MkRole &R, LoaderState &L, const MkGeo &g, uint32_t 
 
 extern __shared__ __attribute__((aligned(16))) char mk_role_lds[];
 
-typedef const __attribute__((address_space(4))) MkProgram MkProgramK;
-typedef const __attribute__((address_space(4))) MkStep MkStepK;
-
 MKD int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 MKD const void *uni_ptr(const void *p) {
   const uint64_t v = (uint64_t)p;
@@ -784,31 +782,30 @@ MKD const void *uni_ptr(const void *p) {
   return (const void *)(((uint64_t)hi << 32) | lo);
 }
 
-struct RoleCtx {
-  const MkProgram &P;
-  const MkStep &S;
-};
-MKD MkRole make_role(const MkProgram &P, const MkStep &S) {
-  char *lds = mk_role_lds;
+// lb: LDS address of the dynamic allocation, taken in the kernel and passed
+// down (inside a called function the address would come from a per-kernel
+// table, which the compiler reloads instead of keeping in a register)
+MKD MkRole make_role(MkProgC &P, MkStepC &S, uint32_t lb) {
   const int par = (P.sync_mode == MK_SYNC_SENTINEL && !S.multi) ? (int)(S.epoch & 1u) : 0;
   return MkRole{P,
                 S,
-                reinterpret_cast<MkCtl *>(lds),
-                reinterpret_cast<float *>(lds + P.lds_x),
-                reinterpret_cast<float *>(lds + P.lds_resid),
-                reinterpret_cast<float *>(lds + P.lds_out),
-                lds + P.lds_ring,
+                (MkCtl3 *)(size_t)lb,
+                (lds_float *)(size_t)(lb + P.lds_x),
+                (lds_float *)(size_t)(lb + P.lds_resid),
+                (lds_float *)(size_t)(lb + P.lds_out),
+                (lds_char *)(size_t)(lb + P.lds_ring),
                 P.n_pages,
                 par};
 }
 
-__device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n, int lid) {
-  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
-  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+__device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
+                                                int lid) {
+  MkProgC &P = *(MkProgC *)uni_ptr(Pg);
+  MkStepC &S = *(MkStepC *)uni_ptr(Sg);
   first = uni(first);
   n = uni(n);
   lid = uni(lid);
-  const MkRole R = make_role(P, S);
+  const MkRole R = make_role(P, S, (uint32_t)uni((int)lb));
   LoaderState L{(uint32_t)lid, lid, 0u, 0, 0};
   uint32_t seq = 0;
   for (int k = 0; k < n; ++k) {
@@ -825,13 +822,14 @@ __device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep
   while (L.inflight > 0) loader_publish_one(R, L);
 }
 
-__device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n, int cw) {
-  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
-  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+__device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
+                                                 int cw) {
+  MkProgC &P = *(MkProgC *)uni_ptr(Pg);
+  MkStepC &S = *(MkStepC *)uni_ptr(Sg);
   first = uni(first);
   n = uni(n);
   cw = uni(cw);
-  const MkRole R = make_role(P, S);
+  const MkRole R = make_role(P, S, (uint32_t)uni((int)lb));
   uint32_t seq = 0;
   int slot0 = 0;
   const int B = S.batch;
@@ -859,12 +857,12 @@ __device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkSte
   }
 }
 
-__device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *Sg, int first, int n) {
-  const MkProgram &P = *(const MkProgram *)(MkProgramK *)uni_ptr(Pg);
-  const MkStep &S = *(const MkStep *)(MkStepK *)uni_ptr(Sg);
+__device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n) {
+  MkProgC &P = *(MkProgC *)uni_ptr(Pg);
+  MkStepC &S = *(MkStepC *)uni_ptr(Sg);
   first = uni(first);
   n = uni(n);
-  const MkRole R = make_role(P, S);
+  const MkRole R = make_role(P, S, (uint32_t)uni((int)lb));
   const MkAct A = mk_act(P, R.par);
   const bool sent = P.sync_mode == MK_SYNC_SENTINEL && !S.multi;
   if (sent) {
@@ -925,7 +923,9 @@ MKD void role_run(const MkProgram *Pg, const MkStep *Sg, int first, int n) {
   if ((int)threadIdx.x < Sg->batch) ctl->pos[threadIdx.x] = gld(Sg->positions + threadIdx.x);
   __syncthreads();
   const int wave = threadIdx.x >> 6;
-  if (wave < MK_NLW) role_loader_entry(Pg, Sg, first, n, wave);
-  else if (wave == MK_SYNCW) role_sync_entry(Pg, Sg, first, n);
-  else role_compute_entry(Pg, Sg, first, n, wave - MK_NLW - 1);
+  uint32_t lb = (uint32_t)(size_t)(lds_char *)mk_role_lds;
+  asm volatile("" : "+s"(lb));  // an opaque value, so it is not propagated back into the callees as a constant
+  if (wave < MK_NLW) role_loader_entry(Pg, Sg, lb, first, n, wave);
+  else if (wave == MK_SYNCW) role_sync_entry(Pg, Sg, lb, first, n);
+  else role_compute_entry(Pg, Sg, lb, first, n, wave - MK_NLW - 1);
 }
