@@ -52,6 +52,7 @@ def main():
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter"],
                     help="execution / synchronisation scheme of the headline number")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
+    ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -95,8 +96,8 @@ def main():
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
 
     def timed(exec_mode, sync_mode, k, w_):
-        eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, sync_mode=sync_mode, exec_mode=exec_mode,
-                            stream=stream)
+        eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, kv_splits=args.kv_splits, sync_mode=sync_mode,
+                            exec_mode=exec_mode, stream=stream)
         try:
             tokens.copy_(torch.tensor(first, dtype=torch.int32))
             positions.copy_(torch.tensor(pos0, dtype=torch.int32))

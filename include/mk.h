@@ -263,8 +263,9 @@ int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
  * 100 MHz real-time counter when its wait began, when its inputs were
  * staged (work began) and when it finished; (cu << 32 | step epoch); for the
  * role-specialised kernel the CU's cumulative ticks of loader waves blocked
- * on a free page and of compute waves waiting for a landed page, and the
- * instruction's page count (else 0).  n_records must cover the plan's
+ * on a free page and of compute waves waiting for a landed page, the
+ * instruction's page count and when its compute waves finished (before the
+ * sync wave's epilogue); else 0.  n_records must cover the plan's
  * instruction count.  NULL switches tracing off.  Synchronises stream. */
 int mk_ctx_set_trace(mk_ctx *ctx, void *d_trace, size_t n_records, void *stream);
 /* Overwrite the host-side step counter of a context.  Setting it ahead of the

@@ -423,11 +423,11 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
   __syncthreads();
   const int last = *s_flag;
   __syncthreads();
-  if (last && tid < S.batch) {
-    const int b = tid;
+  // last arriver: one wave per sequence merges every instruction's (max, index) pair
+  for (int b = tid >> 6; last && b < S.batch; b += MK_NWAVES) {
     float v = -INFINITY;
     int ix = 0x7fffffff;
-    for (int k = 0; k < P.n_lm_parts; ++k) {
+    for (int k = lane; k < P.n_lm_parts; k += 64) {
       const float pv = ldc(P.lm_val + (size_t)k * P.B_max + b);
       const int pi = ldci(P.lm_idx + (size_t)k * P.B_max + b);
       if (better(pv, pi, v, ix)) {
@@ -435,11 +435,22 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
         ix = pi;
       }
     }
-    if (ix == 0x7fffffff) ix = 0;  // every logit NaN: fall back to token 0
-    if (S.next) S.next[b] = ix;
-    if (S.flags & 1u) {
-      S.tokens[b] = ix;
-      S.positions[b] = S.positions[b] + 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(v, o, 64);
+      const int oi = __shfl_xor(ix, o, 64);
+      if (better(ov, oi, v, ix)) {
+        v = ov;
+        ix = oi;
+      }
+    }
+    if (lane == 0) {
+      if (ix == 0x7fffffff) ix = 0;  // every logit NaN: fall back to token 0
+      if (S.next) S.next[b] = ix;
+      if (S.flags & 1u) {
+        S.tokens[b] = ix;
+        S.positions[b] = S.positions[b] + 1;
+      }
     }
   }
   return MK_ST_QUIET;

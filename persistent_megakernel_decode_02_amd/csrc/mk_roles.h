@@ -283,8 +283,10 @@ MKD void loader_publish_one(const MkRole &R, LoaderState &L) {
 
 // Issue one page into the loader's next slot.  Waits (publishing landed
 // pages meanwhile) until the slot's previous page was consumed.  false on abort.
-template <bool FULL>
-MKD bool loader_page(const MkRole &R, LoaderState &L, const char *src, int valid) {
+// SWZ (key/value pages, rows of rb bytes): LDS chunk p of row t receives
+// source chunk p ^ (t & 7) (a permutation of each row's 16-byte chunks)
+template <bool FULL, bool SWZ>
+MKD bool loader_page(const MkRole &R, LoaderState &L, const char *src, int valid, int rb) {
   if (L.s >= (uint32_t)R.np) {
     const uint32_t need = L.s - (uint32_t)R.np + 1u;
     if ((int32_t)(lds_ld(&R.ctl->pg_done[L.slot]) - need) < 0) {
@@ -304,6 +306,10 @@ MKD bool loader_page(const MkRole &R, LoaderState &L, const char *src, int valid
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int off = q * 1024 + lane * 16;
+    if (SWZ) {
+      const int t = off / rb, in_row = off - t * rb;
+      off = t * rb + ((((in_row >> 4) ^ (t & 7)) << 4) | (in_row & 15));
+    }
     if (!FULL && off > valid - 16) off = valid - 16;  // stay inside the source; the tail is never read
     __builtin_amdgcn_global_load_lds((const void *)(src + off), (lds_void *)(dst + q * 1024), 16, 0, 0);
   }

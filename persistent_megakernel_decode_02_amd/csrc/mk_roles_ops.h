@@ -426,141 +426,189 @@ MKD lds_float *attn_wpart(const MkRole &R, int cw) {
   return R.X + (size_t)(G + 2) * d + (size_t)cw * G * (d + 2);
 }
 
-// sum over the lpp (8 or 16) consecutive lanes that hold one key position
-MKD float group_sum(float v, int lpp) {
-  v += dpp_term<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_term<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v += dpp_term<0x141, 0xF>(v);  // row_half_mirror: the other quad of the half row
-  if (lpp == 16) v += dpp_term<0x140, 0xF>(v);  // row_mirror: the other half row
-  return v;
-}
-
 MKD float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Decode attention over this instruction's key blocks (flash-decoding split
-// of the megakernel page, section 2.6's attention instruction).  Lanes come
-// in groups of lpp = d/8, one group per key position, 8 dims per lane; each
-// group keeps its own running max / sum / output for the positions it saw
-// (scores in base 2: the staged queries carry log2(e)/sqrt(d)), and the
-// groups of the wave are merged at the end into one partial per q head.
-MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {
+// ---------------------------------------------------- attention on MFMA
+//
+// Decode attention over this instruction's key blocks (the flash-decoding
+// split of the megakernel page, section 2.6's attention instruction).  A
+// key block is one 4 KiB page: 32 positions for d = 64, 16 for d = 128.
+// Scores and the probability-weighted values are bf16 matrix-core products
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//   scores  S[t][h] = sum_k K[t][k] q[h][k]   (M = 16 positions, N = heads)
+//   output  O[h][n] = sum_t P[h][t] V[t][n]   (M = heads, N = 16 dims, K = 32 positions)
+// Keys and values are bf16 already; the fp32 queries and probabilities are
+// split into bf16 high and low parts (two products each), so the products
+// keep about 16 significant bits, like the fp32 dot products they replace.
+// Heads beyond the group size are zero padding.  Operand layout (one lane
+// i of 64): A[m = i % 16][k = 8 (i / 16) + j], B[k = 8 (i / 16) + j][n = i % 16],
+// D[m = 4 (i / 16) + j][n = i % 16].  The contraction index k may be mapped
+// to dims or positions in any order both operands share: scores use
+// dim = (d/4)(i/16) + 8 s + j for k-step s, so a lane reads one contiguous
+// run of its key row; the value product maps k to position
+// t = j < 4 ? 4 (i/16) + j : 16 + 4 (i/16) + (j - 4), which is exactly where
+// the score product left each probability, so no lanes exchange data.
+
+typedef __bf16 mk_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mk_f32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+MKD mk_f32x4v mfma16x16x32(mk_bf16x8 a, mk_bf16x8 b, mk_f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+MKD mk_bf16x8 as_bf16x8(mk_u32x4 w) { return __builtin_bit_cast(mk_bf16x8, w); }
+// bf16 high / low parts of 8 fp32 values, packed two per word
+MKD void split_hi_lo(const float (&x)[8], mk_u32x4 &hi, mk_u32x4 &lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f2bf(x[e]);
+    l[e] = f2bf(x[e] - __uint_as_float(h[e] << 16));
+  }
+  hi = mk_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  lo = mk_u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+}
+
+// Key/value pages are written to LDS with their 16-byte chunks permuted
+// (chunk c of row t lands in chunk c ^ (t & 7) of that row, done by the
+// loader's per-lane source addresses): the score product reads the same
+// chunk of 16 consecutive rows, which would otherwise hit the same LDS banks.
+MKD int kv_swz(int t, int byte_in_row) { return (((byte_in_row >> 4) ^ (t & 7)) << 4) | (byte_in_row & 15); }
+
+template <int D>
+MKD bool attn_instr_d(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {
+  constexpr int KS = D / 32, NT = D / 16, BP = MK_PAGE / (2 * D), NTILE = BP / 16, DQ = D / 4;
   const int lane = threadIdx.x & 63;
-  const int d = g.d, G = R.P.G;
-  const int lpp = d / 8, ppi = 64 / lpp;
-  const int c8 = (lane % lpp) * 8, pin = lane / lpp;
-  float qv[MK_MAX_GROUP][8];
+  const int G = R.P.G;
+  const int col = lane & 15, qd = lane >> 4;
+  // queries (pre-scaled by log2(e)/sqrt(d)) as the B operand, high and low parts
+  mk_u32x4 qhi[KS], qlo[KS];
 #pragma unroll
-  for (int j = 0; j < MK_MAX_GROUP; ++j) {
-    const lds_f32x4 *q4 = reinterpret_cast<const lds_f32x4 *>(R.X + j * d + c8);
-    const mk_f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const mk_f32x4 a = j < G ? q4[0] : z;
-    const mk_f32x4 b = j < G ? q4[1] : z;
-    qv[j][0] = a.x, qv[j][1] = a.y, qv[j][2] = a.z, qv[j][3] = a.w;
-    qv[j][4] = b.x, qv[j][5] = b.y, qv[j][6] = b.z, qv[j][7] = b.w;
+  for (int s = 0; s < KS; ++s) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = col < G ? R.X[col * D + DQ * qd + 8 * s + e] : 0.f;
+    split_hi_lo(x, qhi[s], qlo[s]);
   }
-  float m[MK_MAX_GROUP], l[MK_MAX_GROUP], o[MK_MAX_GROUP][8];
+  const lds_float *kn = R.X + G * D, *vn = kn + D;  // this step's key and value (bf16-exact)
+  float m = -INFINITY, l = 0.f;                     // running max / partial sum of head `col`
+  mk_f32x4v o[NT];
 #pragma unroll
-  for (int j = 0; j < MK_MAX_GROUP; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-  }
-  const lds_float *kn = R.X + G * d, *vn = kn + d;  // this step's key and value (bf16-rounded)
+  for (int n = 0; n < NT; ++n) o[n] = mk_f32x4v{0.f, 0.f, 0.f, 0.f};
   uint32_t s = seq0 + (uint32_t)(cw * 2);
   int slot = ring_add(slot0, cw * 2, R.np);
   for (int u = cw; u < g.n_units; u += MK_NCW) {
-    const int ta = g.t0 + u * g.bp;
-    const int npos = min(g.bp, g.t1 - ta);
-    const bool here = ta <= g.p && g.p < ta + npos;  // the block holds this step's position
+    const int ta = g.t0 + u * BP;
+    const int npos = min(BP, g.t1 - ta);
     const int vslot = slot + 1 == R.np ? 0 : slot + 1;
     if (!page_wait(R, slot, s) || !page_wait(R, vslot, s + 1)) return false;
-    const lds_char *kp = R.ring + (size_t)slot * MK_PAGE, *vp = R.ring + (size_t)vslot * MK_PAGE;
-    float sc[4][MK_MAX_GROUP];
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int row = pass * ppi + pin;
-      const mk_u32x4 kw = row < npos ? *reinterpret_cast<const lds_u32x4 *>(kp + (size_t)row * 2 * d + c8 * 2)
-                                     : mk_u32x4{0, 0, 0, 0};
-      float k8[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
-                     bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
-      if (here && ta + row == g.p) {  // the page holds the slot's previous contents
-#pragma unroll
-        for (int e = 0; e < 8; ++e) k8[e] = kn[c8 + e];
+    lds_char *kp = R.ring + (size_t)slot * MK_PAGE, *vp = R.ring + (size_t)vslot * MK_PAGE;
+    if (ta <= g.p && g.p < ta + npos) {
+      // the page holds the slot's previous contents: write this step's key and value
+      const int row = g.p - ta;
+      for (int e = lane; e < D; e += 64) {
+        const int off = row * 2 * D + kv_swz(row, 2 * e);
+        *reinterpret_cast<lds_u16 *>(kp + off) = f2bf(kn[e]);
+        *reinterpret_cast<lds_u16 *>(vp + off) = f2bf(vn[e]);
       }
+    }
+    // scores, one 16-position tile at a time
+    float sc[2][4];
 #pragma unroll
-      for (int j = 0; j < MK_MAX_GROUP; ++j) {
-        float a = 0.f;
+    for (int T = 0; T < 2; ++T) {
+      if (T < NTILE) {
+        mk_f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+        const int t = 16 * T + col;
+        const lds_char *kr = kp + t * 2 * D;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf(qv[j][e], k8[e], a);
-        a = group_sum(a, lpp);
-        sc[pass][j] = row < npos ? a : -INFINITY;
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const mk_bf16x8 a = as_bf16x8(*reinterpret_cast<const lds_u32x4 *>(kr + kv_swz(t, 2 * DQ * qd + 16 * s2)));
+          acc = mfma16x16x32(a, as_bf16x8(qhi[s2]), acc);
+          acc = mfma16x16x32(a, as_bf16x8(qlo[s2]), acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[T][j] = 16 * T + 4 * qd + j < npos ? acc[j] : -INFINITY;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[T][j] = -INFINITY;
       }
     }
     page_free(R, slot, s);
-    float pr[4][MK_MAX_GROUP];
+    // online softmax for head `col` (its four lane rows share the max)
+    float mb = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);
+    const float c = m == mn ? 1.f : exp2_fast(m - mn);
+    float pr[8];
 #pragma unroll
-    for (int j = 0; j < MK_MAX_GROUP; ++j) {
-      const float mb = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
-      const float mn = fmaxf(m[j], mb);
-      const float c = m[j] == mn ? 1.f : exp2_fast(m[j] - mn);
-      float ls = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const float v = sc[j >> 2][j & 3];
+      pr[j] = v == -INFINITY ? 0.f : exp2_fast(v - mn);
+    }
+    float ls = 0.f;
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        pr[pass][j] = sc[pass][j] == -INFINITY ? 0.f : exp2_fast(sc[pass][j] - mn);
-        ls += pr[pass][j];
-      }
-      l[j] = fmaf(l[j], c, ls);
-      m[j] = mn;
+    for (int j = 0; j < 8; ++j) ls += pr[j];
+    l = fmaf(l, c, ls);
+    m = mn;
+    // rescale the output rows: row h of the output sits in register h % 4 of
+    // lanes 16 (h / 4) ..; the real heads (h < 4) are in the first 16 lanes
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[j][e] *= c;
+    for (int j = 0; j < 4; ++j) {
+      const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), j));
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n][j] *= cj;
+    }
+    // probabilities as the A operand (rows: heads, k: positions t(qd, j))
+    mk_u32x4 phi, plo;
+    split_hi_lo(pr, phi, plo);
+    // values as the B operand: column = dim, k = position t(qd, j)
+    int vrow[8];
+    bool von[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4);
+      von[j] = t < npos;
+      vrow[j] = min(t, BP - 1);
     }
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int row = pass * ppi + pin;
-      const mk_u32x4 vw = row < npos ? *reinterpret_cast<const lds_u32x4 *>(vp + (size_t)row * 2 * d + c8 * 2)
-                                     : mk_u32x4{0, 0, 0, 0};
-      float v8[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
-                     bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
-      if (here && ta + row == g.p) {
+    for (int n = 0; n < NT; ++n) {
+      const int dim = 16 * n + col;
+      uint32_t vv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = vn[c8 + e];
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t raw = *reinterpret_cast<const lds_u16 *>(vp + vrow[j] * 2 * D + kv_swz(vrow[j], 2 * dim));
+        vv[j] = von[j] ? raw : 0u;
       }
-#pragma unroll
-      for (int j = 0; j < MK_MAX_GROUP; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pr[pass][j], v8[e], o[j][e]);
+      const mk_u32x4 vw = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16), vv[6] | (vv[7] << 16)};
+      o[n] = mfma16x16x32(as_bf16x8(phi), as_bf16x8(vw), o[n]);
+      o[n] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vw), o[n]);
     }
     page_free(R, vslot, s + 1);
     s += (uint32_t)(MK_NCW * 2);
     slot = ring_add(slot, MK_NCW * 2, R.np);
   }
-  // merge the lane groups: rescale to the wave max, then sum groups lane-wise
+  // this wave's partial per head: max, sum, unnormalised output (base-2 scores)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
   lds_float *wp = attn_wpart(R, cw);
+  if (lane < G) {
+    wp[lane * (D + 2)] = m;
+    wp[lane * (D + 2) + 1] = l;
+  }
+  if (qd == 0) {
 #pragma unroll
-  for (int j = 0; j < MK_MAX_GROUP; ++j) {
-    if (j >= G) continue;
-    const float M = wave_max_all(m[j]);
-    const float f = m[j] == -INFINITY ? 0.f : exp2_fast(m[j] - M);
-    const float L = wave_total(l[j] * f) * (1.0f / (float)lpp);
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[j][e] * f;
-      if (lpp == 8) v += dpp_term<0x128, 0xF>(v);  // row_ror:8: the other 8-lane group of the row
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      o[j][e] = v;
-    }
-    if (lane < lpp) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wp[j * (d + 2) + 2 + c8 + e] = o[j][e];
-    }
-    if (lane == 0) {
-      wp[j * (d + 2)] = M;
-      wp[j * (d + 2) + 1] = L;
-    }
+      for (int j = 0; j < 4; ++j)
+        if (j < G) wp[j * (D + 2) + 2 + 16 * n + col] = o[n][j];
   }
   return true;
+}
+
+MKD bool attn_instr(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {
+  return g.d == 64 ? attn_instr_d<64>(R, g, seq0, slot0, cw) : attn_instr_d<128>(R, g, seq0, slot0, cw);
 }
 
 // ------------------------------------------------------- sync epilogues
@@ -678,17 +726,21 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
   if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
   old = __builtin_amdgcn_readfirstlane(old);
   if (old + 1u != (S.epoch + 1u) * (uint32_t)P.n_lm_parts) return 0;
-  if (lane < B) {
-    const int b = lane;
+  // last arriver: merge every instruction's (max, index) pair, lanes in parallel
+  for (int b = 0; b < B; ++b) {
     float v = -INFINITY;
     int ix = 0x7fffffff;
-    for (int k = 0; k < P.n_lm_parts; ++k)
+    for (int k = lane; k < P.n_lm_parts; k += 64)
       argmax_merge(v, ix, ldc(P.lm_val + (size_t)k * P.B_max + b), ldci(P.lm_idx + (size_t)k * P.B_max + b));
-    if (ix == 0x7fffffff) ix = 0;
-    if (S.next) gst(S.next + b, ix);
-    if (S.flags & 1u) {
-      gst(S.tokens + b, ix);
-      gst(S.positions + b, R.ctl->pos[b] + 1);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) argmax_merge(v, ix, __shfl_xor(v, o, 64), __shfl_xor(ix, o, 64));
+    if (lane == 0) {
+      if (ix == 0x7fffffff) ix = 0;
+      if (S.next) gst(S.next + b, ix);
+      if (S.flags & 1u) {
+        gst(S.tokens + b, ix);
+        gst(S.positions + b, R.ctl->pos[b] + 1);
+      }
     }
   }
   return 0;
@@ -732,7 +784,7 @@ MKD void wave_signal_event(const MkRole &R, int ev, int slot) {
     stcu(P.flags + P.ev_flag_base[ev] + slot, R.S.epoch + 1u);
 }
 
-template <bool FULL>
+template <bool FULL, bool SWZ>
 MKD bool loader_instr(const MkRole &R, LoaderState &L, const MkGeo &g, uint32_t seq) {
   const uint32_t npg = (uint32_t)(g.n_units * g.ppu);
   uint32_t j = L.s - seq;  // first page of this instruction with the loader's parity
@@ -745,7 +797,7 @@ MKD bool loader_instr(const MkRole &R, LoaderState &L, const MkGeo &g, uint32_t 
   for (; j < npg; j += MK_NLW) {
     const char *src = (h ? row1 : row0) + (size_t)kk * MK_PAGE;
     const int valid = FULL ? MK_PAGE : mk_page_valid(g, u, kk);
-    if (!loader_page<FULL>(R, L, src, valid)) return false;
+    if (!loader_page<FULL, SWZ>(R, L, src, valid, 2 * g.d)) return false;
 #pragma unroll
     for (int i = 0; i < MK_NLW; ++i) {
       if (++kk == g.ppr) {
@@ -774,6 +826,12 @@ MKD bool loader_instr(const MkRole &R, LoaderState &L, const MkGeo &g, uint32_t 
 
 extern __shared__ __attribute__((aligned(16))) char mk_role_lds[];
 
+// A role's wave ends inside its function: the functions never return, so
+// they need not save the registers a returning call must preserve.
+[[noreturn]] MKD void mk_end() {
+  __builtin_amdgcn_endpgm();
+}
+
 MKD int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 MKD const void *uni_ptr(const void *p) {
   const uint64_t v = (uint64_t)p;
@@ -798,7 +856,7 @@ MKD MkRole make_role(MkProgC &P, MkStepC &S, uint32_t lb) {
                 par};
 }
 
-__device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
+[[noreturn]] __device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
                                                 int lid) {
   MkProgC &P = *(MkProgC *)uni_ptr(Pg);
   MkStepC &S = *(MkStepC *)uni_ptr(Sg);
@@ -815,14 +873,17 @@ __device__ __noinline__ void role_loader_entry(const MkProgram *Pg, const MkStep
       role_abort(R);
       break;
     }
-    const bool ok = g.full ? loader_instr<true>(R, L, g, seq) : loader_instr<false>(R, L, g, seq);
-    if (!ok) return;
+    const bool ok = in.op == MKOP_ATTN ? loader_instr<false, true>(R, L, g, seq)
+                    : g.full          ? loader_instr<true, false>(R, L, g, seq)
+                                      : loader_instr<false, false>(R, L, g, seq);
+    if (!ok) mk_end();
     seq += (uint32_t)(g.n_units * g.ppu);
   }
   while (L.inflight > 0) loader_publish_one(R, L);
+  mk_end();
 }
 
-__device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
+[[noreturn]] __device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n,
                                                  int cw) {
   MkProgC &P = *(MkProgC *)uni_ptr(Pg);
   MkStepC &S = *(MkStepC *)uni_ptr(Sg);
@@ -838,9 +899,9 @@ __device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkSte
     MkGeo g;
     if (!mk_geo(P, S, R.ctl, in, g)) {
       role_abort(R);
-      return;
+      mk_end();
     }
-    if (!role_wait(R, &R.ctl->x_ready, (uint32_t)k + 1u, true)) return;
+    if (!role_wait(R, &R.ctl->x_ready, (uint32_t)k + 1u, true)) mk_end();
     bool ok;
     const bool two = in.op == MKOP_GATEUP;
     if (in.op == MKOP_ATTN) ok = attn_instr(R, g, seq, slot0, cw);
@@ -849,15 +910,16 @@ __device__ __noinline__ void role_compute_entry(const MkProgram *Pg, const MkSte
     else if (B == 1 && g.full) ok = two ? gemv_fast<false, true>(R, g, seq, slot0, cw)
                                         : gemv_fast<false, false>(R, g, seq, slot0, cw);
     else ok = two ? gemv_general<true>(R, g, seq, slot0, cw, B) : gemv_general<false>(R, g, seq, slot0, cw, B);
-    if (!ok) return;
+    if (!ok) mk_end();
     if ((threadIdx.x & 63) == 0) lds_add(&R.ctl->cw_done, 1u);  // one increment per wave
     const uint32_t npg = (uint32_t)(g.n_units * g.ppu);
     seq += npg;
     slot0 = (int)(((uint32_t)slot0 + npg) % (uint32_t)R.np);
   }
+  mk_end();
 }
 
-__device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n) {
+[[noreturn]] __device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *Sg, uint32_t lb, int first, int n) {
   MkProgC &P = *(MkProgC *)uni_ptr(Pg);
   MkStepC &S = *(MkStepC *)uni_ptr(Sg);
   first = uni(first);
@@ -878,21 +940,22 @@ __device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *
     if (!mk_geo(P, S, R.ctl, in, g)) {
       if ((threadIdx.x & 63) == 0) mk_raise(P, MK_E_INPUT, 1000 + in.r0);
       role_abort(R);
-      return;
+      mk_end();
     }
     const uint64_t tw = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     uint32_t gain[MK_XCH][2];
     if (normed_op(in.op)) load_bf16_chunks(norm_gain(P, in), P.H, gain);  // ahead of the wait
-    if (!S.multi && !sent && in.wait_ev >= 0 && !wave_wait_event(R, in.wait_ev)) return;
-    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)k * MK_NCW)) return;  // X is free again
-    if (!sync_stage(R, in, g, A, sent, gain)) return;
+    if (!S.multi && !sent && in.wait_ev >= 0 && !wave_wait_event(R, in.wait_ev)) mk_end();
+    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)k * MK_NCW)) mk_end();  // X is free again
+    if (!sync_stage(R, in, g, A, sent, gain)) mk_end();
     lds_st(&R.ctl->x_ready, (uint32_t)k + 1u);
     const uint64_t ts = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)(k + 1) * MK_NCW, true)) return;
+    if (!role_wait(R, &R.ctl->cw_done, (uint32_t)(k + 1) * MK_NCW, true)) mk_end();
+    const uint64_t tc = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     const int sig = sync_epilogue(R, in, g, A);
     if (sig < 0) {
       role_abort(R);
-      return;
+      mk_end();
     }
     if (sig && !S.multi && !sent && in.sig_ev >= 0) {
       wait_vm();
@@ -908,9 +971,10 @@ __device__ __noinline__ void role_sync_entry(const MkProgram *Pg, const MkStep *
       r[4] = lds_ld(&R.ctl->st_load_block);
       r[5] = lds_ld(&R.ctl->st_page_wait);
       r[6] = (uint64_t)(g.n_units * g.ppu);
-      r[7] = 0;
+      r[7] = tc;  // compute waves done; the epilogue follows
     }
   }
+  mk_end();
 }
 
 // Entry used by both kernels: run instructions [first, first + n) of the
