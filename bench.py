@@ -42,6 +42,39 @@ def bytes_per_pass(shape, positions):
     return total / len(positions)
 
 
+COPY_PROBE_BYTES = 256 << 20
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the HIP/C++ sources of the library (identifies the kernel build)."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "persistent_megakernel_decode_02_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, mode: str):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}_{mode}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources") != kernel_source_digest():
+        return None
+    return round(float(kv["hbm_bytes_per_launch"]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -53,6 +86,8 @@ def main():
                     help="execution / synchronisation scheme of the headline number")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run one 256 MiB device copy (the scale reference for HBM byte counters)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -90,6 +125,13 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s ({args.workload})")
 
     stream = torch.cuda.current_stream()
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {COPY_PROBE_BYTES} bytes read and written")
+        del src, dst
     tokens = torch.tensor(first, dtype=torch.int32, device=dev)
     positions = torch.tensor(pos0, dtype=torch.int32, device=dev)
     logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
@@ -145,7 +187,7 @@ def main():
     bpp = bytes_per_pass(s, positions_timed) if B == 1 else bytes_per_pass(s, positions_timed) * 1.0
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
             "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel"}.get(
                 args.mode, "mk_role_mega_kernel"),
             "bytes_per_launch": bpp if args.mode != "multi" else None}
