@@ -123,6 +123,77 @@ MKD bool stage_scalars(const MkRole &R, lds_float *dst, const float *src, int n,
   return true;
 }
 
+// One round of a vector stage together with up to 64 scalars (any
+// alignment; lane i loads scalar i): all loads in flight at once, polled
+// together, so the residual rows cost no extra memory round trip.
+MKD bool load_vec_and_scalars(const MkRole &R, const float *src, int n, const float *ssrc, int sn, bool sentinel,
+                              mk_u32x4 (&v)[MK_XCH], float &sv) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = mk_rsrc(src, (uint32_t)n * 4u);
+  const int nch = (n + 255) / 256;
+  const bool has_s = lane < sn;
+#pragma unroll
+  for (int j = 0; j < MK_XCH; ++j)
+    if (j < nch) v[j] = ldc16(rs, (j * 64 + lane) * 16);
+  sv = has_s ? ldc(ssrc + lane) : 0.f;
+  if (!sentinel) return true;
+  uint64_t t0 = 0;
+  uint32_t spins = 0;
+  while (true) {
+    bool miss = has_s && __float_as_uint(sv) == MK_SENTINEL;
+#pragma unroll
+    for (int j = 0; j < MK_XCH; ++j)
+      if (j < nch) miss = miss || ((j * 64 + lane) * 4 < n && has_sentinel(v[j]));
+    if (!__any(miss)) return true;
+    if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_s_sleep(1);
+    if ((++spins & 63u) == 0 && !poll_check(R, t0, 0x20002)) return false;
+#pragma unroll
+    for (int j = 0; j < MK_XCH; ++j)
+      if (j < nch && (j * 64 + lane) * 4 < n && has_sentinel(v[j])) v[j] = ldc16(rs, (j * 64 + lane) * 16);
+    if (has_s && __float_as_uint(sv) == MK_SENTINEL) sv = ldc(ssrc + lane);
+  }
+}
+
+// The attention instruction's query group, key and value (each a multiple
+// of 64 floats, at most 512 / 128 / 128): one round, polled together.
+MKD bool stage_qkv(const MkRole &R, const float *qs, int nqf, const float *ks, const float *vs, int d, lds_float *dq,
+                   lds_float *dk, lds_float *dv, bool sentinel) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rq = mk_rsrc(qs, (uint32_t)nqf * 4u), rk = mk_rsrc(ks, (uint32_t)d * 4u),
+                               rv = mk_rsrc(vs, (uint32_t)d * 4u);
+  mk_u32x4 a0 = ldc16(rq, lane * 16), a1 = ldc16(rq, (64 + lane) * 16);
+  mk_u32x4 bk = ldc16(rk, lane * 16), bv = ldc16(rv, lane * 16);
+  const bool on0 = lane * 4 < nqf, on1 = (64 + lane) * 4 < nqf, onk = lane * 4 < d;
+  if (sentinel) {
+    uint64_t t0 = 0;
+    uint32_t spins = 0;
+    while (true) {
+      const bool m0 = on0 && has_sentinel(a0), m1 = on1 && has_sentinel(a1), mk = onk && has_sentinel(bk),
+                 mv = onk && has_sentinel(bv);
+      if (!__any(m0 || m1 || mk || mv)) break;
+      if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+      __builtin_amdgcn_s_sleep(1);
+      if ((++spins & 63u) == 0 && !poll_check(R, t0, 0x20003)) return false;
+      if (m0) a0 = ldc16(rq, lane * 16);
+      if (m1) a1 = ldc16(rq, (64 + lane) * 16);
+      if (mk) bk = ldc16(rk, lane * 16);
+      if (mv) bv = ldc16(rv, lane * 16);
+    }
+  }
+  const auto put = [](lds_float *dst, mk_u32x4 w) {
+    *reinterpret_cast<lds_f32x4 *>(dst) =
+        mk_f32x4{__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+  };
+  if (on0) put(dq + lane * 4, a0);
+  if (on1) put(dq + (64 + lane) * 4, a1);
+  if (onk) {
+    put(dk + lane * 4, bk);
+    put(dv + lane * 4, bv);
+  }
+  return true;
+}
+
 // bf16 values of a length-n vector in the lane layout of load_vec (4 per chunk)
 MKD void load_bf16_chunks(const uint16_t *p, int n, uint32_t (&g)[MK_XCH][2]) {
   const int lane = threadIdx.x & 63;
@@ -179,8 +250,15 @@ MKD const uint16_t *norm_gain(MkProgC &P, const MkInstr &in) {
 
 // returns false on abort (error already raised).  `gain` holds the norm
 // gains of a normed op, loaded before the dependency wait.
+// values a stage needs that do not depend on the instruction's input, loaded
+// before the dependency wait: norm gains, RoPE cos/sin of this position
+struct StagePre {
+  uint32_t gain[MK_XCH][2];
+  float rc, rs;
+};
+
 MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const MkAct &A, bool sent,
-                    const uint32_t (&gain)[MK_XCH][2]) {
+                    const StagePre &pre) {
   MkProgC &P = R.P;
   MkStepC &S = R.S;
   const int lane = threadIdx.x & 63;
@@ -209,7 +287,7 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
                                                     : A.xout + ((size_t)(P.L - 1) * P.B_max + b) * H;
           if (!load_vec(R, src, H, sent, v)) return false;
         }
-        norm_store(R.X + (size_t)b * H, H, v, gain, P.eps);
+        norm_store(R.X + (size_t)b * H, H, v, pre.gain, P.eps);
       }
       return true;
     }
@@ -218,6 +296,11 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       const int K = g.K, nr = in.r1 - in.r0;
       for (int b = 0; b < B; ++b) {
         lds_float *rd = R.resid + (size_t)b * nr;
+        const float *src = in.op == MKOP_OPROJ ? A.attn + ((size_t)l * P.B_max + b) * K
+                                               : A.hbuf + ((size_t)l * P.B_max + b) * K;
+        const float *rs = in.op == MKOP_OPROJ ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H + in.r0
+                                              : A.xmid + ((size_t)l * P.B_max + b) * H + in.r0;
+        int sn = nr <= 64 ? nr : 0;  // residual rows ride along with the first round
         if (in.op == MKOP_OPROJ && l == 0) {
           const int tok = gld(S.tokens + b);
           if (tok < 0 || tok >= P.V) {
@@ -226,15 +309,19 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
             return false;
           }
           for (int i = lane; i < nr; i += 64) rd[i] = bf2f(gld(P.embed + (size_t)tok * H + in.r0 + i));
-        } else {
-          // residual rows first: they were complete before this instruction's input
-          const float *rs = in.op == MKOP_OPROJ ? A.xout + ((size_t)(l - 1) * P.B_max + b) * H + in.r0
-                                                : A.xmid + ((size_t)l * P.B_max + b) * H + in.r0;
+          sn = 0;
+        } else if (nr > 64) {
           if (!stage_scalars(R, rd, rs, nr, sent)) return false;
         }
-        const float *src = in.op == MKOP_OPROJ ? A.attn + ((size_t)l * P.B_max + b) * K
-                                               : A.hbuf + ((size_t)l * P.B_max + b) * K;
-        if (!stage_vec(R, R.X + (size_t)b * K, src, K, sent)) return false;
+        lds_float *x = R.X + (size_t)b * K;
+        for (int base = 0; base < K; base += 256 * MK_XCH) {
+          mk_u32x4 v[MK_XCH];
+          float sv;
+          const int m = min(K - base, 256 * MK_XCH);
+          if (!load_vec_and_scalars(R, src + base, m, rs, base == 0 ? sn : 0, sent, v, sv)) return false;
+          store_vec(x + base, m, v);
+          if (base == 0 && lane < sn) rd[lane] = sv;
+        }
       }
       return true;
     }
@@ -243,16 +330,17 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       const int R0 = (P.nq + 2 * P.nkv) * d;
       const float *qkv = A.qkv + ((size_t)l * P.B_max + b) * R0;
       lds_float *q = R.X, *kc = R.X + G * d, *vc = kc + d;
-      if (!stage_vec(R, q, qkv + (size_t)gg * G * d, G * d, sent)) return false;
-      if (!stage_vec(R, kc, qkv + (size_t)P.nq * d + (size_t)gg * d, d, sent)) return false;
-      if (!stage_vec(R, vc, qkv + (size_t)(P.nq + P.nkv) * d + (size_t)gg * d, d, sent)) return false;
-      const float *cs = P.rope + (size_t)g.p * d;  // read below through gld
-      // queries are pre-scaled by log2(e) / sqrt(d): scores come out in base 2
+      if (!stage_qkv(R, qkv + (size_t)gg * G * d, G * d, qkv + (size_t)P.nq * d + (size_t)gg * d,
+                     qkv + (size_t)(P.nq + P.nkv) * d + (size_t)gg * d, d, q, kc, vc, sent))
+        return false;
+      // queries are pre-scaled by log2(e) / sqrt(d): scores come out in base 2.
+      // pre.rc / pre.rs: cos and sin of pair i = lane % half at this position
+      // (every element a lane handles below has that pair index)
       const float qs = 1.4426950408889634f / sqrtf((float)d);
       for (int e = lane; e < (G + 1) * half; e += 64) {
         const int j = e / half, i = e - j * half;  // j == G is the key
         lds_float *u = j < G ? q + j * d : kc;
-        const float a = u[i], c = u[i + half], co = gld(cs + 2 * i), si = gld(cs + 2 * i + 1);
+        const float a = u[i], c = u[i + half], co = pre.rc, si = pre.rs;
         float r0 = a * co - c * si, r1 = c * co + a * si;
         if (j == G) {
           r0 = bf2f(f2bf(r0));
@@ -943,11 +1031,16 @@ MKD MkRole make_role(MkProgC &P, MkStepC &S, uint32_t lb) {
       mk_end();
     }
     const uint64_t tw = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    uint32_t gain[MK_XCH][2];
-    if (normed_op(in.op)) load_bf16_chunks(norm_gain(P, in), P.H, gain);  // ahead of the wait
+    StagePre pre;  // ahead of the wait
+    if (normed_op(in.op)) load_bf16_chunks(norm_gain(P, in), P.H, pre.gain);
+    if (in.op == MKOP_ATTN) {
+      const int half = P.d / 2, i = (threadIdx.x & 63) % half;
+      pre.rc = gld(P.rope + (size_t)g.p * P.d + 2 * i);
+      pre.rs = gld(P.rope + (size_t)g.p * P.d + 2 * i + 1);
+    }
     if (!S.multi && !sent && in.wait_ev >= 0 && !wave_wait_event(R, in.wait_ev)) mk_end();
     if (!role_wait(R, &R.ctl->cw_done, (uint32_t)k * MK_NCW)) mk_end();  // X is free again
-    if (!sync_stage(R, in, g, A, sent, gain)) mk_end();
+    if (!sync_stage(R, in, g, A, sent, pre)) mk_end();
     lds_st(&R.ctl->x_ready, (uint32_t)k + 1u);
     const uint64_t ts = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     if (!role_wait(R, &R.ctl->cw_done, (uint32_t)(k + 1) * MK_NCW, true)) mk_end();
