@@ -202,7 +202,7 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // stream over the CUs
   int S = opts->kv_splits;
   if (S == 0) {
-    int64_t s1 = ceil_div(p->max_ctx, 256);
+    int64_t s1 = ceil_div(p->max_ctx, 384);
     int64_t cap = std::max<int64_t>(1, n_cu / (B * nkv));
     S = (int)std::min(s1, cap);
     S = (int)std::max<int64_t>(S, ceil_div(p->max_ctx, 1024));
