@@ -21,6 +21,16 @@
 #define MKD __device__ __forceinline__
 
 typedef uint32_t mk_u32x4 __attribute__((ext_vector_type(4)));
+// LDS-typed pointers (address space 3): ds_* instructions, no generic-pointer checks
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) mk_u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mk_f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
 
 #define MK_E_TIMEOUT (-7)
 #define MK_E_INPUT (-8)
@@ -52,6 +62,24 @@ MKD uint32_t addcu(uint32_t *p, uint32_t v) { return __hip_atomic_fetch_add((MK_
 // plain global store / load (no coherence requirement)
 template <class T> MKD void gst(T *p, T v) { *(MK_G(T) *)p = v; }
 template <class T> MKD T gld(const T *p) { return *(const MK_G(T) *)p; }
+
+MKD __amdgpu_buffer_rsrc_t mk_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+// 16-byte load with device scope (sc1): coherent across XCDs
+MKD mk_u32x4 ldc16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
+}
+
+// Thread index as an opaque per-use value: the engine's instruction loop
+// inlines every op, and values derived from a loop-invariant thread index
+// would otherwise be hoisted out of that loop and stay live (in registers)
+// across all ops.
+MKD int mk_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // wait until this wave's outstanding memory operations (stores included) completed
 MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -98,6 +126,37 @@ MKD float wave_max_all(float v) {
   v = fmaxf(v, dpp_keep<0x143, 0xC>(v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+
+// 2^x on the transcendental unit (v_exp_f32)
+MKD float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ----------------------------------------------------- bf16 MFMA 16x16x32
+// Operand layout of v_mfma_f32_16x16x32_bf16 (64 lanes): lane i holds row
+// (A) or column (B) i % 16 and the eight k values 8 (i / 16) .. + 7; the fp32
+// result lane i holds column i % 16, rows 4 (i / 16) + j for j = 0..3.
+typedef __bf16 mk_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mk_f32x4v __attribute__((ext_vector_type(4)));
+
+MKD mk_f32x4v mfma16x16x32(mk_bf16x8 a, mk_bf16x8 b, mk_f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+MKD mk_bf16x8 as_bf16x8(mk_u32x4 w) { return __builtin_bit_cast(mk_bf16x8, w); }
+// bf16 high / low parts of 8 fp32 values, packed two per word
+MKD void split_hi_lo(const float (&x)[8], mk_u32x4 &hi, mk_u32x4 &lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f2bf(x[e]);
+    l[e] = f2bf(x[e] - __uint_as_float(h[e] << 16));
+  }
+  hi = mk_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  lo = mk_u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+}
+
+// Key/value rows are written to LDS with their 16-byte chunks permuted
+// (chunk c of row t lands in chunk c ^ (t & 7) of that row): the score product reads the same
+// chunk of 16 consecutive rows, which would otherwise hit the same LDS banks.
+MKD int kv_swz(int t, int byte_in_row) { return (((byte_in_row >> 4) ^ (t & 7)) << 4) | (byte_in_row & 15); }
 
 // sum over the workgroup; red: LDS scratch of MK_NWAVES floats
 MKD float block_sum(float v, float *red) {

@@ -12,7 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include "mk_launch.h"
-#include "mk_ops.h"
+#include "mk_ops_batched.h"
 #include "mk_roles_ops.h"
 
 // Role-specialised persistent kernel: one workgroup per CU runs the CU's

@@ -22,6 +22,23 @@
 #define MK_CTL_BYTES 1024                 // LDS control block
 #define MK_LDS_TOTAL (160 * 1024)         // LDS of one gfx950 workgroup
 
+// batched projections of the homogeneous engine (bf16 MFMA, up to 16 sequences)
+#define MK_MFMA_MIN_BATCH 2                   // sequences from which projections run on MFMA
+#define MK_BKC 2048                           // input columns staged in LDS per chunk
+#define MK_BROW (MK_BKC * 2 + 16)             // bytes per sequence row of one bf16 plane (+16: bank skew)
+#define MK_BPLANE (MK_MAX_BATCH * MK_BROW)    // one bf16 plane (high or low parts) of the staged inputs
+#define MK_BRED (2 * MK_BPLANE)               // per-wave fp32 partial tiles [MK_NWAVES][256]
+#define MK_BARG (MK_BRED + MK_NWAVES * 1024)  // per-wave argmax (value, index) per sequence
+#define MK_BLDS (MK_BARG + MK_NWAVES * MK_MAX_BATCH * 8)
+
+// attention instruction of the homogeneous engine (byte offsets into dynamic LDS)
+#define MK_FA_Q 0                                                // [G][d] fp32 scaled, rotated queries
+#define MK_FA_KN (MK_FA_Q + MK_MAX_GROUP * 128 * 4)              // [d] bf16 key of this step
+#define MK_FA_VN (MK_FA_KN + 256)                                // [d] bf16 value of this step
+#define MK_FA_VB (MK_FA_VN + 256)                                // [MK_NWAVES][32][2 d + 16 bytes] bf16 value blocks
+#define MK_FA_WP (MK_FA_VB + MK_NWAVES * 32 * (2 * 128 + 16))    // [MK_NWAVES][G][d + 2] wave partials
+#define MK_FA_LDS (MK_FA_WP + MK_NWAVES * MK_MAX_GROUP * 130 * 4)
+
 enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
 enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2 };
 

@@ -41,13 +41,6 @@
 #define MK_QMAX 12                        // pages a loader keeps in flight (4 loads each, vmcnt <= 63)
 #define MK_SENTINEL 0x7FBADBADu           // quiet NaN payload the arithmetic never produces
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef __attribute__((address_space(3))) mk_u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) float lds_float;
-typedef float mk_f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) mk_f32x4 lds_f32x4;
 
 // LDS control block (start of dynamic LDS)
 struct MkCtl {

@@ -6,16 +6,6 @@
 #define MK_SYNC_SENTINEL MKSYNC_SENTINEL
 #define MK_XCH 16  // 16-byte chunks per lane the sync wave stages in one round (4096 floats)
 
-// ----------------------------------------------- device-coherent vector loads
-
-MKD __amdgpu_buffer_rsrc_t mk_rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
-}
-// 16-byte load with device scope (sc1): coherent across XCDs
-MKD mk_u32x4 ldc16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
-}
-
 // activation buffers of this step (two parities in sentinel mode)
 struct MkAct {
   float *qkv, *attn, *xmid, *hbuf, *xout;
@@ -514,7 +504,6 @@ MKD lds_float *attn_wpart(const MkRole &R, int cw) {
   return R.X + (size_t)(G + 2) * d + (size_t)cw * G * (d + 2);
 }
 
-MKD float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------- attention on MFMA
 //
@@ -537,31 +526,7 @@ MKD float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // t = j < 4 ? 4 (i/16) + j : 16 + 4 (i/16) + (j - 4), which is exactly where
 // the score product left each probability, so no lanes exchange data.
 
-typedef __bf16 mk_bf16x8 __attribute__((ext_vector_type(8)));
-typedef float mk_f32x4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-MKD mk_f32x4v mfma16x16x32(mk_bf16x8 a, mk_bf16x8 b, mk_f32x4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-MKD mk_bf16x8 as_bf16x8(mk_u32x4 w) { return __builtin_bit_cast(mk_bf16x8, w); }
-// bf16 high / low parts of 8 fp32 values, packed two per word
-MKD void split_hi_lo(const float (&x)[8], mk_u32x4 &hi, mk_u32x4 &lo) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f2bf(x[e]);
-    l[e] = f2bf(x[e] - __uint_as_float(h[e] << 16));
-  }
-  hi = mk_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  lo = mk_u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
-}
-
-// Key/value pages are written to LDS with their 16-byte chunks permuted
-// (chunk c of row t lands in chunk c ^ (t & 7) of that row, done by the
-// loader's per-lane source addresses): the score product reads the same
-// chunk of 16 consecutive rows, which would otherwise hit the same LDS banks.
-MKD int kv_swz(int t, int byte_in_row) { return (((byte_in_row >> 4) ^ (t & 7)) << 4) | (byte_in_row & 15); }
 
 template <int D>
 MKD bool attn_instr_d(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0, int cw) {

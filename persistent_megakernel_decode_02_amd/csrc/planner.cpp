@@ -95,15 +95,15 @@ static int role_lds_layout(mk_plan *p) {
 
 static int lds_requirement(const mk_plan *p) {
   const mk_model_shape &s = p->shape;
-  const int B = p->B, d = s.head_dim, G = p->G;
+  const int B = p->B, d = s.head_dim;
   int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * d, (int64_t)s.ffn});
-  // GEMV ops stage one sequence's input vector at a time
+  // vector GEMV ops stage one sequence's input vector at a time; with two or
+  // more sequences the projections stage bf16 high/low planes of every
+  // sequence's inputs (MK_BKC columns at a time) for the matrix cores
   int64_t gemv = kmax * 4 + (int64_t)MK_NWAVES * 16 + 256;
-  (void)B;
-  int64_t chunk = ceil_div(p->max_ctx, p->S);
-  int64_t attn = (int64_t)G * d * 4 + 2 * d * 4 + 2 * d * 2 + (int64_t)G * chunk * 4 + MK_BLOCK * 4 +
-                 (int64_t)G * 16 + 256;
-  return (int)std::max(gemv, attn);
+  if (B >= MK_MFMA_MIN_BATCH) gemv = std::max<int64_t>(gemv, MK_BLDS);
+  // attention: queries, this step's key/value, per-wave value blocks and partials
+  return (int)std::max<int64_t>(gemv, MK_FA_LDS);
 }
 
 void mk_plan_finalize_lists(mk_plan *p) {
@@ -197,20 +197,13 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   p->G = nq / nkv;
   const int R = (nq + 2 * nkv) * d;
 
-  // attention splits: enough key-range pieces to keep one split's scores in
-  // LDS (<= 1024 positions) and, when contexts are long, to spread the key
-  // stream over the CUs
+  // attention splits: when contexts are long, spread the key stream over the
+  // CUs (about one split per 384 positions, at most one unit per CU)
   int S = opts->kv_splits;
   if (S == 0) {
     int64_t s1 = ceil_div(p->max_ctx, 384);
     int64_t cap = std::max<int64_t>(1, n_cu / (B * nkv));
-    S = (int)std::min(s1, cap);
-    S = (int)std::max<int64_t>(S, ceil_div(p->max_ctx, 1024));
-    S = std::max(S, 1);
-  }
-  if (opts->exec_mode == MK_EXEC_FLAT && ceil_div(p->max_ctx, S) > 1024) {
-    delete p;
-    return MK_ERR_UNSUPPORTED;
+    S = (int)std::max<int64_t>(1, std::min(s1, cap));
   }
   p->S = S;
 

@@ -114,6 +114,44 @@ def test_llama1b_pos8192_split_attention(llama1b, mode):
     check_kv(res)
 
 
+# Batched decode (projections on the matrix cores): per-sequence context
+# lengths drawn uniformly, every sequence checked against the oracle.
+TINY_BATCHED = {b: si.Workload(f"tiny_b{b}", TINY.shape, batch=b, steps=6, start_pos=-1, len_lo=1, len_hi=100,
+                               max_ctx=TINY.max_ctx) for b in (2, 5, 16)}
+
+
+@pytest.mark.parametrize("batch", sorted(TINY_BATCHED))
+@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag"])
+def test_tiny_batched_decode_matches_oracle(tiny_setup, batch, mode):
+    wl = TINY_BATCHED[batch]
+    w, gw, model = tiny_setup
+    res = run_decode(wl, wl.steps, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                     sync_mode=MODES[mode][1])
+    print(f"tiny b={batch} {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}")
+    assert res.max_rel_err <= 1e-3
+    assert res.near_ties == 0
+    check_kv(res)
+
+
+def test_tiny_batched_split_attention(tiny_setup):
+    wl = TINY_BATCHED[16]
+    w, gw, model = tiny_setup
+    res = run_decode(wl, 3, weights=w, gpu_weights=gw, model=model, exec_mode=mk.MK_EXEC_FLAT, kv_splits=4)
+    assert res.max_rel_err <= 1e-3
+    check_kv(res)
+
+
+def test_llama1b_batch16_first_passes(llama1b):
+    # the batched configuration as the benchmark runs it: 16 sequences with
+    # context lengths 512..4096, FLAT engine, projections on MFMA
+    wl = si.WORKLOADS["llama1b_b16"]
+    w, gw, model = llama1b
+    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model, exec_mode=mk.MK_EXEC_FLAT)
+    print(f"llama1b b16: errs max {res.max_rel_err:.2e} near ties {res.near_ties} tokens {res.tokens}")
+    assert res.max_rel_err <= 1e-3
+    print(f"kv exact fraction {check_kv(res, min_exact=0.97):.5f}")
+
+
 @pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter"])
 def test_invalid_token_reports_input_error_and_poisons(tiny_setup, mode):
     w, gw, model = tiny_setup
