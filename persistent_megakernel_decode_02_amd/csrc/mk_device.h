@@ -81,6 +81,14 @@ MKD int mk_tid() {
   return t;
 }
 
+// Workgroup barrier that waits for LDS traffic only (a __syncthreads would
+// also wait for every global load in flight, draining the weight prefetch).
+MKD void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // wait until this wave's outstanding memory operations (stores included) completed
 MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -141,16 +149,26 @@ MKD mk_f32x4v mfma16x16x32(mk_bf16x8 a, mk_bf16x8 b, mk_f32x4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 MKD mk_bf16x8 as_bf16x8(mk_u32x4 w) { return __builtin_bit_cast(mk_bf16x8, w); }
+// Two fp32 values to a packed bf16 pair, round to nearest even
+// (v_cvt_pk_bf16_f32); a in the low half.  Same bits as f2bf for every
+// non-NaN input.
+typedef __bf16 mk_bf16x2 __attribute__((ext_vector_type(2)));
+MKD uint32_t pk_bf16(float a, float b) {
+  const mk_bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// bf16 high and low parts of two fp32 values: hi = bf16(x), lo = bf16(x - hi)
+MKD void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
 // bf16 high / low parts of 8 fp32 values, packed two per word
 MKD void split_hi_lo(const float (&x)[8], mk_u32x4 &hi, mk_u32x4 &lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f2bf(x[e]);
-    l[e] = f2bf(x[e] - __uint_as_float(h[e] << 16));
-  }
-  hi = mk_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  lo = mk_u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], h[e], l[e]);
+  hi = mk_u32x4{h[0], h[1], h[2], h[3]};
+  lo = mk_u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // Key/value rows are written to LDS with their 16-byte chunks permuted
@@ -194,7 +212,8 @@ MKD void mk_raise(const PT &P, int code, int detail) {
 template <class PT>
 MKD bool mk_aborted(const PT &P) { return __builtin_amdgcn_readfirstlane(ldci(P.err + 2)) != 0; }
 
-// Wait for event `ev` of this step.  Counter mode: one lane polls the
+// Wait for event `ev` of this step (global loads issued before the wait stay
+// in flight: the workgroup barriers wait for LDS traffic only).  Counter mode: one lane polls the
 // monotonic counter until it reaches (epoch+1) * triggers.  Flag mode: one
 // wave polls all trigger flags of the event (each holds the epoch+1 of the
 // last step its producer finished).  Bounded by the watchdog; returns false
@@ -246,9 +265,9 @@ MKD bool mk_wait(const MkProgram &P, const MkStep &S, int ev, int *s_flag) {
     }
     if (lane == 0) *s_flag = ok;
   }
-  __syncthreads();
+  lds_barrier();
   const int ok = *s_flag;
-  __syncthreads();
+  lds_barrier();
   return ok != 0;
 }
 

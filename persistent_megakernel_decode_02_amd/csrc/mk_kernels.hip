@@ -6,9 +6,10 @@
 // and 5): one workgroup per CU walks its static instruction list; before an
 // instruction it waits for the instruction's input event, dispatches on the
 // (workgroup-uniform) opcode, and triggers the output event when done.
-// The multi-launch build runs one kernel per dependency level instead, so
-// kernel boundaries replace the events (the contrast the executive-summary
-// page draws between a sequence of kernels and one persistent launch).
+// The multi-launch build runs the role-specialised ops one kernel per
+// dependency level instead, so kernel boundaries replace the events (the
+// contrast the executive-summary page draws between a sequence of kernels and
+// one persistent launch).
 #include <hip/hip_runtime.h>
 
 #include "mk_launch.h"
@@ -53,9 +54,8 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
   for (int i = i0; i < i1; ++i) {
     const MkInstr in = P.instr[i];
     const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    if (in.wait_ev >= 0 && !mk_wait(P, S, in.wait_ev, &s_flag)) return;
-    const uint64_t ts = trace ? __builtin_amdgcn_s_memrealtime() : 0;
-    const int st = run_instr(P, S, in, smem, &s_flag);
+    uint64_t ts = 0;
+    const int st = run_instr(P, S, in, smem, &s_flag, trace != nullptr, ts);
     if (st == MK_ST_ABORT) return;
     if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
@@ -70,16 +70,6 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
   }
 }
 
-extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_level_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_flag;
-  const MkProgram &P = *Pp;
-  if (mk_aborted(P)) return;
-  const int idx = P.level_list[P.level_begin[S.level] + blockIdx.x];
-  const MkInstr in = P.instr[idx];
-  run_instr(P, S, in, smem, &s_flag);
-}
-
 extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -91,13 +81,6 @@ static hipError_t set_lds(const void *fn, int lds) {
 int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
   if (set_lds((const void *)mk_mega_kernel, lds) != hipSuccess) return -1;
   hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int mk_launch_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s) {
-  if (n_blocks <= 0) return 0;
-  if (set_lds((const void *)mk_level_kernel, lds) != hipSuccess) return -1;
-  hipLaunchKernelGGL(mk_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

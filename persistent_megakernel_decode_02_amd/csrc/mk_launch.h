@@ -7,7 +7,6 @@
 #include "mk_program.h"
 
 int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
-int mk_launch_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_occupancy_role(int lds, int *blocks_per_cu);

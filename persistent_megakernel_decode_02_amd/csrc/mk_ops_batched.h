@@ -79,10 +79,6 @@ MKD float bnorm_rs(const Src &src, int K, float eps) {
   return 1.0f / sqrtf(ss / (float)K + eps);
 }
 
-MKD uint64_t pack4_bf16(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return (uint64_t)(a | (b << 16)) | ((uint64_t)(c | (d << 16)) << 32);
-}
-
 // Stage columns [c0, c0 + kc) of the 16 input rows into the bf16 high and
 // low planes.  With a gain the row is RMS-normalised, x * rs * gain[k]; rs is
 // computed here when the chunk is the whole row (kc == K), else taken from
@@ -124,65 +120,50 @@ MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16
         x[2] = (x[2] * rs) * bf_lo(g1);
         x[3] = (x[3] * rs) * bf_hi(g1);
       }
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = f2bf(x[e]);
-        l[e] = f2bf(x[e] - __uint_as_float(h[e] << 16));
-      }
-      hi[c4] = pack4_bf16(h[0], h[1], h[2], h[3]);
-      lo[c4] = pack4_bf16(l[0], l[1], l[2], l[3]);
+      uint32_t h0, h1, l0, l1;
+      split2(x[0], x[1], h0, l0);
+      split2(x[2], x[3], h1, l1);
+      hi[c4] = (uint64_t)h0 | ((uint64_t)h1 << 32);
+      lo[c4] = (uint64_t)l0 | ((uint64_t)l1 << 32);
     }
 }
 
-// ------------------------------------------------------------- MFMA steps
+// ------------------------------------------------------- MFMA contraction
 //
-// Reduction steps [sa, sb) of one staged chunk (step s = chunk columns
-// 32 s .. 32 s + 31; lane quarter q = lane / 16 takes columns 32 s + 8 q .. + 7
-// of both operands).  xr: this lane's high-plane position (row lane % 16,
-// column 8 q); wp[t]: this lane's weight row of tile t at the chunk's column
-// 8 q.  PF steps of weights stay in flight per wave.
-template <int TPW, int PF>
-MKD void bsteps(const lds_char *xr, const uint16_t *const (&wp)[TPW], int sa, int sb, mk_f32x4v (&acc)[TPW]) {
-  mk_u32x4 w[PF][TPW];
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (sa + p < sb)
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wp[t] + 32 * (sa + p)));
-  for (int s = sa; s < sb; s += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int k = s + p;
-      if (k < sb) {
-        const mk_u32x4 xh = *(const lds_u32x4 *)(xr + 64 * k);
-        const mk_u32x4 xl = *(const lds_u32x4 *)(xr + MK_BPLANE + 64 * k);
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          acc[t] = mfma16x16x32(as_bf16x8(xh), as_bf16x8(w[p][t]), acc[t]);
-          acc[t] = mfma16x16x32(as_bf16x8(xl), as_bf16x8(w[p][t]), acc[t]);
-        }
-        if (k + PF < sb)
-#pragma unroll
-          for (int t = 0; t < TPW; ++t)
-            w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wp[t] + 32 * (k + PF)));
-      }
-    }
-  }
-}
+// Reduction step j of a wave covers 32 input columns: lane quarter
+// q = lane / 16 takes columns 8 q .. + 7 of both operands.  A wave's steps
+// run chunk by chunk (MK_BKC columns staged at a time; in chunk c it takes
+// steps kp pc .. (kp + 1) pc - 1 of the chunk's pc = columns / 32 / ks); its
+// weights are loaded PF steps ahead of use into registers, the first PF
+// before the instruction's dependency wait, so the weight stream overlaps
+// the wait, the input staging and the chunk barriers.
 
-// One group of tiles: wave (kp, wl) with kp = wave / nw, wl = wave % nw runs
-// tiles g0 + wl + nw t (t < TPW) over reduction part kp of ks.  Partial
-// tiles (ks > 1) are added through LDS; fin(tile, acc) then runs on all 64
-// lanes of the wave holding the tile's full sums (lane: weight row
-// 16 tile + lane % 16, sequences 4 (lane / 16) + j).
-template <int TPW, class Src, class RowPtr, class Fin>
-MKD void bgroup(lds_char *L, const Src &src, int K, int g0, int ng, int ks, bool staged, const uint16_t *gain, float eps,
-                float rs, RowPtr rowptr, Fin fin) {
-  const int lane = mk_tid() & 63, wave = mk_tid() >> 6;
-  const int n = lane & 15, q = lane >> 4;
+template <int TPW>
+struct BPf {
+  static constexpr int PF = TPW == 1 ? 8 : 16 / TPW;  // steps of weights in flight per wave
+};
+
+// One group of ng tiles starting at tile g0: wave (kp, wl), kp = wave / nw,
+// wl = wave % nw, runs tiles g0 + wl + nw t (t < TPW) over reduction part kp
+// of ks.  Partial tiles (ks > 1) are added through LDS; fin(tile, acc) then
+// runs on all 64 lanes of the wave holding the tile's full sums (lane: weight
+// row 16 tile + lane % 16, sequences 4 (lane / 16) + j).  `wait` (the
+// instruction's dependency wait) runs once the first weights are in flight
+// when `first`; false from it aborts.
+template <int TPW, class Src, class RowPtr, class Fin, class Wait>
+MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, const uint16_t *gain, float eps,
+                   RowPtr rowptr, Fin fin, Wait wait) {
+  constexpr int PF = BPf<TPW>::PF;
+  lds_char *L = (lds_char *)mk_flat_lds;
+  const int lane = mk_tid() & 63, wave = mk_tid() >> 6, n = lane & 15, q = lane >> 4;
   const int nw = MK_NWAVES / ks, kp = wave / nw, wl = wave - kp * nw;
+  const int nch = (K + MK_BKC - 1) / MK_BKC, kcl = K - (nch - 1) * MK_BKC;
+  const int per = (MK_BKC / 32) / ks, perl = (kcl / 32) / ks;  // steps per full / last chunk
+  const int J = (nch - 1) * per + perl;
+  auto col = [&](int j) {  // weight column of step j (this lane's quarter)
+    const int c = min(j / per, nch - 1), s = j - c * per;
+    return c * MK_BKC + 32 * (kp * (c == nch - 1 ? perl : per) + s) + 8 * q;
+  };
   const uint16_t *wrow[TPW];
   bool live[TPW];
 #pragma unroll
@@ -190,66 +171,84 @@ MKD void bgroup(lds_char *L, const Src &src, int K, int g0, int ng, int ks, bool
     live[t] = wl + nw * t < ng;
     wrow[t] = rowptr(16 * (g0 + (live[t] ? wl + nw * t : 0)) + n);
   }
+  const bool run = live[0];
+  mk_u32x4 w[PF][TPW];
+  if (run)
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < J)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + col(p)));
+  if (first && !wait()) return false;
+  const float rs = (gain && nch > 1) ? bnorm_rs(src, K, eps) : 1.f;
   mk_f32x4v acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t] = mk_f32x4v{0.f, 0.f, 0.f, 0.f};
-  const lds_char *xr = L + n * MK_BROW + 16 * q;
-  for (int c0 = 0; c0 < K; c0 += MK_BKC) {
-    const int kc = min(MK_BKC, K - c0);
-    if (!staged) {
-      __syncthreads();
-      bstage(L, src, K, c0, kc, gain, eps, rs);
-      __syncthreads();
-    }
-    if (live[0]) {
-      const int per = (kc >> 5) / ks;
-      const uint16_t *wp[TPW];
+  for (int c = 0; c < nch; ++c) {
+    const int last = c == nch - 1, kc = last ? kcl : MK_BKC, pc = last ? perl : per, j0 = c * per;
+    lds_barrier();
+    bstage(L, src, K, c * MK_BKC, kc, gain, eps, rs);
+    lds_barrier();
+    if (run) {
+      const lds_char *xc = L + n * MK_BROW + 16 * q + 64 * kp * pc;
+      // j0 is a multiple of PF (per is), so step j0 + s + p sits in ring slot p
+      for (int s = 0; s < pc; s += PF) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) wp[t] = wrow[t] + c0 + 8 * q;
-      bsteps<TPW, 8 / TPW>(xr, wp, kp * per, (kp + 1) * per, acc);
+        for (int p = 0; p < PF; ++p) {
+          if (s + p < pc) {
+            const mk_u32x4 xh = *(const lds_u32x4 *)(xc + 64 * (s + p));
+            const mk_u32x4 xl = *(const lds_u32x4 *)(xc + MK_BPLANE + 64 * (s + p));
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+              acc[t] = mfma16x16x32(as_bf16x8(xh), as_bf16x8(w[p][t]), acc[t]);
+              acc[t] = mfma16x16x32(as_bf16x8(xl), as_bf16x8(w[p][t]), acc[t]);
+            }
+            const int jn = j0 + s + p + PF;
+            if (jn < J)
+#pragma unroll
+              for (int t = 0; t < TPW; ++t)
+                w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + col(jn)));
+          }
+        }
+      }
     }
   }
   if (ks > 1) {
     lds_f32x4 *red = (lds_f32x4 *)(L + MK_BRED);
     if (kp > 0) red[wave * 64 + lane] = acc[0];
-    __syncthreads();
-    if (kp == 0 && live[0])
+    lds_barrier();
+    if (kp == 0 && run)
       for (int k2 = 1; k2 < ks; ++k2) acc[0] += red[(wave + k2 * nw) * 64 + lane];
-    __syncthreads();
   }
   if (kp == 0)
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
       if (live[t]) fin(g0 + wl + nw * t, acc[t]);
+  return true;
 }
 
 // Y[b][r] for the instruction's nt tiles of 16 rows (rowptr(v): weight row
 // of virtual row v in [0, 16 nt), already clamped to a valid row), inputs
 // from src (K columns, RMSNorm with `gain` when non-null).
-template <class Src, class RowPtr, class Fin>
-MKD void bgemm(const Src &src, int K, int nt, const uint16_t *gain, float eps, RowPtr rowptr, Fin fin) {
-  lds_char *L = (lds_char *)mk_flat_lds;
-  const bool one = K <= MK_BKC;
-  const float rs = (gain && !one) ? bnorm_rs(src, K, eps) : 1.f;
-  if (one) {
-    __syncthreads();
-    bstage(L, src, K, 0, K, gain, eps, rs);
-    __syncthreads();
-  }
+template <class Src, class RowPtr, class Fin, class Wait>
+MKD bool bgemm(const Src &src, int K, int nt, const uint16_t *gain, float eps, RowPtr rowptr, Fin fin, Wait wait) {
   if (nt < MK_NWAVES) {
     const int ks = nt == 1 ? 8 : nt == 2 ? 4 : nt <= 4 ? 2 : 1;
-    bgroup<1>(L, src, K, 0, nt, ks, one, gain, eps, rs, rowptr, fin);
-    return;
+    return bgemm_run<1>(src, K, 0, nt, ks, true, gain, eps, rowptr, fin, wait);
   }
   for (int g0 = 0; g0 < nt; g0 += 4 * MK_NWAVES) {
     const int ng = min(nt - g0, 4 * MK_NWAVES);
+    const bool first = g0 == 0;
+    bool ok;
     if (ng > 2 * MK_NWAVES)
-      bgroup<4>(L, src, K, g0, ng, 1, one, gain, eps, rs, rowptr, fin);
+      ok = bgemm_run<4>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else if (ng > MK_NWAVES)
-      bgroup<2>(L, src, K, g0, ng, 1, one, gain, eps, rs, rowptr, fin);
+      ok = bgemm_run<2>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else
-      bgroup<1>(L, src, K, g0, ng, 1, one, gain, eps, rs, rowptr, fin);
+      ok = bgemm_run<1>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+    if (!ok) return false;
   }
+  return true;
 }
 
 // ------------------------------------------------------------ batched ops
@@ -262,7 +261,8 @@ MKD bool tokens_ok_all(const MkProgram &P, const MkStep &S) {
   return __syncthreads_or(bad) == 0;
 }
 
-MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
+template <class Wait>
+MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, nb = S.batch, lane = mk_tid() & 63;
   const int R = (P.nq + 2 * P.nkv) * P.d, qd = P.nq * P.d, kd = P.nkv * P.d;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
@@ -285,14 +285,16 @@ MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
     if (!tokens_ok_all(P, S)) return MK_ST_ABORT;
     const int b = mk_tid() >> 5;
     const BEmbSrc src{b < nb ? P.embed + (size_t)S.tokens[b] * H : nullptr};
-    bgemm(src, H, nt, W.attn_norm, P.eps, rowptr, fin);
+    if (!bgemm(src, H, nt, W.attn_norm, P.eps, rowptr, fin, wait)) return MK_ST_ABORT;
   } else {
-    bgemm(bact(P.xout + (size_t)(l - 1) * P.B_max * H, nb, H), H, nt, W.attn_norm, P.eps, rowptr, fin);
+    if (!bgemm(bact(P.xout + (size_t)(l - 1) * P.B_max * H, nb, H), H, nt, W.attn_norm, P.eps, rowptr, fin, wait))
+      return MK_ST_ABORT;
   }
   return MK_ST_SIGNAL;
 }
 
-MKD int op_oproj_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
+template <class Wait>
+MKD int op_oproj_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, K = P.nq * P.d, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
   if (l == 0 && !tokens_ok_all(P, S)) return MK_ST_ABORT;
@@ -312,15 +314,17 @@ MKD int op_oproj_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
         }
       }
   };
-  bgemm(bact(P.attn + (size_t)l * P.B_max * K, nb, K), K, nt, nullptr, 0.f,
-        [&](int v) { return W.wo + (size_t)(r0 + min(v, nr - 1)) * K; }, fin);
+  if (!bgemm(bact(P.attn + (size_t)l * P.B_max * K, nb, K), K, nt, nullptr, 0.f,
+             [&](int v) { return W.wo + (size_t)(r0 + min(v, nr - 1)) * K; }, fin, wait))
+    return MK_ST_ABORT;
   return MK_ST_SIGNAL;
 }
 
 // gate/up: tile t holds hidden units r0 + 8 t .. + 7 as virtual rows 0..7
 // (gate) and 8..15 (up), so lane n and lane n + 8 of a row group hold the
 // gate and up sums of one unit.
-MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
+template <class Wait>
+MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nh = in.r1 - in.r0, nt = (nh + 7) >> 3;
   const MkLayerW &W = P.layers[l];
@@ -338,11 +342,13 @@ MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
       if (n < 8 && u < nh && b0 + j < nb) stc(out + (size_t)(b0 + j) * P.I + u, (g / (1.0f + expf(-g))) * up);
     }
   };
-  bgemm(bact(P.xmid + (size_t)l * P.B_max * H, nb, H), H, nt, W.mlp_norm, P.eps, rowptr, fin);
+  if (!bgemm(bact(P.xmid + (size_t)l * P.B_max * H, nb, H), H, nt, W.mlp_norm, P.eps, rowptr, fin, wait))
+    return MK_ST_ABORT;
   return MK_ST_SIGNAL;
 }
 
-MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
+template <class Wait>
+MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, K = P.I, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
   const MkLayerW &W = P.layers[l];
@@ -358,12 +364,14 @@ MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in) {
           stc(out + o, ldc(xm + o) + a[j]);
         }
   };
-  bgemm(bact(P.hbuf + (size_t)l * P.B_max * K, nb, K), K, nt, nullptr, 0.f,
-        [&](int v) { return W.wd + (size_t)(r0 + min(v, nr - 1)) * K; }, fin);
+  if (!bgemm(bact(P.hbuf + (size_t)l * P.B_max * K, nb, K), K, nt, nullptr, 0.f,
+             [&](int v) { return W.wd + (size_t)(r0 + min(v, nr - 1)) * K; }, fin, wait))
+    return MK_ST_ABORT;
   return MK_ST_SIGNAL;
 }
 
-MKD int op_lmhead_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
+template <class Wait>
+MKD int op_lmhead_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait wait) {
   const int H = P.H, V = P.V, nb = S.batch, tid = mk_tid(), lane = tid & 63, wave = tid >> 6;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
   const uint16_t *Wlm = P.tied ? P.embed : P.lm_head;
@@ -388,8 +396,9 @@ MKD int op_lmhead_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int 
           }
         }
   };
-  bgemm(bact(P.xout + (size_t)(P.L - 1) * P.B_max * H, nb, H), H, nt, P.final_norm, P.eps,
-        [&](int v) { return Wlm + (size_t)(r0 + min(v, nr - 1)) * H; }, fin);
+  if (!bgemm(bact(P.xout + (size_t)(P.L - 1) * P.B_max * H, nb, H), H, nt, P.final_norm, P.eps,
+             [&](int v) { return Wlm + (size_t)(r0 + min(v, nr - 1)) * H; }, fin, wait))
+    return MK_ST_ABORT;
   // best per sequence: over the 16 rows of a lane group, then over waves
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -700,18 +709,27 @@ MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int
 
 // ----------------------------------------------------------------- dispatch
 
-MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag) {
+// Run one instruction: wait for its input event, then the op.  The batched
+// projections start their weight stream first and wait inside.  `ts`
+// receives the time the wait ended when `timed`.
+MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, bool timed,
+                  uint64_t &ts) {
+  auto wait = [&]() -> bool {
+    const bool ok = in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, s_flag);
+    if (timed) ts = __builtin_amdgcn_s_memrealtime();
+    return ok;
+  };
   if (S.batch >= MK_MFMA_MIN_BATCH) {
     switch (in.op) {
-      case MKOP_QKV: return op_qkv_b(P, S, in);
-      case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag);
-      case MKOP_OPROJ: return op_oproj_b(P, S, in);
-      case MKOP_GATEUP: return op_gateup_b(P, S, in);
-      case MKOP_DOWN: return op_down_b(P, S, in);
-      case MKOP_LMHEAD: return op_lmhead_b(P, S, in, s_flag);
-      default: return MK_ST_ABORT;
+      case MKOP_QKV: return op_qkv_b(P, S, in, wait);
+      case MKOP_OPROJ: return op_oproj_b(P, S, in, wait);
+      case MKOP_GATEUP: return op_gateup_b(P, S, in, wait);
+      case MKOP_DOWN: return op_down_b(P, S, in, wait);
+      case MKOP_LMHEAD: return op_lmhead_b(P, S, in, s_flag, wait);
+      default: break;
     }
   }
+  if (!wait()) return MK_ST_ABORT;
   switch (in.op) {
     case MKOP_QKV: return op_qkv(P, S, in, smem);
     case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag);
