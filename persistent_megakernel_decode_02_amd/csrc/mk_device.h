@@ -196,6 +196,44 @@ MKD size_t kv_off(const PT &P, int l, int plane, int b, int g) {
   return ((((size_t)l * 2 + plane) * P.B_max + b) * P.nkv + g) * (size_t)P.max_ctx * P.d;
 }
 
+// Merge the key-range partials of one attention output element: split s2
+// stored (max, sum, unnormalised output) of head j at
+// part[(s2 G + j)(d + 2)] (scores in base 2); returns output element i of
+// head j.  Up to 8 splits' values are loaded at once (one memory round trip
+// per 8 splits), the running sums rescaled to each group's new maximum.
+MKD float merge_splits(const float *part, int NS, int G, int d, int j, int i) {
+  float mx = -INFINITY, z = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < NS; s0 += 8) {
+    float ms[8], ls[8], os[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < NS) {
+        const float *pp = part + ((size_t)(s0 + k) * G + j) * (d + 2);
+        ms[k] = ldc(pp);
+        ls[k] = ldc(pp + 1);
+        os[k] = ldc(pp + 2 + i);
+      } else {
+        ms[k] = -INFINITY;
+        ls[k] = os[k] = 0.f;
+      }
+    float gm = mx;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gm = fmaxf(gm, ms[k]);
+    if (gm == -INFINITY) continue;  // every split so far is empty
+    const float c0 = mx == -INFINITY ? 0.f : exp2_fast(mx - gm);
+    z *= c0;
+    o *= c0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float c = ms[k] == -INFINITY ? 0.f : exp2_fast(ms[k] - gm);
+      z = fmaf(ls[k], c, z);
+      o = fmaf(os[k], c, o);
+    }
+    mx = gm;
+  }
+  return o / z;
+}
+
 // greedy order: larger value wins, equal values go to the smaller index
 MKD bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 

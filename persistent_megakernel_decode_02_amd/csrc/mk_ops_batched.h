@@ -552,23 +552,25 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   for (int t = 0; t < NT; ++t) o[t] = mk_f32x4v{0.f, 0.f, 0.f, 0.f};
   lds_char *vb = L + MK_FA_VB + wave * (32 * VROW);
   const int nu = (t1 - t0 + 31) >> 5;
-  FaBlock<D> cur;
-  if (wave < nu) fa_load<D>(cur, Kc, Vc, t0 + 32 * wave, t1);
-  for (int u = wave; u < nu; u += MK_NWAVES) {
+  // blocks u = wave + 8 i; DEPTH of them in flight per wave (a register ring;
+  // head_dim 128 keeps one: more would spill)
+  constexpr int DEPTH = D == 64 ? 3 : 1;
+  FaBlock<D> ring[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (wave + MK_NWAVES * i < nu) fa_load<D>(ring[i], Kc, Vc, t0 + 32 * (wave + MK_NWAVES * i), t1);
+  auto process = [&](FaBlock<D> &blk, int u) {
     const int ta = t0 + 32 * u, npos = min(32, t1 - ta);
     // the value block into this wave's LDS rows
 #pragma unroll
     for (int r = 0; r < CPL; ++r) {
       const int c = lane + 64 * r, row = c / CPR, ch = c - row * CPR;
-      *(lds_u32x4 *)(vb + row * VROW + 16 * ch) = cur.v[r];
+      *(lds_u32x4 *)(vb + row * VROW + 16 * ch) = blk.v[r];
     }
     if (ta <= p && p < ta + 32 && lane < CPR) {  // this step's value at slot p
       const int row = p - ta;
       *(lds_u32x4 *)(vb + row * VROW + 16 * lane) = *(const lds_u32x4 *)(vn + 8 * lane);
     }
-    // next block in flight during this one (head_dim 64; 128 would spill)
-    FaBlock<D> nxt;
-    if (D == 64 && u + MK_NWAVES < nu) fa_load<D>(nxt, Kc, Vc, ta + 32 * MK_NWAVES, t1);
     // scores of the two 16-position tiles
     float sc[2][4];
 #pragma unroll
@@ -576,7 +578,7 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
       mk_f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        mk_u32x4 kk = cur.k[T][s];
+        mk_u32x4 kk = blk.k[T][s];
         if (ta + 16 * T + col == p) kk = *(const lds_u32x4 *)(kn + DQ * qd + 8 * s);  // this step's key
         acc = mfma16x16x32(as_bf16x8(kk), as_bf16x8(qhi[s]), acc);
         acc = mfma16x16x32(as_bf16x8(kk), as_bf16x8(qlo[s]), acc);
@@ -584,6 +586,7 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[T][j] = 16 * T + 4 * qd + j < npos ? acc[j] : -INFINITY;
     }
+    if (u + MK_NWAVES * DEPTH < nu) fa_load<D>(blk, Kc, Vc, ta + 32 * MK_NWAVES * DEPTH, t1);
     // online softmax of head `col` (lanes col, col + 16, col + 32, col + 48 share it)
     float mb = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
@@ -626,10 +629,11 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
       o[t] = mfma16x16x32(as_bf16x8(plo), as_bf16x8(vw), o[t]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // gathers done before the rows are rewritten
-    if (D == 64)
-      cur = nxt;
-    else if (u + MK_NWAVES < nu)
-      fa_load<D>(cur, Kc, Vc, ta + 32 * MK_NWAVES, t1);
+  };
+  for (int u0 = wave; u0 < nu; u0 += MK_NWAVES * DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+      if (u0 + MK_NWAVES * i < nu) process(ring[i], u0 + MK_NWAVES * i);
   }
   // wave partials per head: max, sum, unnormalised output (base-2 scores)
   lsum += __shfl_xor(lsum, 16, 64);
@@ -688,17 +692,7 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   if (!last) return MK_ST_QUIET;
   if (tid < G * D) {
     const int j = tid / D, i = tid - j * D;
-    float mx = -INFINITY;
-    for (int s2 = 0; s2 < NS; ++s2) mx = fmaxf(mx, ldc(part + ((size_t)s2 * G + j) * (D + 2)));
-    float z = 0.f, ov = 0.f;
-    for (int s2 = 0; s2 < NS; ++s2) {
-      const float *pp = part + ((size_t)s2 * G + j) * (D + 2);
-      const float ms = ldc(pp);
-      const float w = ms == -INFINITY ? 0.f : exp2_fast(ms - mx);
-      z = fmaf(ldc(pp + 1), w, z);
-      ov = fmaf(ldc(pp + 2 + i), w, ov);
-    }
-    stc(attn_out + tid, ov / z);
+    stc(attn_out + tid, merge_splits(part, NS, G, D, j, i));
   }
   return MK_ST_SIGNAL;
 }

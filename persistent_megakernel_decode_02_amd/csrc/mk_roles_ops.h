@@ -714,17 +714,7 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
     if (old + 1u != (S.epoch + 1u) * (uint32_t)NS) return 0;
     for (int e = lane; e < G * d; e += 64) {
       const int j = e / d, i = e - j * d;
-      float mx = -INFINITY;
-      for (int s2 = 0; s2 < NS; ++s2) mx = fmaxf(mx, ldc(part + ((size_t)s2 * G + j) * (d + 2)));
-      float z = 0.f, o = 0.f;
-      for (int s2 = 0; s2 < NS; ++s2) {
-        const float *pp = part + ((size_t)s2 * G + j) * (d + 2);
-        const float ms = ldc(pp);
-        const float c = ms == -INFINITY ? 0.f : exp2_fast(ms - mx);
-        z = fmaf(ldc(pp + 1), c, z);
-        o = fmaf(ldc(pp + 2 + i), c, o);
-      }
-      stc(out + e, o / z);
+      stc(out + e, merge_splits(part, NS, G, d, j, i));
     }
     return 1;
   }
