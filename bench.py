@@ -8,7 +8,9 @@ enqueued back to back with the on-device token/position advance, inputs
 resident in HBM.  Prints one JSON line with the headline number, the HBM
 roofline of the megakernel, the CPU-oracle baseline, and extras (the
 multi-launch build of the same ops, the flag-synchronised variant, the
-grid-barrier microbenchmark and the streaming-read probe).
+homogeneous engine, batched decode of 16 sequences with context lengths
+512..4096 on the matrix cores, the grid-barrier microbenchmark and the
+streaming-read probe).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -24,11 +26,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
-def bytes_per_pass(shape, positions):
-    """Algorithmic HBM bytes of one pass: every bf16 parameter once (the
-    embedding matrix once, as the tied LM head; one embedding row otherwise
-    extra), keys/values of the cached positions read, the new position's
-    keys/values written, fp32 logits written, the token's embedding row."""
+def bytes_per_pass(shape, passes):
+    """Algorithmic HBM bytes of one pass, averaged over `passes` (each the
+    list of the batch's positions in that pass): every bf16 parameter once
+    for the whole batch (the embedding matrix once, as the tied LM head; one
+    embedding row per sequence otherwise extra); per sequence, the keys and
+    values of its cached positions read, the new position's keys/values
+    written, fp32 logits written and the token's embedding row read."""
     s = shape
     d, L, H = s.head_dim, s.n_layers, s.hidden
     params = L * (H * (s.n_q_heads + 2 * s.n_kv_heads) * d + s.n_q_heads * d * H + 3 * H * s.ffn + 2 * H) \
@@ -37,9 +41,9 @@ def bytes_per_pass(shape, positions):
         params += s.vocab * H  # separate LM head; the embedding contributes one row below
     kv_b = L * s.n_kv_heads * d * 2 * 2  # bytes per cached position (keys + values)
     total = 0.0
-    for p in positions:
-        total += 2 * params + p * kv_b + kv_b + 4 * s.vocab + 2 * H
-    return total / len(positions)
+    for ps in passes:
+        total += 2 * params + sum(p * kv_b + kv_b + 4 * s.vocab + 2 * H for p in ps)
+    return total / len(passes)
 
 
 COPY_PROBE_BYTES = 256 << 20
@@ -75,15 +79,62 @@ def stored_traffic(workload: str, mode: str):
     return round(float(kv["hbm_bytes_per_launch"]))
 
 
+def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
+    """Time k batched decode passes of workload `wl` (homogeneous engine,
+    counter synchronisation) after w_ untimed ones; returns a summary dict."""
+    import torch
+    s, B = wl.shape, wl.batch
+    pos0 = wl.positions0(0)
+    max_ctx = max(wl.max_ctx, max(pos0) + max(k, w_) + 1)
+    t0 = time.time()
+    kv = si.make_kv_cache(s, B, max_ctx, pos0, master=0).to(dev)
+    first = si.workload_tokens(wl, 0)[:B]
+    log(f"[bench] batched inputs ready in {time.time() - t0:.1f}s ({wl.name})")
+    tokens = torch.tensor(first, dtype=torch.int32, device=dev)
+    positions = torch.tensor(pos0, dtype=torch.int32, device=dev)
+    logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, exec_mode=mk.MK_EXEC_FLAT,
+                        sync_mode=mk.MK_SYNC_COUNTER, stream=stream)
+    try:
+        for _ in range(w_):
+            eng.step(tokens, positions, kv, logits, nxt, advance=True)
+        tokens.copy_(torch.tensor(first, dtype=torch.int32))
+        positions.copy_(torch.tensor(pos0, dtype=torch.int32))
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            eng.step(tokens, positions, kv, logits, nxt, advance=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rc, det = eng.device_error()
+        if rc != 0:
+            raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
+        ms = e0.elapsed_time(e1) / k
+        info = eng.info
+    finally:
+        eng.close()
+    bpp = bytes_per_pass(s, [[p + t for p in pos0] for t in range(k)])
+    log(f"[bench] batched {wl.name}: {k} passes in {ms * k:.3f} ms")
+    return {"workload": wl.name, "batch": B, "exec": "flat-counter", "passes": k,
+            "passes_per_s": round(1000.0 / ms, 2), "tokens_per_s": round(1000.0 * B / ms, 1),
+            "ms_per_pass": round(ms, 5), "bytes_per_pass": bpp,
+            "hbm_frac": round(bpp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "kv_splits": info.kv_splits,
+            "context_lengths": [min(pos0), max(pos0)]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
-    ap.add_argument("--mode", default="mega-sentinel",
+    ap.add_argument("--mode", default=None,
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter"],
-                    help="execution / synchronisation scheme of the headline number")
+                    help="execution / synchronisation scheme of the headline number (default: mega-sentinel; "
+                         "flat-counter for batches above 4, which only the homogeneous engine runs)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -111,6 +162,8 @@ def main():
     wl = si.WORKLOADS[args.workload]
     s = wl.shape
     B = wl.batch
+    if args.mode is None:
+        args.mode = "mega-sentinel" if B <= 4 else "flat-counter"
     K, W = args.steps, args.warmup
     max_ctx = max(wl.max_ctx, (wl.start_pos if wl.start_pos > 0 else 0) + K + 1)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
@@ -183,8 +236,7 @@ def main():
     log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
     ms_per = ms / K
     passes_s = 1000.0 / ms_per * 1.0
-    positions_timed = [p + t for t in range(K) for p in pos0]
-    bpp = bytes_per_pass(s, positions_timed) if B == 1 else bytes_per_pass(s, positions_timed) * 1.0
+    bpp = bytes_per_pass(s, [[p + t for p in pos0] for t in range(K)])
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
@@ -196,7 +248,7 @@ def main():
                        "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
                        "block_threads": info.block_threads}}
     if not args.no_extras:
-        for name in [m for m in modes if m != args.mode]:
+        for name in [m for m in modes if m != args.mode and (B <= 4 or m == "flat-counter")]:
             ms2, _ = timed(*modes[name], K, W)
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -204,6 +256,11 @@ def main():
         if "multi" in extras and args.mode.startswith("mega"):
             extras["bubble_us_per_pass"] = round((extras["multi"]["ms_per_pass"] - ms_per) * 1000.0, 2)
             extras["launches_per_pass_multi"] = info.n_levels
+        # batched decode on the same weights: 16 sequences with context
+        # lengths 512..4096, projections as MFMA contractions (FLAT engine)
+        bw = si.WORKLOADS["llama1b_b16"]
+        if bw.shape == s and B != bw.batch:
+            extras["batched"] = run_batched(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log)
         # grid-barrier microbenchmark
         dinfo = mk.mk_device_query(0)
         n = dinfo.num_cus
