@@ -134,26 +134,22 @@ MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16
 // q = lane / 16 takes columns 8 q .. + 7 of both operands.  A wave's steps
 // run chunk by chunk (MK_BKC columns staged at a time; in chunk c it takes
 // steps kp pc .. (kp + 1) pc - 1 of the chunk's pc = columns / 32 / ks); its
-// weights are loaded PF steps ahead of use into registers, the first PF
-// before the instruction's dependency wait, so the weight stream overlaps
-// the wait, the input staging and the chunk barriers.
-
-template <int TPW>
-struct BPf {
-  static constexpr int PF = TPW == 1 ? 8 : 16 / TPW;  // steps of weights in flight per wave
-};
+// weights are loaded PF steps ahead of use into registers (up to 16 steps,
+// 16 KiB per wave), the first PF before the instruction's dependency wait,
+// so the weight stream overlaps the wait, the input staging and the chunk
+// barriers.
 
 // One group of ng tiles starting at tile g0: wave (kp, wl), kp = wave / nw,
 // wl = wave % nw, runs tiles g0 + wl + nw t (t < TPW) over reduction part kp
-// of ks.  Partial tiles (ks > 1) are added through LDS; fin(tile, acc) then
+// of ks, with PF steps of weights in flight (PF divides a full chunk's steps
+// per wave, (MK_BKC / 32) / ks).  Partial tiles (ks > 1) are added through LDS; fin(tile, acc) then
 // runs on all 64 lanes of the wave holding the tile's full sums (lane: weight
 // row 16 tile + lane % 16, sequences 4 (lane / 16) + j).  `wait` (the
 // instruction's dependency wait) runs once the first weights are in flight
 // when `first`; false from it aborts.
-template <int TPW, class Src, class RowPtr, class Fin, class Wait>
+template <int TPW, int PF, class Src, class RowPtr, class Fin, class Wait>
 MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, const uint16_t *gain, float eps,
                    RowPtr rowptr, Fin fin, Wait wait) {
-  constexpr int PF = BPf<TPW>::PF;
   lds_char *L = (lds_char *)mk_flat_lds;
   const int lane = mk_tid() & 63, wave = mk_tid() >> 6, n = lane & 15, q = lane >> 4;
   const int nw = MK_NWAVES / ks, kp = wave / nw, wl = wave - kp * nw;
@@ -232,20 +228,20 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
 // from src (K columns, RMSNorm with `gain` when non-null).
 template <class Src, class RowPtr, class Fin, class Wait>
 MKD bool bgemm(const Src &src, int K, int nt, const uint16_t *gain, float eps, RowPtr rowptr, Fin fin, Wait wait) {
-  if (nt < MK_NWAVES) {
-    const int ks = nt == 1 ? 8 : nt == 2 ? 4 : nt <= 4 ? 2 : 1;
-    return bgemm_run<1>(src, K, 0, nt, ks, true, gain, eps, rowptr, fin, wait);
-  }
+  // up to 16 steps (64 registers) of weights in flight per wave
+  if (nt == 1) return bgemm_run<1, 8>(src, K, 0, nt, 8, true, gain, eps, rowptr, fin, wait);
+  if (nt == 2) return bgemm_run<1, 16>(src, K, 0, nt, 4, true, gain, eps, rowptr, fin, wait);
+  if (nt < MK_NWAVES) return bgemm_run<1, 16>(src, K, 0, nt, nt <= 4 ? 2 : 1, true, gain, eps, rowptr, fin, wait);
   for (int g0 = 0; g0 < nt; g0 += 4 * MK_NWAVES) {
     const int ng = min(nt - g0, 4 * MK_NWAVES);
     const bool first = g0 == 0;
     bool ok;
     if (ng > 2 * MK_NWAVES)
-      ok = bgemm_run<4>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<4, 4>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else if (ng > MK_NWAVES)
-      ok = bgemm_run<2>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<2, 8>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else
-      ok = bgemm_run<1>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<1, 8>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     if (!ok) return false;
   }
   return true;
