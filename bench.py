@@ -81,7 +81,7 @@ def stored_traffic(workload: str, mode: str):
 
 def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
     """Time k batched decode passes of workload `wl` (homogeneous engine,
-    counter synchronisation) after w_ untimed ones; returns a summary dict."""
+    flag synchronisation) after w_ untimed ones; returns a summary dict."""
     import torch
     s, B = wl.shape, wl.batch
     pos0 = wl.positions0(0)
@@ -95,7 +95,7 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
     logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, exec_mode=mk.MK_EXEC_FLAT,
-                        sync_mode=mk.MK_SYNC_COUNTER, stream=stream)
+                        sync_mode=mk.MK_SYNC_FLAG, stream=stream)
     try:
         for _ in range(w_):
             eng.step(tokens, positions, kv, logits, nxt, advance=True)
@@ -118,7 +118,7 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
         eng.close()
     bpp = bytes_per_pass(s, [[p + t for p in pos0] for t in range(k)])
     log(f"[bench] batched {wl.name}: {k} passes in {ms * k:.3f} ms")
-    return {"workload": wl.name, "batch": B, "exec": "flat-counter", "passes": k,
+    return {"workload": wl.name, "batch": B, "exec": "flat-flag", "passes": k,
             "passes_per_s": round(1000.0 / ms, 2), "tokens_per_s": round(1000.0 * B / ms, 1),
             "ms_per_pass": round(ms, 5), "bytes_per_pass": bpp,
             "hbm_frac": round(bpp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "kv_splits": info.kv_splits,
@@ -132,9 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
-                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter"],
+                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag"],
                     help="execution / synchronisation scheme of the headline number (default: mega-sentinel; "
-                         "flat-counter for batches above 4, which only the homogeneous engine runs)")
+                         "flat-flag for batches above 4, which only the homogeneous engine runs)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -163,7 +163,7 @@ def main():
     s = wl.shape
     B = wl.batch
     if args.mode is None:
-        args.mode = "mega-sentinel" if B <= 4 else "flat-counter"
+        args.mode = "mega-sentinel" if B <= 4 else "flat-flag"
     K, W = args.steps, args.warmup
     max_ctx = max(wl.max_ctx, (wl.start_pos if wl.start_pos > 0 else 0) + K + 1)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
@@ -231,7 +231,7 @@ def main():
     modes = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
              "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL),
              "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
-             "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER)}
+             "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG)}
     ms, info = timed(*modes[args.mode], K, W)
     log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
     ms_per = ms / K
@@ -240,7 +240,7 @@ def main():
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
-            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel"}.get(
+            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel", "flat-flag": "mk_mega_kernel"}.get(
                 args.mode, "mk_role_mega_kernel"),
             "bytes_per_launch": bpp if args.mode != "multi" else None}
 
@@ -248,7 +248,7 @@ def main():
                        "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
                        "block_threads": info.block_threads}}
     if not args.no_extras:
-        for name in [m for m in modes if m != args.mode and (B <= 4 or m == "flat-counter")]:
+        for name in [m for m in modes if m != args.mode and (B <= 4 or m.startswith("flat"))]:
             ms2, _ = timed(*modes[name], K, W)
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

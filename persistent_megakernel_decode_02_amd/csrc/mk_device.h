@@ -89,6 +89,23 @@ MKD void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// read-only program data (instruction lists, pointer tables) through the
+// constant address space: scalar loads, counted by lgkmcnt, never by vmcnt
+template <class T>
+MKD T cld(const T *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  T v;
+  const __attribute__((address_space(4))) uint32_t *src = (const __attribute__((address_space(4))) uint32_t *)p;
+  uint32_t *dst = reinterpret_cast<uint32_t *>(&v);
+  static_assert(sizeof(T) % 4 == 0, "word-sized records");
+#pragma unroll
+  for (unsigned i = 0; i < sizeof(T) / 4; ++i) dst[i] = src[i];
+  return v;
+#else
+  return *p;
+#endif
+}
+
 // wait until this wave's outstanding memory operations (stores included) completed
 MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -49,10 +49,10 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
   const MkProgram &P = *Pp;
   if (mk_aborted(P)) return;
   const int cu = blockIdx.x;
-  const int i0 = P.cu_begin[cu], i1 = P.cu_begin[cu + 1];
+  const int i0 = cld(&P.cu_begin[cu]), i1 = cld(&P.cu_begin[cu + 1]);  // scalar: the list walk stays uniform
   uint64_t *const trace = P.trace;
   for (int i = i0; i < i1; ++i) {
-    const MkInstr in = P.instr[i];
+    const MkInstr in = cld(&P.instr[i]);  // scalar loads: every field stays wave-uniform
     const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
     uint64_t ts = 0;
     const int st = run_instr(P, S, in, smem, &s_flag, trace != nullptr, ts);

@@ -86,7 +86,7 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
   const int H = P.H, l = in.layer;
   const int R = (P.nq + 2 * P.nkv) * P.d;
   float *xs = smem, *red = smem + H;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {
@@ -120,7 +120,7 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
 MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
   const int H = P.H, l = in.layer, K = P.nq * P.d;
   float *xs = smem;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {
@@ -150,7 +150,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
 MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
   const int H = P.H, l = in.layer;
   float *xs = smem, *red = smem + H;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   for (int b = 0; b < S.batch; ++b) {
     const float *x = P.xmid + ((size_t)l * P.B_max + b) * H;
     for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
@@ -178,7 +178,7 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
 MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
   const int H = P.H, l = in.layer, K = P.I;
   float *xs = smem;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   for (int b = 0; b < S.batch; ++b) {
     const float *h = P.hbuf + ((size_t)l * P.B_max + b) * K;
     for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(h + i);

@@ -262,7 +262,7 @@ MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wa
   const int H = P.H, l = in.layer, nb = S.batch, lane = mk_tid() & 63;
   const int R = (P.nq + 2 * P.nkv) * P.d, qd = P.nq * P.d, kd = P.nkv * P.d;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   auto rowptr = [&](int v) -> const uint16_t * {
     const int row = r0 + min(v, nr - 1);
     if (row < qd) return W.wq + (size_t)row * H;
@@ -294,7 +294,7 @@ MKD int op_oproj_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait 
   const int H = P.H, l = in.layer, K = P.nq * P.d, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
   if (l == 0 && !tokens_ok_all(P, S)) return MK_ST_ABORT;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   float *out = P.xmid + (size_t)l * P.B_max * H;
   auto fin = [&](int tile, mk_f32x4v a) {
     const int v = 16 * tile + (lane & 15), b0 = 4 * (lane >> 4);
@@ -323,7 +323,7 @@ template <class Wait>
 MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nh = in.r1 - in.r0, nt = (nh + 7) >> 3;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   auto rowptr = [&](int v) -> const uint16_t * {
     const int u = r0 + min(8 * (v >> 4) + (v & 7), nh - 1);
     return ((v & 8) ? W.wu : W.wg) + (size_t)u * H;
@@ -347,7 +347,7 @@ template <class Wait>
 MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
   const int H = P.H, l = in.layer, K = P.I, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
-  const MkLayerW &W = P.layers[l];
+  const MkLayerW W = cld(&P.layers[l]);
   const float *xm = P.xmid + (size_t)l * P.B_max * H;
   float *out = P.xout + (size_t)l * P.B_max * H;
   auto fin = [&](int tile, mk_f32x4v a) {

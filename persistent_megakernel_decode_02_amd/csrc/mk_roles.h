@@ -92,23 +92,6 @@ MKD uint32_t lds_ld(lds_u32 *p) {
 MKD void lds_st(lds_u32 *p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
 MKD void lds_add(lds_u32 *p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
 
-// read-only program data (instruction lists, pointer tables) through the
-// constant address space: scalar loads, counted by lgkmcnt, never by vmcnt
-template <class T>
-MKD T cld(const T *p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  T v;
-  const __attribute__((address_space(4))) uint32_t *src = (const __attribute__((address_space(4))) uint32_t *)p;
-  uint32_t *dst = reinterpret_cast<uint32_t *>(&v);
-  static_assert(sizeof(T) % 4 == 0, "word-sized records");
-#pragma unroll
-  for (unsigned i = 0; i < sizeof(T) / 4; ++i) dst[i] = src[i];
-  return v;
-#else
-  return *p;
-#endif
-}
-
 // Spin (one wave, uniform) until *p >= v.  false: the kernel is aborting.
 // Long waits (`nap`) sleep 4 x 64 clocks per poll so the spinning wave
 // leaves issue slots to the waves doing work.
