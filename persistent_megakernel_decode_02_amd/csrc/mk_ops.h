@@ -11,47 +11,119 @@
 // -------------------------------------------------------------- GEMV core
 //
 // Dot products of `nrows` weight rows (bf16, K columns, rowptr(r) gives row
-// r) with one fp32 vector xs[K] held in LDS.  Waves take NR consecutive
-// rows at a time; lanes stride over 8-element (16-byte) chunks so a wave's
-// loads of one row are contiguous 1 KiB pieces.  Weights are read once per
-// pass, so they use non-temporal loads.  fin(first_row, acc) runs on every
-// lane with the NR full sums.
-template <int NR, class RowPtr, class Fin>
-MKD void gemv_rows(int K, int nrows, const float *xs, RowPtr rowptr, Fin fin) {
-  const int lane = mk_tid() & 63, wave = mk_tid() >> 6;
+// r) with one fp32 vector xs[K] held in LDS.
+//
+// Work split.  Rows form groups of NR; a wave owns whole groups.  With fewer
+// groups than waves the waves also split the columns of each group into kp
+// parts (as long as each part keeps U iterations of 64 chunks) and add their
+// partial sums through LDS (`part`: MK_NWAVES * NR floats; callers put it 64
+// floats past the staged vector, after the norm and argmax scratch).
+//
+// Streaming.  A batch is NR rows x U iterations; lanes stride over 8-element
+// (16-byte) chunks, so one row's loads are contiguous 1 KiB pieces.  The
+// loads are buffer loads on a per-row descriptor: a chunk past the part's
+// end, a row past nrows, or a whole batch past the wave's last one falls
+// outside the descriptor's range and reads zero without touching memory, so
+// every load is issued unconditionally.  Two batches are in flight: the
+// next is issued before the current one is reduced, and the compiler's
+// wait counts stay exact because no load sits under a branch.  Weights are
+// read once per pass, so the loads are non-temporal.  pro() runs on every
+// thread once the first two batches are in flight (it may wait, stage xs
+// and synchronise the block; false aborts and is returned).  fin(first_row,
+// acc) runs on every lane of one wave with the NR full sums.
+template <int NR, int U, class RowPtr, class Pro, class Fin>
+MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr, Pro pro, Fin fin) {
+  const int lane = mk_tid() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(mk_tid() >> 6);  // wave-uniform, scalar
   const int nch = K >> 3;
+  const int ng = (nrows + NR - 1) / NR;
+  if (ng <= 0) return pro();
+  const int nit = (nch + 63) >> 6;
+  const int kp = max(1, min(ng >= MK_NWAVES ? 1 : MK_NWAVES / ng, nit / U));  // column parts
+  const int nw = min(ng, MK_NWAVES);                                          // waves per part
+  const int kpart = wave / nw, gw = wave - kpart * nw;
+  const int pit = (nit + kp - 1) / kp;  // iterations per part
+  const int c0 = kpart * pit * 64, c1 = min(nch, c0 + pit * 64);
+  const int nb = (pit + U - 1) / U;  // batches per group
+  const int T = kpart < kp ? (ng - gw + nw - 1) / nw * nb : 0;
   const float4 *x4 = reinterpret_cast<const float4 *>(xs);
-  for (int g0 = wave * NR; g0 < nrows; g0 += MK_NWAVES * NR) {
-    const mk_u32x4 *rp[NR];
+  float acc[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) rp[j] = reinterpret_cast<const mk_u32x4 *>(rowptr(min(g0 + j, nrows - 1)));
-    float acc[NR];
+  for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+
+  auto load = [&](int k, bool on, mk_u32x4 (&w)[NR][U]) {
+    const int gi = k / nb, ib = k - gi * nb;
+    const int g0 = (gw + gi * nw) * NR;
+    const int cb = c0 + ib * (U * 64) + lane;
 #pragma unroll
-    for (int j = 0; j < NR; ++j) acc[j] = 0.f;
-#pragma unroll 2
-    for (int c = lane; c < nch; c += 64) {
-      mk_u32x4 w[NR];
+    for (int j = 0; j < NR; ++j) {
+      const bool row_on = on && g0 + j < nrows;
+      const __amdgpu_buffer_rsrc_t r = mk_rsrc(rowptr(min(g0 + j, nrows - 1)), row_on ? (uint32_t)K * 2u : 0u);
 #pragma unroll
-      for (int j = 0; j < NR; ++j) w[j] = __builtin_nontemporal_load(rp[j] + c);
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + 64 * u;
+        w[j][u] = __builtin_amdgcn_raw_buffer_load_b128(r, c < c1 ? c * 16 : 0x40000000, 0, 2);
+      }
+    }
+  };
+  auto comp = [&](int k, const mk_u32x4 (&w)[NR][U]) {
+    const int gi = k / nb, ib = k - gi * nb;
+    const int cb = c0 + ib * (U * 64) + lane;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = min(cb + 64 * u, nch - 1);  // out-of-range chunks carry zero weights
       const float4 xa = x4[2 * c], xb = x4[2 * c + 1];
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         float a = acc[j];
-        a = fmaf(bf_lo(w[j].x), xa.x, a);
-        a = fmaf(bf_hi(w[j].x), xa.y, a);
-        a = fmaf(bf_lo(w[j].y), xa.z, a);
-        a = fmaf(bf_hi(w[j].y), xa.w, a);
-        a = fmaf(bf_lo(w[j].z), xb.x, a);
-        a = fmaf(bf_hi(w[j].z), xb.y, a);
-        a = fmaf(bf_lo(w[j].w), xb.z, a);
-        a = fmaf(bf_hi(w[j].w), xb.w, a);
+        a = fmaf(bf_lo(w[j][u].x), xa.x, a);
+        a = fmaf(bf_hi(w[j][u].x), xa.y, a);
+        a = fmaf(bf_lo(w[j][u].y), xa.z, a);
+        a = fmaf(bf_hi(w[j][u].y), xa.w, a);
+        a = fmaf(bf_lo(w[j][u].z), xb.x, a);
+        a = fmaf(bf_hi(w[j][u].z), xb.y, a);
+        a = fmaf(bf_lo(w[j][u].w), xb.z, a);
+        a = fmaf(bf_hi(w[j][u].w), xb.w, a);
         acc[j] = a;
       }
     }
+    if (kp == 1 && ib == nb - 1) {  // group complete
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
+      fin((gw + gi * nw) * NR, acc);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = 0.f;
+    }
+  };
+
+  // the first two batches go out before the prologue (the dependency wait
+  // and the staging of xs), so they load while the wave waits
+  mk_u32x4 wa[NR][U], wb[NR][U];
+  load(0, T > 0, wa);
+  load(min(1, max(T - 1, 0)), T > 1, wb);
+  if (!pro()) return false;
+  for (int k = 0; k < T; k += 2) {
+    comp(k, wa);
+    if (k + 1 >= T) break;
+    load(min(k + 2, T - 1), k + 2 < T, wa);
+    comp(k + 1, wb);
+    load(min(k + 3, T - 1), k + 3 < T, wb);
+  }
+  if (kp > 1) {  // one group per wave of each part: add the parts
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[j] = wave_sum(acc[j]);
-    fin(g0, acc);
+    if (lane == 0)
+#pragma unroll
+      for (int j = 0; j < NR; ++j) part[wave * NR + j] = acc[j];
+    __syncthreads();
+    if (kpart == 0)
+      for (int k2 = 1; k2 < kp; ++k2)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) acc[j] += part[(wave + k2 * nw) * NR + j];
+    __syncthreads();
+    if (kpart == 0) fin(gw * NR, acc);
   }
+  return true;
 }
 
 // In-place RMSNorm of xs[K] (LDS): x * (1 / sqrt(mean(x^2) + eps)) * gain.
@@ -82,45 +154,54 @@ MKD bool token_ok(const MkProgram &P, const MkStep &S, int b, int *tok) {
 enum { MK_ST_ABORT = -1, MK_ST_QUIET = 0, MK_ST_SIGNAL = 1 };
 
 // ---------------------------------------------------------------- QKV
-MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
+// Every op issues its first weight batches, then runs `wait` (the
+// instruction's dependency, for the first sequence only) and stages its
+// input vector; the weights load meanwhile.
+template <class Wait>
+MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer;
   const int R = (P.nq + 2 * P.nkv) * P.d;
   float *xs = smem, *red = smem + H;
   const MkLayerW W = cld(&P.layers[l]);
+  const int qd = P.nq * P.d, kd = P.nkv * P.d, r0 = in.r0, n = in.r1 - in.r0;
+  auto rowptr = [&](int r) -> const uint16_t * {
+    const int row = r0 + r;
+    if (row < qd) return W.wq + (size_t)row * H;
+    if (row < qd + kd) return W.wk + (size_t)(row - qd) * H;
+    return W.wv + (size_t)(row - qd - kd) * H;
+  };
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {
       if (mk_tid() == 0) mk_raise(P, MK_E_INPUT, b);
       return MK_ST_ABORT;
     }
-    for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = resid_in(P, S, l, b, i, tok);
-    __syncthreads();
-    rmsnorm_lds(xs, H, W.attn_norm, P.eps, red);
     float *out = P.qkv + ((size_t)l * P.B_max + b) * R + in.r0;
-    const int qd = P.nq * P.d, kd = P.nkv * P.d, r0 = in.r0;
-    auto rowptr = [&](int r) -> const uint16_t * {
-      const int row = r0 + r;
-      if (row < qd) return W.wq + (size_t)row * H;
-      if (row < qd + kd) return W.wk + (size_t)(row - qd) * H;
-      return W.wv + (size_t)(row - qd - kd) * H;
-    };
-    const int n = in.r1 - in.r0;
-    gemv_rows<4>(H, n, xs, rowptr, [&](int g0, const float *acc) {
+    const bool ok = gemv_rows<4, 4>(H, n, xs, xs + H + 64, rowptr, [&]() -> bool {
+      if (b == 0 && !wait()) return false;
+      for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = resid_in(P, S, l, b, i, tok);
+      __syncthreads();
+      rmsnorm_lds(xs, H, W.attn_norm, P.eps, red);
+      return true;
+    }, [&](int g0, const float *acc) {
       if ((mk_tid() & 63) == 0)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (g0 + j < n) stc(out + g0 + j, acc[j]);
     });
+    if (!ok) return MK_ST_ABORT;
     __syncthreads();
   }
   return MK_ST_SIGNAL;
 }
 
 // ------------------------------------------------------ O projection + add
-MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
+template <class Wait>
+MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.nq * P.d;
   float *xs = smem;
   const MkLayerW W = cld(&P.layers[l]);
+  const int r0 = in.r0, n = in.r1 - in.r0;
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {
@@ -128,70 +209,89 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
       return MK_ST_ABORT;
     }
     const float *a = P.attn + ((size_t)l * P.B_max + b) * K;
-    for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(a + i);
-    __syncthreads();
     float *out = P.xmid + ((size_t)l * P.B_max + b) * H;
-    const int r0 = in.r0, n = in.r1 - in.r0;
-    gemv_rows<4>(K, n, xs, [&](int r) { return W.wo + (size_t)(r0 + r) * K; }, [&](int g0, const float *acc) {
-      if ((mk_tid() & 63) == 0)
+    const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wo + (size_t)(r0 + r) * K; },
+                                    [&]() -> bool {
+                                      if (b == 0 && !wait()) return false;
+                                      for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(a + i);
+                                      __syncthreads();
+                                      return true;
+                                    },
+                                    [&](int g0, const float *acc) {
+                                      if ((mk_tid() & 63) == 0)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (g0 + j < n) {
-            const int row = r0 + g0 + j;
-            stc(out + row, resid_in(P, S, l, b, row, tok) + acc[j]);
-          }
-    });
+                                        for (int j = 0; j < 4; ++j)
+                                          if (g0 + j < n) {
+                                            const int row = r0 + g0 + j;
+                                            stc(out + row, resid_in(P, S, l, b, row, tok) + acc[j]);
+                                          }
+                                    });
+    if (!ok) return MK_ST_ABORT;
     __syncthreads();
   }
   return MK_ST_SIGNAL;
 }
 
 // ------------------------------------------- gate/up + SiLU (norm prologue)
-MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
+template <class Wait>
+MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer;
   float *xs = smem, *red = smem + H;
   const MkLayerW W = cld(&P.layers[l]);
+  const int r0 = in.r0, n = 2 * (in.r1 - in.r0);
   for (int b = 0; b < S.batch; ++b) {
     const float *x = P.xmid + ((size_t)l * P.B_max + b) * H;
-    for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
-    __syncthreads();
-    rmsnorm_lds(xs, H, W.mlp_norm, P.eps, red);
     float *out = P.hbuf + ((size_t)l * P.B_max + b) * P.I;
-    const int r0 = in.r0, n = 2 * (in.r1 - in.r0);
     // virtual rows: 2j = gate row r0+j, 2j+1 = up row r0+j
-    gemv_rows<4>(H, n, xs, [&](int v) { return ((v & 1) ? W.wu : W.wg) + (size_t)(r0 + (v >> 1)) * H; },
-                 [&](int g0, const float *acc) {
-                   if ((mk_tid() & 63) == 0)
+    const bool ok = gemv_rows<4, 4>(
+        H, n, xs, xs + H + 64, [&](int v) { return ((v & 1) ? W.wu : W.wg) + (size_t)(r0 + (v >> 1)) * H; },
+        [&]() -> bool {
+          if (b == 0 && !wait()) return false;
+          for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
+          __syncthreads();
+          rmsnorm_lds(xs, H, W.mlp_norm, P.eps, red);
+          return true;
+        },
+        [&](int g0, const float *acc) {
+          if ((mk_tid() & 63) == 0)
 #pragma unroll
-                     for (int j = 0; j < 4; j += 2)
-                       if (g0 + j < n) {
-                         const float a = acc[j], u = acc[j + 1];
-                         stc(out + r0 + ((g0 + j) >> 1), (a / (1.0f + expf(-a))) * u);
-                       }
-                 });
+            for (int j = 0; j < 4; j += 2)
+              if (g0 + j < n) {
+                const float a = acc[j], u = acc[j + 1];
+                stc(out + r0 + ((g0 + j) >> 1), (a / (1.0f + expf(-a))) * u);
+              }
+        });
+    if (!ok) return MK_ST_ABORT;
     __syncthreads();
   }
   return MK_ST_SIGNAL;
 }
 
 // ------------------------------------------------ down projection + add
-MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem) {
+template <class Wait>
+MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.I;
   float *xs = smem;
   const MkLayerW W = cld(&P.layers[l]);
+  const int r0 = in.r0, n = in.r1 - in.r0;
   for (int b = 0; b < S.batch; ++b) {
     const float *h = P.hbuf + ((size_t)l * P.B_max + b) * K;
-    for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(h + i);
-    __syncthreads();
     const float *xm = P.xmid + ((size_t)l * P.B_max + b) * H;
     float *out = P.xout + ((size_t)l * P.B_max + b) * H;
-    const int r0 = in.r0, n = in.r1 - in.r0;
-    gemv_rows<4>(K, n, xs, [&](int r) { return W.wd + (size_t)(r0 + r) * K; }, [&](int g0, const float *acc) {
-      if ((mk_tid() & 63) == 0)
+    const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wd + (size_t)(r0 + r) * K; },
+                                    [&]() -> bool {
+                                      if (b == 0 && !wait()) return false;
+                                      for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(h + i);
+                                      __syncthreads();
+                                      return true;
+                                    },
+                                    [&](int g0, const float *acc) {
+                                      if ((mk_tid() & 63) == 0)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (g0 + j < n) stc(out + r0 + g0 + j, ldc(xm + r0 + g0 + j) + acc[j]);
-    });
+                                        for (int j = 0; j < 4; ++j)
+                                          if (g0 + j < n) stc(out + r0 + g0 + j, ldc(xm + r0 + g0 + j) + acc[j]);
+                                    });
+    if (!ok) return MK_ST_ABORT;
     __syncthreads();
   }
   return MK_ST_SIGNAL;
@@ -246,7 +346,8 @@ MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   return MK_ST_QUIET;
 }
 
-MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag) {
+template <class Wait>
+MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, Wait &wait) {
   const int H = P.H, L = P.L, V = P.V;
   const int tid = mk_tid(), lane = tid & 63, wave = tid >> 6;
   float *xs = smem, *red = smem + H;
@@ -255,14 +356,19 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
   const uint16_t *Wlm = P.tied ? P.embed : P.lm_head;
   for (int b = 0; b < S.batch; ++b) {
     const float *x = P.xout + ((size_t)(L - 1) * P.B_max + b) * H;
-    for (int i = tid; i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
-    __syncthreads();
-    rmsnorm_lds(xs, H, P.final_norm, P.eps, red);
     float *lg = S.logits + (size_t)b * V;
     const int r0 = in.r0, n = in.r1 - in.r0;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    gemv_rows<4>(H, n, xs, [&](int r) { return Wlm + (size_t)(r0 + r) * H; }, [&](int g0, const float *acc) {
+    auto pro = [&]() -> bool {
+      if (b == 0 && !wait()) return false;
+      for (int i = tid; i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
+      __syncthreads();
+      rmsnorm_lds(xs, H, P.final_norm, P.eps, red);
+      return true;
+    };
+    const bool ok = gemv_rows<4, 4>(H, n, xs, xs + H + 64, [&](int r) { return Wlm + (size_t)(r0 + r) * H; }, pro,
+                                    [&](int g0, const float *acc) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (g0 + j < n) {
@@ -274,6 +380,7 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
           }
         }
     });
+    if (!ok) return MK_ST_ABORT;
     if (lane == 0) {
       wv[wave] = bv;
       wi[wave] = bi;

@@ -699,8 +699,9 @@ MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int
 
 // ----------------------------------------------------------------- dispatch
 
-// Run one instruction: wait for its input event, then the op.  The batched
-// projections start their weight stream first and wait inside.  `ts`
+// Run one instruction: wait for its input event, then the op.  The
+// projections (vector and batched) start their weight stream first and
+// wait inside.  `ts`
 // receives the time the wait ended when `timed`.
 MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, bool timed,
                   uint64_t &ts) {
@@ -719,14 +720,17 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
       default: break;
     }
   }
+  switch (in.op) {
+    case MKOP_QKV: return op_qkv(P, S, in, smem, wait);
+    case MKOP_OPROJ: return op_oproj(P, S, in, smem, wait);
+    case MKOP_GATEUP: return op_gateup(P, S, in, smem, wait);
+    case MKOP_DOWN: return op_down(P, S, in, smem, wait);
+    case MKOP_LMHEAD: return op_lmhead(P, S, in, smem, s_flag, wait);
+    default: break;
+  }
   if (!wait()) return MK_ST_ABORT;
   switch (in.op) {
-    case MKOP_QKV: return op_qkv(P, S, in, smem);
     case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag);
-    case MKOP_OPROJ: return op_oproj(P, S, in, smem);
-    case MKOP_GATEUP: return op_gateup(P, S, in, smem);
-    case MKOP_DOWN: return op_down(P, S, in, smem);
-    case MKOP_LMHEAD: return op_lmhead(P, S, in, smem, s_flag);
     default: return MK_ST_ABORT;
   }
 }

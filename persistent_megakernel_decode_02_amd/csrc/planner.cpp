@@ -100,7 +100,9 @@ static int lds_requirement(const mk_plan *p) {
   // vector GEMV ops stage one sequence's input vector at a time; with two or
   // more sequences the projections stage bf16 high/low planes of every
   // sequence's inputs (MK_BKC columns at a time) for the matrix cores
-  int64_t gemv = kmax * 4 + (int64_t)MK_NWAVES * 16 + 256;
+  // (the staged vector, 64 floats of norm/argmax scratch, then per-wave
+  // partial sums of 4 rows for instructions that split the columns)
+  int64_t gemv = kmax * 4 + 256 + (int64_t)MK_NWAVES * 4 * 4;
   if (B >= MK_MFMA_MIN_BATCH) gemv = std::max<int64_t>(gemv, MK_BLDS);
   // attention: queries, this step's key/value, per-wave value blocks and partials
   return (int)std::max<int64_t>(gemv, MK_FA_LDS);
