@@ -136,6 +136,7 @@ def main():
                     help="execution / synchronisation scheme of the headline number (default: mega-sentinel; "
                          "flat-flag for batches above 4, which only the homogeneous engine runs)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
+    ap.add_argument("--trace-passes", type=int, default=4, help="traced passes run back to back (the last is kept)")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one 256 MiB device copy (the scale reference for HBM byte counters)")
@@ -218,7 +219,8 @@ def main():
             if args.trace and (exec_mode, sync_mode) == modes[args.mode]:
                 tr = torch.zeros(eng.n_instr * 8 + 16, dtype=torch.int64, device=dev)
                 mk.mk_ctx_set_trace(eng.ctx, tr.data_ptr(), eng.n_instr, stream.cuda_stream)
-                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+                for _ in range(args.trace_passes):  # back to back, as in the timed loop; the last one is kept
+                    eng.step(tokens, positions, kv, logits, nxt, advance=True)
                 torch.cuda.synchronize()
                 mk.mk_ctx_set_trace(eng.ctx, None, 0, stream.cuda_stream)
                 descs = mk.mk_plan_export(eng.plan)

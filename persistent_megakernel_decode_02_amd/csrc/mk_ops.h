@@ -126,16 +126,92 @@ MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr
   return true;
 }
 
-// In-place RMSNorm of xs[K] (LDS): x * (1 / sqrt(mean(x^2) + eps)) * gain.
-MKD void rmsnorm_lds(float *xs, int K, const uint16_t *gain, float eps, float *red) {
-  float ss = 0.f;
-  for (int i = mk_tid(); i < K; i += MK_BLOCK) ss = fmaf(xs[i], xs[i], ss);
-  ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)K + eps);
-  for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = (xs[i] * r) * bf2f(gain[i]);
-  __syncthreads();
+// ------------------------------------------------------- input staging
+//
+// Inputs are staged with 16-byte device-coherent loads, all issued back to
+// back: a chunk past the end reads zero through the descriptor's range, so
+// no load sits under a branch.  n is a multiple of 4.
+#define MK_OOB 0x40000000  // byte offset past every descriptor's range
+
+MKD void stage_vec(float *xs, const float *src, int n) {
+  const int tid = mk_tid(), nc = n >> 2;
+  const __amdgpu_buffer_rsrc_t r = mk_rsrc(src, (uint32_t)n * 4u);
+  for (int c0 = 0; c0 < nc; c0 += 4 * MK_BLOCK) {
+    mk_u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + tid + k * MK_BLOCK;
+      v[k] = ldc16(r, c < nc ? c * 16 : MK_OOB);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + tid + k * MK_BLOCK;
+      if (c < nc) *reinterpret_cast<mk_u32x4 *>(xs + 4 * c) = v[k];
+    }
+  }
 }
 
+// RMSNorm gain chunks of this thread (4 bf16 per chunk, up to four chunks:
+// n <= 16 * MK_BLOCK), loaded ahead of the dependency wait.
+struct NormGain {
+  uint32_t w[4][2];
+};
+MKD void load_gain(NormGain &g, const uint16_t *gain, int n) {
+  const int tid = mk_tid(), nc = n >> 2;
+  const __amdgpu_buffer_rsrc_t r = mk_rsrc(gain, (uint32_t)n * 2u);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tid + k * MK_BLOCK;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, c < nc ? c * 8 : MK_OOB, 0, 0);
+    g.w[k][0] = v[0];
+    g.w[k][1] = v[1];
+  }
+}
+
+// Stage x[n] (fp32 from coherent memory, or the bf16 embedding row when
+// `emb` is set) into xs as x * (1 / sqrt(mean(x^2) + eps)) * gain.  The sum
+// of squares comes from the registers the loads filled; ends with a barrier.
+MKD void stage_norm(float *xs, const float *src, const uint16_t *emb, int n, const NormGain &g, float eps,
+                    float *red) {
+  const int tid = mk_tid(), nc = n >> 2;
+  float4 x[4];
+  if (emb) {
+    const __amdgpu_buffer_rsrc_t r = mk_rsrc(emb, (uint32_t)n * 2u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = tid + k * MK_BLOCK;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, c < nc ? c * 8 : MK_OOB, 0, 0);
+      x[k] = make_float4(bf_lo(v[0]), bf_hi(v[0]), bf_lo(v[1]), bf_hi(v[1]));
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t r = mk_rsrc(src, (uint32_t)n * 4u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = tid + k * MK_BLOCK;
+      const mk_u32x4 v = ldc16(r, c < nc ? c * 16 : MK_OOB);
+      x[k] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ss = fmaf(x[k].x, x[k].x, ss);
+    ss = fmaf(x[k].y, x[k].y, ss);
+    ss = fmaf(x[k].z, x[k].z, ss);
+    ss = fmaf(x[k].w, x[k].w, ss);
+  }
+  ss = block_sum(ss, red);
+  const float rn = 1.0f / sqrtf(ss / (float)n + eps);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tid + k * MK_BLOCK;
+    if (c < nc)
+      *reinterpret_cast<float4 *>(xs + 4 * c) =
+          make_float4((x[k].x * rn) * bf_lo(g.w[k][0]), (x[k].y * rn) * bf_hi(g.w[k][0]),
+                      (x[k].z * rn) * bf_lo(g.w[k][1]), (x[k].w * rn) * bf_hi(g.w[k][1]));
+  }
+  __syncthreads();
+}
 
 // Residual-stream input of layer l for sequence b, element i: the embedding
 // row of the token for layer 0, else the previous layer's output.
@@ -178,10 +254,11 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
     }
     float *out = P.qkv + ((size_t)l * P.B_max + b) * R + in.r0;
     const bool ok = gemv_rows<4, 4>(H, n, xs, xs + H + 64, rowptr, [&]() -> bool {
+      NormGain g;
+      load_gain(g, W.attn_norm, H);
       if (b == 0 && !wait()) return false;
-      for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = resid_in(P, S, l, b, i, tok);
-      __syncthreads();
-      rmsnorm_lds(xs, H, W.attn_norm, P.eps, red);
+      stage_norm(xs, l > 0 ? P.xout + ((size_t)(l - 1) * P.B_max + b) * H : nullptr,
+                 l == 0 ? P.embed + (size_t)tok * H : nullptr, H, g, P.eps, red);
       return true;
     }, [&](int g0, const float *acc) {
       if ((mk_tid() & 63) == 0)
@@ -199,7 +276,7 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
 template <class Wait>
 MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.nq * P.d;
-  float *xs = smem;
+  float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
   const MkLayerW W = cld(&P.layers[l]);
   const int r0 = in.r0, n = in.r1 - in.r0;
   for (int b = 0; b < S.batch; ++b) {
@@ -213,7 +290,8 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
     const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wo + (size_t)(r0 + r) * K; },
                                     [&]() -> bool {
                                       if (b == 0 && !wait()) return false;
-                                      for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(a + i);
+                                      for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = resid_in(P, S, l, b, r0 + i, tok);
+                                      stage_vec(xs, a, K);
                                       __syncthreads();
                                       return true;
                                     },
@@ -221,10 +299,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
                                       if ((mk_tid() & 63) == 0)
 #pragma unroll
                                         for (int j = 0; j < 4; ++j)
-                                          if (g0 + j < n) {
-                                            const int row = r0 + g0 + j;
-                                            stc(out + row, resid_in(P, S, l, b, row, tok) + acc[j]);
-                                          }
+                                          if (g0 + j < n) stc(out + r0 + g0 + j, res[g0 + j] + acc[j]);
                                     });
     if (!ok) return MK_ST_ABORT;
     __syncthreads();
@@ -246,10 +321,10 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
     const bool ok = gemv_rows<4, 4>(
         H, n, xs, xs + H + 64, [&](int v) { return ((v & 1) ? W.wu : W.wg) + (size_t)(r0 + (v >> 1)) * H; },
         [&]() -> bool {
+          NormGain g;
+          load_gain(g, W.mlp_norm, H);
           if (b == 0 && !wait()) return false;
-          for (int i = mk_tid(); i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
-          __syncthreads();
-          rmsnorm_lds(xs, H, W.mlp_norm, P.eps, red);
+          stage_norm(xs, x, nullptr, H, g, P.eps, red);
           return true;
         },
         [&](int g0, const float *acc) {
@@ -271,7 +346,7 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
 template <class Wait>
 MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.I;
-  float *xs = smem;
+  float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
   const MkLayerW W = cld(&P.layers[l]);
   const int r0 = in.r0, n = in.r1 - in.r0;
   for (int b = 0; b < S.batch; ++b) {
@@ -281,7 +356,8 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
     const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wd + (size_t)(r0 + r) * K; },
                                     [&]() -> bool {
                                       if (b == 0 && !wait()) return false;
-                                      for (int i = mk_tid(); i < K; i += MK_BLOCK) xs[i] = ldc(h + i);
+                                      for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = ldc(xm + r0 + i);
+                                      stage_vec(xs, h, K);
                                       __syncthreads();
                                       return true;
                                     },
@@ -289,7 +365,7 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
                                       if ((mk_tid() & 63) == 0)
 #pragma unroll
                                         for (int j = 0; j < 4; ++j)
-                                          if (g0 + j < n) stc(out + r0 + g0 + j, ldc(xm + r0 + g0 + j) + acc[j]);
+                                          if (g0 + j < n) stc(out + r0 + g0 + j, res[g0 + j] + acc[j]);
                                     });
     if (!ok) return MK_ST_ABORT;
     __syncthreads();
@@ -361,10 +437,10 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     auto pro = [&]() -> bool {
+      NormGain g;
+      load_gain(g, P.final_norm, H);
       if (b == 0 && !wait()) return false;
-      for (int i = tid; i < H; i += MK_BLOCK) xs[i] = ldc(x + i);
-      __syncthreads();
-      rmsnorm_lds(xs, H, P.final_norm, P.eps, red);
+      stage_norm(xs, x, nullptr, H, g, P.eps, red);
       return true;
     };
     const bool ok = gemv_rows<4, 4>(H, n, xs, xs + H + 64, [&](int r) { return Wlm + (size_t)(r0 + r) * H; }, pro,

@@ -100,9 +100,10 @@ static int lds_requirement(const mk_plan *p) {
   // vector GEMV ops stage one sequence's input vector at a time; with two or
   // more sequences the projections stage bf16 high/low planes of every
   // sequence's inputs (MK_BKC columns at a time) for the matrix cores
-  // (the staged vector, 64 floats of norm/argmax scratch, then per-wave
-  // partial sums of 4 rows for instructions that split the columns)
-  int64_t gemv = kmax * 4 + 256 + (int64_t)MK_NWAVES * 4 * 4;
+  // (the staged vector, 64 floats of norm/argmax scratch, per-wave partial
+  // sums of 4 rows for instructions that split the columns, then the
+  // residual inputs of an instruction's output rows, at most H)
+  int64_t gemv = kmax * 4 + 256 + (int64_t)MK_NWAVES * 4 * 4 + (int64_t)s.hidden * 4;
   if (B >= MK_MFMA_MIN_BATCH) gemv = std::max<int64_t>(gemv, MK_BLDS);
   // attention: queries, this step's key/value, per-wave value blocks and partials
   return (int)std::max<int64_t>(gemv, MK_FA_LDS);
@@ -400,7 +401,8 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   mk_plan_finalize_lists(p);
   if (opts->exec_mode == MK_EXEC_FLAT) {
     p->lds_bytes = lds_requirement(p);
-    if (p->lds_bytes > MK_LDS_TOTAL) {
+    // the one-sequence ops stage a normalised vector of at most 16 floats per thread
+    if (p->lds_bytes > MK_LDS_TOTAL || shape->hidden > 16 * MK_BLOCK) {
       delete p;
       return MK_ERR_UNSUPPORTED;
     }
