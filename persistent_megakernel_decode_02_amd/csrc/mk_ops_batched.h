@@ -483,8 +483,8 @@ MKD void fa_load(FaBlock<D> &f, const uint16_t *Kc, const uint16_t *Vc, int ta, 
   }
 }
 
-template <int D>
-MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
+template <int D, class Wait>
+MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait &wait) {
   constexpr int KS = D / 32, NT = D / 16, DQ = D / 4, HALF = D / 2, CPR = D / 8, CPL = D / 16;
   constexpr int VROW = 2 * D + 16;  // bytes per value row in LDS (+16: the gathers' four rows hit distinct banks)
   const int b = in.r0, g = in.r1, sp = in.split, NS = in.nsplit, l = in.layer;
@@ -503,6 +503,21 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   lds_char *L = (lds_char *)mk_flat_lds;
   lds_float *qs = (lds_float *)(L + MK_FA_Q);
   lds_u16 *kn = (lds_u16 *)(L + MK_FA_KN), *vn = (lds_u16 *)(L + MK_FA_VN);
+
+  uint16_t *Kc = S.kv + kv_off(P, l, 0, b, g);
+  uint16_t *Vc = S.kv + kv_off(P, l, 1, b, g);
+  // the cached keys and values do not depend on this step: their first blocks
+  // load while the wave waits (slot p is read stale and replaced below)
+  lds_char *vb = L + MK_FA_VB + wave * (32 * VROW);
+  const int nu = (t1 - t0 + 31) >> 5;
+  // blocks u = wave + 8 i; DEPTH of them in flight per wave (a register ring;
+  // head_dim 128 keeps one: more would spill)
+  constexpr int DEPTH = D == 64 ? 3 : 1;
+  FaBlock<D> ring[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (wave + MK_NWAVES * i < nu) fa_load<D>(ring[i], Kc, Vc, t0 + 32 * (wave + MK_NWAVES * i), t1);
+  if (!wait()) return MK_ST_ABORT;
 
   // RoPE on the group's queries (scaled) and the new key; the new value
   const float *cs = P.rope + (size_t)p * D;  // (cos, sin) pairs
@@ -525,8 +540,6 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   for (int i = tid; i < D; i += MK_BLOCK) vn[i] = f2bf(ldc(qkv + (size_t)(nq + nkv + g) * D + i));
   __syncthreads();
 
-  uint16_t *Kc = S.kv + kv_off(P, l, 0, b, g);
-  uint16_t *Vc = S.kv + kv_off(P, l, 1, b, g);
   if (t0 <= p && p < t1)
     for (int i = tid; i < D; i += MK_BLOCK) {
       Kc[(size_t)p * D + i] = kn[i];
@@ -546,15 +559,6 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   mk_f32x4v o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) o[t] = mk_f32x4v{0.f, 0.f, 0.f, 0.f};
-  lds_char *vb = L + MK_FA_VB + wave * (32 * VROW);
-  const int nu = (t1 - t0 + 31) >> 5;
-  // blocks u = wave + 8 i; DEPTH of them in flight per wave (a register ring;
-  // head_dim 128 keeps one: more would spill)
-  constexpr int DEPTH = D == 64 ? 3 : 1;
-  FaBlock<D> ring[DEPTH];
-#pragma unroll
-  for (int i = 0; i < DEPTH; ++i)
-    if (wave + MK_NWAVES * i < nu) fa_load<D>(ring[i], Kc, Vc, t0 + 32 * (wave + MK_NWAVES * i), t1);
   auto process = [&](FaBlock<D> &blk, int u) {
     const int ta = t0 + 32 * u, npos = min(32, t1 - ta);
     // the value block into this wave's LDS rows
@@ -693,15 +697,16 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   return MK_ST_SIGNAL;
 }
 
-MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
-  return P.d == 64 ? op_attn_d<64>(P, S, in, s_flag) : op_attn_d<128>(P, S, in, s_flag);
+template <class Wait>
+MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait &wait) {
+  return P.d == 64 ? op_attn_d<64>(P, S, in, s_flag, wait) : op_attn_d<128>(P, S, in, s_flag, wait);
 }
 
 // ----------------------------------------------------------------- dispatch
 
-// Run one instruction: wait for its input event, then the op.  The
-// projections (vector and batched) start their weight stream first and
-// wait inside.  `ts`
+// Run one instruction.  Every op starts the loads that do not depend on the
+// instruction's input event (weights; attention's cached keys and values),
+// then waits for the event inside.  `ts`
 // receives the time the wait ended when `timed`.
 MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, bool timed,
                   uint64_t &ts) {
@@ -726,11 +731,7 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
     case MKOP_GATEUP: return op_gateup(P, S, in, smem, wait);
     case MKOP_DOWN: return op_down(P, S, in, smem, wait);
     case MKOP_LMHEAD: return op_lmhead(P, S, in, smem, s_flag, wait);
-    default: break;
-  }
-  if (!wait()) return MK_ST_ABORT;
-  switch (in.op) {
-    case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag);
+    case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag, wait);
     default: return MK_ST_ABORT;
   }
 }
