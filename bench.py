@@ -133,8 +133,8 @@ def main():
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag"],
-                    help="execution / synchronisation scheme of the headline number (default: mega-sentinel; "
-                         "flat-flag for batches above 4, which only the homogeneous engine runs)")
+                    help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
+                         "homogeneous engine with flag events)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--trace-passes", type=int, default=4, help="traced passes run back to back (the last is kept)")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
@@ -146,7 +146,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode megakernel path "
-                                   "is single-GPU (see DESIGN.md for how it would shard)", "n_gpus": args.gpus}))
+                                   "is single-GPU (a sharded layout is designed, not built)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -164,7 +164,7 @@ def main():
     s = wl.shape
     B = wl.batch
     if args.mode is None:
-        args.mode = "mega-sentinel" if B <= 4 else "flat-flag"
+        args.mode = "flat-flag"
     K, W = args.steps, args.warmup
     max_ctx = max(wl.max_ctx, (wl.start_pos if wl.start_pos > 0 else 0) + K + 1)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
