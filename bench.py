@@ -85,7 +85,7 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
     import torch
     s, B = wl.shape, wl.batch
     pos0 = wl.positions0(0)
-    max_ctx = max(wl.max_ctx, max(pos0) + max(k, w_) + 1)
+    max_ctx = max(wl.max_ctx, max(pos0) + max(k, w_))
     t0 = time.time()
     kv = si.make_kv_cache(s, B, max_ctx, pos0, master=0).to(dev)
     first = si.workload_tokens(wl, 0)[:B]
@@ -166,7 +166,9 @@ def main():
     if args.mode is None:
         args.mode = "flat-flag"
     K, W = args.steps, args.warmup
-    max_ctx = max(wl.max_ctx, (wl.start_pos if wl.start_pos > 0 else 0) + K + 1)
+    # passes restart from the first position after the warmup (and before a
+    # trace), so the workload's own context bound holds whenever it covers them
+    max_ctx = max(wl.max_ctx, max(wl.positions0(0)) + max(K, W, args.trace_passes))
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
     t0 = time.time()
@@ -219,6 +221,8 @@ def main():
             if args.trace and (exec_mode, sync_mode) == modes[args.mode]:
                 tr = torch.zeros(eng.n_instr * 8 + 16, dtype=torch.int64, device=dev)
                 mk.mk_ctx_set_trace(eng.ctx, tr.data_ptr(), eng.n_instr, stream.cuda_stream)
+                tokens.copy_(torch.tensor(first, dtype=torch.int32))
+                positions.copy_(torch.tensor(pos0, dtype=torch.int32))
                 for _ in range(args.trace_passes):  # back to back, as in the timed loop; the last one is kept
                     eng.step(tokens, positions, kv, logits, nxt, advance=True)
                 torch.cuda.synchronize()

@@ -91,7 +91,7 @@ def llama1b():
     return w, engine.to_gpu(w), orc.Model(wl.shape, w)
 
 
-@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "flat-counter"])
+@pytest.mark.parametrize("mode", ["flat-flag", "flat-counter", "mega-counter", "mega-sentinel"])
 def test_llama1b_pos1024_first_passes(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
     w, gw, model = llama1b
@@ -103,7 +103,7 @@ def test_llama1b_pos1024_first_passes(llama1b, mode):
     check_kv(res)
 
 
-@pytest.mark.parametrize("mode", ["mega-sentinel", "flat-counter"])
+@pytest.mark.parametrize("mode", ["flat-flag", "mega-sentinel"])
 def test_llama1b_pos8192_split_attention(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos8192"]
     w, gw, model = llama1b
