@@ -43,6 +43,17 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_role_level_kernel(cons
   role_run(Pp, kernarg_step(), idx, 1);
 }
 
+// per-instruction trace record: start, end of the wait, end, cu | epoch
+__device__ __forceinline__ void trace_record(uint64_t *trace, int i, uint64_t tw, uint64_t ts, uint64_t te, int cu,
+                                             uint32_t epoch) {
+  uint64_t *r = trace + (size_t)i * 8;
+  r[0] = tw;
+  r[1] = ts;
+  r[2] = te;
+  r[3] = ((uint64_t)cu << 32) | epoch;
+  r[4] = r[5] = r[6] = r[7] = 0;
+}
+
 extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int s_flag;
@@ -55,18 +66,27 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
     const MkInstr in = cld(&P.instr[i]);  // scalar loads: every field stays wave-uniform
     const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
     uint64_t ts = 0;
+    if (S.batch < MK_MFMA_MIN_BATCH && in.op == MKOP_OPROJ && i + 1 < i1) {
+      const MkInstr nx = cld(&P.instr[i + 1]);
+      if (nx.op == MKOP_GATEUP && nx.layer == in.layer) {  // O and gate/up as one unit
+        uint64_t te_o = 0, ts_g = 0;
+        const int st = run_o_gateup(P, S, in, nx, smem, &s_flag, trace != nullptr, ts, te_o, ts_g);
+        if (st == MK_ST_ABORT) return;
+        if (st == MK_ST_SIGNAL && nx.sig_ev >= 0) mk_signal(P, S, nx.sig_ev, nx.sig_slot);
+        __syncthreads();
+        if (trace && threadIdx.x == 0) {
+          trace_record(trace, i, tw, ts, te_o, cu, S.epoch);
+          trace_record(trace, i + 1, te_o, ts_g, __builtin_amdgcn_s_memrealtime(), cu, S.epoch);
+        }
+        ++i;
+        continue;
+      }
+    }
     const int st = run_instr(P, S, in, smem, &s_flag, trace != nullptr, ts);
     if (st == MK_ST_ABORT) return;
     if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
-    if (trace && threadIdx.x == 0) {
-      uint64_t *r = trace + (size_t)i * 8;
-      r[0] = tw;
-      r[1] = ts;
-      r[2] = __builtin_amdgcn_s_memrealtime();
-      r[3] = ((uint64_t)cu << 32) | S.epoch;
-      r[4] = r[5] = r[6] = r[7] = 0;
-    }
+    if (trace && threadIdx.x == 0) trace_record(trace, i, tw, ts, __builtin_amdgcn_s_memrealtime(), cu, S.epoch);
   }
 }
 

@@ -273,7 +273,9 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
 }
 
 // ------------------------------------------------------ O projection + add
-template <class Wait>
+// U: 16-byte pieces per row and lane in one load batch (1 when the op runs
+// inside the gate/up instruction's prologue and must leave registers free)
+template <int U = 4, class Wait>
 MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.nq * P.d;
   float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
@@ -287,7 +289,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
     }
     const float *a = P.attn + ((size_t)l * P.B_max + b) * K;
     float *out = P.xmid + ((size_t)l * P.B_max + b) * H;
-    const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wo + (size_t)(r0 + r) * K; },
+    const bool ok = gemv_rows<4, U>(K, n, xs, xs + K + 64, [&](int r) { return W.wo + (size_t)(r0 + r) * K; },
                                     [&]() -> bool {
                                       if (b == 0 && !wait()) return false;
                                       for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = resid_in(P, S, l, b, r0 + i, tok);
@@ -308,8 +310,10 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
 }
 
 // ------------------------------------------- gate/up + SiLU (norm prologue)
-template <class Wait>
-MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
+// before(): runs once the first weight batches are in flight and before the
+// wait (false aborts); the paired O projection runs there.
+template <class Wait, class Before>
+MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait, Before &before) {
   const int H = P.H, l = in.layer;
   float *xs = smem, *red = smem + H;
   const MkLayerW W = cld(&P.layers[l]);
@@ -323,6 +327,7 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
         [&]() -> bool {
           NormGain g;
           load_gain(g, W.mlp_norm, H);
+          if (b == 0 && !before()) return false;
           if (b == 0 && !wait()) return false;
           stage_norm(xs, x, nullptr, H, g, P.eps, red);
           return true;

@@ -728,10 +728,43 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
   switch (in.op) {
     case MKOP_QKV: return op_qkv(P, S, in, smem, wait);
     case MKOP_OPROJ: return op_oproj(P, S, in, smem, wait);
-    case MKOP_GATEUP: return op_gateup(P, S, in, smem, wait);
+    case MKOP_GATEUP: {
+      auto none = []() -> bool { return true; };
+      return op_gateup(P, S, in, smem, wait, none);
+    }
     case MKOP_DOWN: return op_down(P, S, in, smem, wait);
     case MKOP_LMHEAD: return op_lmhead(P, S, in, smem, s_flag, wait);
     case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag, wait);
     default: return MK_ST_ABORT;
   }
+}
+
+// One sequence: a CU's O projection and the gate/up instruction that follows
+// it in its list run as one unit.  Gate/up's weights (the largest level of a
+// layer) are requested first, then the O projection waits for attention,
+// computes and signals; the weights travel meanwhile, through the attention
+// and O levels, which move little data.  Returns gate/up's status; O's
+// status is signalled here.  ts_o / te_o / ts_g: end of O's wait, end of O,
+// end of gate/up's wait (when `timed`).
+MKD int run_o_gateup(const MkProgram &P, const MkStep &S, const MkInstr &io, const MkInstr &ig, float *smem, int *s_flag,
+                     bool timed, uint64_t &ts_o, uint64_t &te_o, uint64_t &ts_g) {
+  auto wait_o = [&]() -> bool {
+    const bool ok = io.wait_ev < 0 || mk_wait(P, S, io.wait_ev, s_flag);
+    if (timed) ts_o = __builtin_amdgcn_s_memrealtime();
+    return ok;
+  };
+  auto wait_g = [&]() -> bool {
+    const bool ok = ig.wait_ev < 0 || mk_wait(P, S, ig.wait_ev, s_flag);
+    if (timed) ts_g = __builtin_amdgcn_s_memrealtime();
+    return ok;
+  };
+  auto o_first = [&]() -> bool {
+    const int st = op_oproj<1>(P, S, io, smem, wait_o);
+    if (st == MK_ST_ABORT) return false;
+    if (st == MK_ST_SIGNAL && io.sig_ev >= 0) mk_signal(P, S, io.sig_ev, io.sig_slot);
+    __syncthreads();
+    if (timed) te_o = __builtin_amdgcn_s_memrealtime();
+    return true;
+  };
+  return op_gateup(P, S, ig, smem, wait_g, o_first);
 }
