@@ -223,10 +223,16 @@ int mk_device_query(int32_t device, mk_device_info *out);
  *     maintenance,
  *   3 per-block epoch flags (plain stores, one vector poll of all flags),
  *   4 data sentinel: each block's payload word starts as a NaN pattern no
- *     arithmetic produces and the barrier waits until every payload changed.
+ *     arithmetic produces and the barrier waits until every payload changed,
+ *   5 two-level epoch flags (n_blocks >= 8): blocks b % 8 == g form group g
+ *     (one XCD under round-robin dispatch, up to a rotation); block g polls
+ *     every flag and publishes a group flag that the group's other blocks
+ *     poll.
  * d_scratch: device memory of at least mk_gridsync_scratch_bytes(n_blocks)
  * bytes; d_result: device int32[4]: [0] = number of data-visibility errors
- * seen, [1] = watchdog expiries.  Enqueued on `stream`. */
+ * seen, [1] = watchdog expiries, [2] = (variant 5) blocks whose XCD differs
+ * from b % 8 (information only: every access is device scope).  Enqueued on `stream`; MK_ERR_INVALID_ARG for an unknown
+ * variant or variant 5 with fewer than 8 blocks. */
 size_t mk_gridsync_scratch_bytes(int32_t n_blocks);
 int mk_gridsync_bench(int32_t variant, int32_t n_barriers, int32_t n_blocks, void *d_scratch,
                       int32_t *d_result, void *stream);

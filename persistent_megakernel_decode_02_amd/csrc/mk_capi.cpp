@@ -493,7 +493,7 @@ size_t mk_gridsync_scratch_bytes(int32_t n_blocks) { return n_blocks > 0 ? mk_gr
 
 int mk_gridsync_bench(int32_t variant, int32_t n_barriers, int32_t n_blocks, void *d_scratch, int32_t *d_result,
                       void *stream) {
-  if (variant < 0 || variant > 4 || n_barriers < 1 || n_blocks < 1 || !d_scratch || !d_result)
+  if (variant < 0 || variant > 5 || n_barriers < 1 || n_blocks < 1 || !d_scratch || !d_result || (variant == 5 && n_blocks < 8))
     return MK_ERR_INVALID_ARG;
   if (((uintptr_t)d_scratch & 255u) != 0) return MK_ERR_ALIGN;
   int rc = mk_launch_gridsync(variant, n_barriers, n_blocks, d_scratch, d_result, (hipStream_t)stream);

@@ -25,6 +25,7 @@ struct GsScratch {
   uint32_t *data;    // [n] value written before each barrier
   uint32_t *pay;     // [3][n] sentinel payloads (triple-buffered)
   uint32_t *abort;   // [1]
+  uint32_t *xflag;   // [8] per-group flags of the two-level barrier (one 128-byte line each)
 };
 
 static __host__ __device__ size_t gs_align(size_t v) { return (v + 255) / 256 * 256; }
@@ -41,10 +42,14 @@ static __device__ GsScratch gs_layout(void *base, int n) {
   s.pay = (uint32_t *)p;
   p += gs_align(12 * (size_t)n);
   s.abort = (uint32_t *)p;
+  p += 256;
+  s.xflag = (uint32_t *)p;
   return s;
 }
 
-size_t mk_gridsync_scratch(int n) { return 256 + 2 * gs_align(4 * (size_t)n) + gs_align(12 * (size_t)n) + 256; }
+size_t mk_gridsync_scratch(int n) {
+  return 256 + 2 * gs_align(4 * (size_t)n) + gs_align(12 * (size_t)n) + 256 + 8 * 128;
+}
 
 // bounded spin bookkeeping: returns true when the barrier must give up
 static __device__ __forceinline__ bool gs_expired(uint64_t t0, uint32_t *abort, int32_t *res) {
@@ -201,10 +206,71 @@ extern "C" __global__ void __launch_bounds__(GS_BLOCK) mk_gs_sentinel(int nb, vo
   if (threadIdx.x == 0 && errs) atomicAdd(res, errs);
 }
 
+// variant 5: two levels.  Workgroups are dispatched to the 8 XCDs in turn,
+// so group g = {blocks b : b % 8 == g} shares one XCD (up to a rotation of
+// the XCDs that depends on earlier launches).  Every block stores
+// its epoch flag; the group's leader (block g) polls all n flags, then
+// stores the group flag (its own 128-byte line), which the other members
+// poll.  Only eight blocks read the all-producer lines, and each group line
+// has n / 8 readers, so the memory side serves far fewer requests per line
+// than when every block polls every flag (variant 3).  Every access is
+// device scope: a group flag stored without write-through was not seen by
+// the members' L1-bypassing loads, so correctness does not depend on the
+// grouping.  Blocks whose XCD (hardware register XCC_ID) differs from b % 8
+// are counted in res[2] (information only).
+MKD uint32_t gs_xcc_id() { return __builtin_amdgcn_s_getreg((20) | (3 << 11)) & 15u; }
+
+extern "C" __global__ void __launch_bounds__(GS_BLOCK) mk_gs_xcd(int nb, void *scratch, int32_t *res) {
+  GsScratch s = gs_layout(scratch, gridDim.x);
+  const int blk = blockIdx.x, n = gridDim.x, lane = threadIdx.x & 63;
+  const int grp = blk & 7;
+  const bool leader = blk < 8;
+  __shared__ int ok;
+  int errs = 0;
+  if (threadIdx.x == 0 && (int)gs_xcc_id() != grp) atomicAdd(res + 2, 1);
+  for (int k = 0; k < nb; ++k) {
+    const uint32_t want = (uint32_t)k + 1u;
+    if (threadIdx.x < 64) {
+      if (lane == 0) {
+        stcu(s.data + blk, want);
+        wait_vm();
+        stcu(s.flags + blk, want);
+      }
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int good = 1;
+      uint32_t spins = 0;
+      if (leader) {
+        while (true) {
+          bool mine = true;
+          for (int j = lane; j < n; j += 64) mine = mine && ((int32_t)(ldcu(s.flags + j) - want) >= 0);
+          if (__all(mine)) break;
+          __builtin_amdgcn_s_sleep(1);
+          if ((++spins & 15u) == 0 && gs_expired(t0, s.abort, res)) { good = 0; break; }
+        }
+        if (lane == 0) stcu(s.xflag + grp * 32, want);
+      } else {
+        while (true) {
+          if ((int32_t)(ldcu(s.xflag + grp * 32) - want) >= 0) break;
+          __builtin_amdgcn_s_sleep(1);
+          if ((++spins & 15u) == 0 && gs_expired(t0, s.abort, res)) { good = 0; break; }
+        }
+      }
+      if (lane == 0) {
+        if (good && ldcu(s.data + (blk + 1) % n) < want) ++errs;
+        ok = good;
+      }
+    }
+    __syncthreads();
+    if (!ok) break;
+  }
+  if (threadIdx.x == 0 && errs) atomicAdd(res, errs);
+}
+
 extern "C" __global__ void mk_gs_init(void *scratch, int n) {
   GsScratch s = gs_layout(scratch, n);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < 3 * n; i += gridDim.x * blockDim.x) {
-    s.pay[i] = GS_SENTINEL;
+  const int m = 3 * n > 8 * 32 ? 3 * n : 8 * 32;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += gridDim.x * blockDim.x) {
+    if (i < 3 * n) s.pay[i] = GS_SENTINEL;
     if (i < n) {
       s.flags[i] = 0;
       s.data[i] = 0;
@@ -213,6 +279,7 @@ extern "C" __global__ void mk_gs_init(void *scratch, int n) {
       *s.ctr = 0;
       *s.abort = 0;
     }
+    if (i < 8 * 32) s.xflag[i] = 0;
   }
 }
 
@@ -230,6 +297,10 @@ int mk_launch_gridsync(int variant, int n_barriers, int n_blocks, void *d_scratc
     case 2: hipLaunchKernelGGL(mk_gs_counter, dim3(n_blocks), dim3(GS_BLOCK), 0, st, n_barriers, d_scratch, d_result); break;
     case 3: hipLaunchKernelGGL(mk_gs_flags, dim3(n_blocks), dim3(GS_BLOCK), 0, st, n_barriers, d_scratch, d_result); break;
     case 4: hipLaunchKernelGGL(mk_gs_sentinel, dim3(n_blocks), dim3(GS_BLOCK), 0, st, n_barriers, d_scratch, d_result); break;
+    case 5:
+      if (n_blocks < 8) return -2;
+      hipLaunchKernelGGL(mk_gs_xcd, dim3(n_blocks), dim3(GS_BLOCK), 0, st, n_barriers, d_scratch, d_result);
+      break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

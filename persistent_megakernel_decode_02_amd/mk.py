@@ -33,7 +33,7 @@ MK_ADVANCE = 1
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6
 
 GRIDSYNC_VARIANTS = {0: "cooperative_grid_sync", 1: "counter_release_acquire", 2: "counter_write_through",
-                     3: "epoch_flags", 4: "nan_sentinel_payload"}
+                     3: "epoch_flags", 4: "nan_sentinel_payload", 5: "xcd_two_level_flags"}
 
 
 class MkError(RuntimeError):

@@ -208,7 +208,7 @@ def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup, mode):
         eng.close()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_gridsync_variants_are_correct(variant):
     info = mk.mk_device_query(0)
     n = info.num_cus
@@ -226,6 +226,6 @@ def test_gridsync_variants_are_correct(variant):
     us = e0.elapsed_time(e1) * 1000.0 / nb
     r = res.cpu().tolist()
     print(f"gridsync {mk.GRIDSYNC_VARIANTS[variant]}: {us:.2f} us/barrier at {n} blocks, errors {r[0]}, "
-          f"timeouts {r[1]}")
+          f"timeouts {r[1]}, blocks off the XCD b % 8: {r[2]}")
     assert r[1] == 0
     assert r[0] == 0
