@@ -217,7 +217,16 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // rows per instruction
   int rq = d;
   while (rq > 8 && (R / (rq / 2)) <= n_cu) rq /= 2;
-  const int ro = (int)ceil_div(H, n_cu), rg = (int)ceil_div(I, n_cu), rd = (int)ceil_div(H, n_cu),
+  // O and gate/up slices: on the homogeneous engine at batch 1 the CUs that
+  // run a layer's attention get none (the least-loaded CUs take the slices,
+  // and attention CUs carry the most bytes).  They finish attention when O's
+  // input is about ready; weights they request only then queue behind the
+  // gate/up stream the other CUs started during attention, and would hold
+  // up the O and gate/up events
+  int og_cus = n_cu;
+  if (opts->exec_mode == MK_EXEC_FLAT && B == 1 && (int64_t)B * nkv * S < n_cu / 2) og_cus = n_cu - B * nkv * S;
+  const int rg = (int)((ceil_div(I, og_cus) + 3) / 4 * 4), ro = (int)ceil_div(H, og_cus);
+  const int rd = (int)ceil_div(H, n_cu),
             rl = (int)ceil_div(V, n_cu);
   p->n_lm_parts = (int)ceil_div(V, rl);
   p->n_tickets = (S > 1 ? L * B * nkv : 0) + 1;
@@ -241,15 +250,18 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   };
 
   std::vector<double> load(n_cu, 0.0);
-  auto assign = [&](std::vector<Pending> &lvl) {
+  std::vector<char> busy(n_cu, 0);  // CUs left out of a level (this layer's attention CUs)
+  auto assign = [&](std::vector<Pending> &lvl, bool skip_busy = false) {
     // spread a level evenly (each CU gets floor or ceil of n / n_cu slices);
     // the CUs with the least bytes so far take the first and largest slices
     std::stable_sort(lvl.begin(), lvl.end(), [](const Pending &a, const Pending &b) { return a.bytes > b.bytes; });
-    std::vector<int> order(n_cu);
-    for (int c = 0; c < n_cu; ++c) order[c] = c;
+    std::vector<int> order;
+    for (int c = 0; c < n_cu; ++c)
+      if (!skip_busy || !busy[c]) order.push_back(c);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return load[a] < load[b]; });
+    const size_t nc = order.size();
     for (size_t k = 0; k < lvl.size(); ++k) {
-      const int c = order[k % n_cu];
+      const int c = order[k % nc];
       p->instr.push_back(lvl[k].in);
       p->instr_cu.push_back(c);
       load[c] += lvl[k].bytes;
@@ -301,7 +313,10 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
             lvl.push_back({in, 4.0 * d * (double)ceil_div(p->max_ctx, S)});
           }
       p->ev_count[ev.attn(l)] = B * nkv;
+      const size_t first = p->instr_cu.size();
       assign(lvl);
+      std::fill(busy.begin(), busy.end(), 0);
+      for (size_t k = first; k < p->instr_cu.size(); ++k) busy[p->instr_cu[k]] = 1;
     }
     // O projection + residual
     {
@@ -317,7 +332,7 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
         lvl.push_back({in, 2.0 * (in.r1 - in.r0) * nq * d});
         wbytes += 2.0 * (in.r1 - in.r0) * nq * d;
       }
-      assign(lvl);
+      assign(lvl, og_cus < n_cu);
     }
     // gate/up + SiLU (RMSNorm prologue)
     {
@@ -333,7 +348,7 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
         lvl.push_back({in, 4.0 * (in.r1 - in.r0) * H});
         wbytes += 4.0 * (in.r1 - in.r0) * H;
       }
-      assign(lvl);
+      assign(lvl, og_cus < n_cu);
     }
     // down projection + residual
     {
