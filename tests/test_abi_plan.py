@@ -85,6 +85,41 @@ def test_plan_llama1b_one_gemv_slice_per_cu():
         mk.mk_plan_destroy(plan)
 
 
+def test_flat_plan_keeps_attention_cus_out_of_o_and_gateup():
+    """Homogeneous engine, one sequence: every layer's O and gate/up slices go
+    to CUs that run none of that layer's attention, while every row is still
+    covered exactly once and the plan validates and simulates; with 176
+    attention units (position 8192) the exclusion is off."""
+    shape, batch, max_ctx = SHAPES["llama1b_pos1024"]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256,
+                                                           exec_mode=mk.MK_EXEC_FLAT,
+                                                           sync_mode=mk.MK_SYNC_FLAG))
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        descs = mk.mk_plan_export(plan)
+        for layer in range(shape.n_layers):
+            attn = {d.cu for d in descs if d.op == mk.MK_OP_ATTN and d.layer == layer}
+            assert len(attn) == shape.n_kv_heads * 3  # 3 splits at this context bound
+            for op, rows in ((mk.MK_OP_OPROJ, shape.hidden), (mk.MK_OP_GATEUP, shape.ffn)):
+                sl = [d for d in descs if d.op == op and d.layer == layer]
+                assert not attn & {d.cu for d in sl}
+                assert len({d.cu for d in sl}) == len(sl)  # one slice per CU
+                cover = sorted((d.r0, d.r1) for d in sl)
+                assert cover[0][0] == 0 and cover[-1][1] == rows
+                assert all(a[1] == b[0] for a, b in zip(cover, cover[1:]))
+        assert mk.mk_plan_simulate(plan, 3, 11) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+    shape, batch, max_ctx = SHAPES["llama1b_pos8192"]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256,
+                                                           exec_mode=mk.MK_EXEC_FLAT))
+    try:
+        descs = mk.mk_plan_export(plan)
+        assert len({d.cu for d in descs if d.op == mk.MK_OP_OPROJ and d.layer == 0}) == 256
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
 def _tiny_plan(n_cu=8, **kw):
     shape, batch, max_ctx = SHAPES["tiny"]
     return mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=n_cu, **kw))
