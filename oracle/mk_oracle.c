@@ -198,10 +198,13 @@ int64_t orc_kv_index(const orc_shape *sh, int64_t b_max, int64_t max_ctx, int64_
 /* One decode step for `batch` sequences.  Sequence b reads token tokens[b] at
  * position positions[b], appends its keys/values to the cache at that slot of
  * every layer, attends over slots [0, positions[b]] and writes logits[b][V]
- * (double) and, if next_tokens is not NULL, the greedy next token. */
+ * (double) and, if next_tokens is not NULL, the greedy next token.
+ * kv_probe (optional, test instrumentation): receives, for every sequence and
+ * layer, the appended keys before and after the rotation and the appended
+ * values, all unrounded: double [batch][n_layers][3][n_kv_heads][head_dim]. */
 int orc_decode_step(const orc_shape *sh, const orc_weights *w, int32_t batch, const int32_t *tokens,
                     const int32_t *positions, void *kv, int32_t kv_mode, int32_t b_max, int32_t max_ctx,
-                    double *logits, int32_t *next_tokens) {
+                    double *logits, int32_t *next_tokens, double *kv_probe) {
   if (!sh || !w || !tokens || !positions || !kv || !logits) return ORC_ERR_ARG;
   const int64_t H = sh->hidden, nq = sh->n_q_heads, nkv = sh->n_kv_heads, d = sh->head_dim;
   const int64_t I = sh->ffn, V = sh->vocab, L = sh->n_layers;
@@ -239,8 +242,16 @@ int orc_decode_step(const orc_shape *sh, const orc_weights *w, int32_t batch, co
       orc_matvec(w->wq[l], nq * d, H, xn, q);
       orc_matvec(w->wk[l], nkv * d, H, xn, k);
       orc_matvec(w->wv[l], nkv * d, H, xn, v);
+      double *probe = kv_probe ? kv_probe + ((size_t)b * L + l) * 3 * nkv * d : NULL;
+      if (probe)
+        for (int64_t i = 0; i < nkv * d; ++i) {
+          probe[i] = k[i];
+          probe[2 * nkv * d + i] = v[i];
+        }
       for (int64_t h = 0; h < nq; ++h) orc_rope(q + h * d, (int)d, p, sh->rope_theta);
       for (int64_t g = 0; g < nkv; ++g) orc_rope(k + g * d, (int)d, p, sh->rope_theta);
+      if (probe)
+        for (int64_t i = 0; i < nkv * d; ++i) probe[nkv * d + i] = k[i];
       for (int64_t g = 0; g < nkv; ++g) {
         int64_t ki = orc_kv_index(sh, b_max, max_ctx, l, 0, b, g, p);
         int64_t vi = orc_kv_index(sh, b_max, max_ctx, l, 1, b, g, p);

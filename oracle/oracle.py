@@ -86,7 +86,8 @@ def lib():
                                        C.c_int64, C.c_int64, C.c_int64]
             L.orc_decode_step.restype = C.c_int
             L.orc_decode_step.argtypes = [C.POINTER(Shape), C.POINTER(Weights), C.c_int32, C.c_void_p,
-                                          C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, dp, C.c_void_p]
+                                          C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, dp, C.c_void_p,
+                                          dp]
             L.orc_num_threads.restype = C.c_int
             _lib = L
     return _lib
@@ -210,10 +211,12 @@ class Model:
                                 *[C.cast(arrs[n], _PP) for n in ("attn_norm", "wq", "wk", "wv", "wo",
                                                                   "mlp_norm", "wg", "wu", "wd")])
 
-    def step(self, tokens, positions, kv: np.ndarray, b_max: int, max_ctx: int):
+    def step(self, tokens, positions, kv: np.ndarray, b_max: int, max_ctx: int, probe: Optional[np.ndarray] = None):
         """One decode step.  kv: numpy uint16 (bf16 cache) or float64 array laid
         out [L][2][b_max][n_kv][max_ctx][d]; updated in place.  Returns
-        (logits float64 [B][V], next tokens int32 [B])."""
+        (logits float64 [B][V], next tokens int32 [B]).  probe (optional,
+        float64 [B][L][3][n_kv][d]) receives the appended keys before and
+        after the rotation and the appended values, unrounded."""
         tok = np.ascontiguousarray(tokens, dtype=np.int32)
         pos = np.ascontiguousarray(positions, dtype=np.int32)
         B = tok.size
@@ -228,7 +231,7 @@ class Model:
         nxt = np.empty(B, dtype=np.int32)
         rc = lib().orc_decode_step(C.byref(self.cshape), C.byref(self.cweights), B, tok.ctypes.data,
                                    pos.ctypes.data, kv.ctypes.data, mode, b_max, max_ctx, _dptr(logits),
-                                   nxt.ctypes.data)
+                                   nxt.ctypes.data, None if probe is None else _dptr(probe))
         if rc != 0:
             raise ValueError(f"oracle step failed with code {rc}")
         return logits, nxt

@@ -174,3 +174,24 @@ def test_step_rejects_bad_inputs():
         model.step([32], [0], kv, 1, 4)   # token out of range
     with pytest.raises(ValueError):
         model.step([1], [4], kv, 1, 4)    # position beyond the cache
+
+
+def test_step_probe_is_what_the_cache_receives():
+    # the unrounded keys/values the step reports are exactly the values it
+    # appends: rounded to bf16 they equal the cache bits at the slot, and the
+    # pre-rotation keys rotated at the position give the post-rotation ones
+    s = si.TINY
+    w = si.make_weights(s, master=3)
+    model = orc.Model(s, w)
+    max_ctx, B = 16, 2
+    kv = np.zeros(si.kv_cache_shape(s, B, max_ctx), dtype=np.uint16)
+    pos = [5, 9]
+    probe = np.empty((B, s.n_layers, 3, s.n_kv_heads, s.head_dim))
+    model.step([7, 11], pos, kv, B, max_ctx, probe=probe)
+    for b in range(B):
+        for l in range(s.n_layers):
+            for g in range(s.n_kv_heads):
+                assert np.array_equal(orc.f64_to_bf16(probe[b, l, 1, g]), kv[l, 0, b, g, pos[b]])
+                assert np.array_equal(orc.f64_to_bf16(probe[b, l, 2, g]), kv[l, 1, b, g, pos[b]])
+                np.testing.assert_allclose(orc.rope(probe[b, l, 0, g], pos[b], s.rope_theta), probe[b, l, 1, g],
+                                           rtol=0, atol=1e-15)
