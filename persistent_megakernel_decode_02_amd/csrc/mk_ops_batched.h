@@ -483,6 +483,21 @@ MKD void fa_load(FaBlock<D> &f, const uint16_t *Kc, const uint16_t *Vc, int ta, 
   }
 }
 
+// Every split of an attention unit takes a ticket once its partial is
+// stored; true (uniformly) on the last arriver of this step.
+MKD bool attn_ticket(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
+  wait_vm();
+  __syncthreads();
+  if (mk_tid() == 0) {
+    const uint32_t old = addcu(P.tickets + in.ticket, 1u);
+    *s_flag = (old + 1u == (S.epoch + 1u) * (uint32_t)in.nsplit) ? 1 : 0;
+  }
+  __syncthreads();
+  const int last = *s_flag;
+  __syncthreads();
+  return last != 0;
+}
+
 template <int D, class Wait>
 MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait &wait) {
   constexpr int KS = D / 32, NT = D / 16, DQ = D / 4, HALF = D / 2, CPR = D / 8, CPL = D / 16;
@@ -490,6 +505,9 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   const int b = in.r0, g = in.r1, sp = in.split, NS = in.nsplit, l = in.layer;
   const int G = P.G, nq = P.nq, nkv = P.nkv;
   const int tid = mk_tid(), lane = tid & 63, wave = tid >> 6, col = lane & 15, qd = lane >> 4;
+  // a sequence slot beyond this step's batch: no position, no queries, no
+  // cache access; the unit only keeps the event and ticket protocol
+  if (b >= S.batch) return NS == 1 ? MK_ST_SIGNAL : attn_ticket(P, S, in, s_flag) ? MK_ST_SIGNAL : MK_ST_QUIET;
   const int p = S.positions[b];
   if (p < 0 || p >= P.max_ctx) {
     if (tid == 0) mk_raise(P, MK_E_INPUT, 1000 + b);
@@ -564,8 +582,11 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
     // the value block into this wave's LDS rows
 #pragma unroll
     for (int r = 0; r < CPL; ++r) {
+      // rows past the block's last position repeat a cache row (possibly
+      // slot p's stale contents); they meet zero probabilities, and are
+      // zeroed so a non-finite stale value cannot reach the product
       const int c = lane + 64 * r, row = c / CPR, ch = c - row * CPR;
-      *(lds_u32x4 *)(vb + row * VROW + 16 * ch) = blk.v[r];
+      *(lds_u32x4 *)(vb + row * VROW + 16 * ch) = row < npos ? blk.v[r] : mk_u32x4{0u, 0u, 0u, 0u};
     }
     if (ta <= p && p < ta + 32 && lane < CPR) {  // this step's value at slot p
       const int row = p - ta;
@@ -680,16 +701,7 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   }
   if (NS == 1) return MK_ST_SIGNAL;
   // last arriver merges the splits
-  wait_vm();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = addcu(P.tickets + in.ticket, 1u);
-    *s_flag = (old + 1u == (S.epoch + 1u) * (uint32_t)NS) ? 1 : 0;
-  }
-  __syncthreads();
-  const int last = *s_flag;
-  __syncthreads();
-  if (!last) return MK_ST_QUIET;
+  if (!attn_ticket(P, S, in, s_flag)) return MK_ST_QUIET;
   if (tid < G * D) {
     const int j = tid / D, i = tid - j * D;
     stc(attn_out + tid, merge_splits(part, NS, G, D, j, i));

@@ -73,24 +73,7 @@ static_assert(sizeof(MkCtl) <= MK_CTL_BYTES, "LDS control block");
 
 // ------------------------------------------------------------- LDS sync
 
-// LDS flags are plain ds instructions in inline assembly, with no fences.
-// A wave's LDS operations execute in program order and LDS is shared by the
-// whole workgroup, so a flag written after a wave's data writes (or after its
-// last reads of a page) is seen only once those have taken effect.  Compiled
-// atomics with workgroup fences would instead wait for every global access
-// still in flight (global->LDS loads write LDS and are counted by vmcnt; the
-// compiler cannot prove they do not overlap the flag), which puts a full
-// memory round trip on every page a compute wave frees after storing an
-// output.  Ordering against global memory is made explicit where it matters
-// (a vmcnt wait before a wave reports results that other CUs will read).
-MKD uint32_t lds_off(const lds_u32 *p) { return (uint32_t)(size_t)p; }
-MKD uint32_t lds_ld(lds_u32 *p) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
-  return __builtin_amdgcn_readfirstlane(v);  // one address for the wave: the value is uniform
-}
-MKD void lds_st(lds_u32 *p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
-MKD void lds_add(lds_u32 *p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
+
 
 // Spin (one wave, uniform) until *p >= v.  false: the kernel is aborting.
 // Long waits (`nap`) sleep 4 x 64 clocks per poll so the spinning wave
@@ -176,10 +159,23 @@ MKD bool mk_geo(MkProgC &P, MkStepC &S, const MkCtl3 *ctl, const MkInstr &in, Mk
       break;
     case MKOP_ATTN: {
       const int b = in.r0, gg = in.r1, NS = in.nsplit;
+      g.bp = MK_PAGE / (2 * P.d);
+      g.nh = 2;
+      g.ppr = 1;
+      g.ppu = 2;
+      g.K = 0;
+      g.rb = MK_PAGE;
+      g.ustride = MK_PAGE;
+      if (b >= S.batch) {  // a sequence slot beyond this step's batch: no keys, no cache access
+        g.p = -1;
+        g.n_units = 0;
+        g.full = 1;
+        g.src0 = g.src1 = nullptr;
+        return true;
+      }
       const int p = __builtin_amdgcn_readfirstlane(ctl->pos[b]);
       if (p < 0 || p >= P.max_ctx) return false;
       const int n = p + 1;
-      g.bp = MK_PAGE / (2 * P.d);
       // splits start on page boundaries so pages never straddle two splits
       const int chunk = ((n + NS - 1) / NS + g.bp - 1) / g.bp * g.bp;
       g.p = p;
@@ -188,12 +184,6 @@ MKD bool mk_geo(MkProgC &P, MkStepC &S, const MkCtl3 *ctl, const MkInstr &in, Mk
       g.src0 = (const char *)(S.kv + kv_off(P, in.layer, 0, b, gg) + (size_t)g.t0 * P.d);
       g.src1 = (const char *)(S.kv + kv_off(P, in.layer, 1, b, gg) + (size_t)g.t0 * P.d);
       g.n_units = (g.t1 - g.t0 + g.bp - 1) / g.bp;
-      g.nh = 2;
-      g.ppr = 1;
-      g.ppu = 2;
-      g.K = 0;
-      g.rb = MK_PAGE;
-      g.ustride = MK_PAGE;
       g.full = ((g.t1 - g.t0) % g.bp) == 0;
       return true;
     }

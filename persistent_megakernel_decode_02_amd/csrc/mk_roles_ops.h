@@ -316,6 +316,7 @@ MKD bool sync_stage(const MkRole &R, const MkInstr &in, const MkGeo &g, const Mk
       return true;
     }
     case MKOP_ATTN: {
+      if (g.p < 0) return true;  // sequence slot beyond this step's batch: nothing to stage
       const int b = in.r0, gg = in.r1, d = P.d, G = P.G, half = d / 2;
       const int R0 = (P.nq + 2 * P.nkv) * d;
       const float *qkv = A.qkv + ((size_t)l * P.B_max + b) * R0;
@@ -679,6 +680,14 @@ MKD int sync_epilogue(const MkRole &R, const MkInstr &in, const MkGeo &g, const 
   MkStepC &S = R.S;
   const int lane = threadIdx.x & 63;
   const int B = S.batch, l = in.layer;
+  if (in.op == MKOP_ATTN && g.p < 0) {
+    // sequence slot beyond this step's batch: only the event and ticket protocol
+    if (in.nsplit == 1) return 1;
+    uint32_t old = 0;
+    if (lane == 0) old = addcu(P.tickets + in.ticket, 1u);
+    old = __builtin_amdgcn_readfirstlane(old);
+    return old + 1u == (S.epoch + 1u) * (uint32_t)in.nsplit ? 1 : 0;
+  }
   if (in.op == MKOP_ATTN) {
     const int b = in.r0, gg = in.r1, d = P.d, G = P.G, NS = in.nsplit;
     float *out = A.attn + ((size_t)l * P.B_max + b) * P.nq * d + (size_t)gg * G * d;
@@ -988,7 +997,7 @@ MKD MkRole make_role(MkProgC &P, MkStepC &S, uint32_t lb) {
     const uint64_t tw = P.trace ? __builtin_amdgcn_s_memrealtime() : 0;
     StagePre pre;  // ahead of the wait
     if (normed_op(in.op)) load_bf16_chunks(norm_gain(P, in), P.H, pre.gain);
-    if (in.op == MKOP_ATTN) {
+    if (in.op == MKOP_ATTN && g.p >= 0) {
       const int half = P.d / 2, i = (threadIdx.x & 63) % half;
       pre.rc = gld(P.rope + (size_t)g.p * P.d + 2 * i);
       pre.rs = gld(P.rope + (size_t)g.p * P.d + 2 * i + 1);
