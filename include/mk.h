@@ -73,11 +73,16 @@ enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step, loader /
                                sync-storer / compute wavefronts, LDS page ring */
        MK_EXEC_MULTI = 1,   /* the same role-specialised ops, one launch per
                                dependency level (kernel boundaries) */
-       MK_EXEC_FLAT = 2     /* one persistent launch with homogeneous waves: all
-                               waves load, wait and compute each instruction */ };
+       MK_EXEC_FLAT = 2,    /* one persistent launch with homogeneous waves: all
+                               waves load, wait and compute each instruction */
+       MK_EXEC_STREAM = 3   /* one persistent launch, one sequence per step:
+                               streamer waves keep projection weights in flight
+                               across instructions, one wave synchronises
+                               (MK_SYNC_COUNTER or MK_SYNC_FLAG, max_batch 1) */ };
 
 typedef struct {
-  int32_t max_batch;   /* sequences per step: 1..16 (MK_EXEC_FLAT), 1..4 otherwise */
+  int32_t max_batch;   /* sequences per step: 1..16 (MK_EXEC_FLAT), 1 (MK_EXEC_STREAM),
+                          1..4 otherwise */
   int32_t max_ctx;     /* KV slots per sequence */
   int32_t kv_splits;   /* attention splits per (sequence, kv head); 0 = auto */
   int32_t sync_mode;   /* MK_SYNC_* */
@@ -87,7 +92,7 @@ typedef struct {
   int32_t flags;       /* reserved, 0 */
 } mk_plan_opts;
 
-typedef struct mk_plan mk_plan; /* opaque, host memory, owned by the library */
+typedef struct mk_plan_s mk_plan_t; /* opaque, host memory, owned by the library */
 typedef struct mk_ctx mk_ctx;   /* opaque, host memory, owned by the library */
 
 /* Read-only description of a plan (for tests and tools). */
@@ -121,35 +126,37 @@ enum { MK_OP_QKV = 1, MK_OP_ATTN = 2, MK_OP_OPROJ = 3, MK_OP_GATEUP = 4, MK_OP_D
  * opts->num_cus == 0, which queries the current device's CU count.
  * (Megakernel page, section 2.5: the CPU builds the per-unit instruction
  * lists; section 2.6 item 5: static per-unit lists.) */
-int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan **out);
+int mk_plan(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan_t **out);
+/* The same call under its longer name (kept for existing callers). */
+int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan_t **out);
 
 /* Re-check a plan: every RAW dependency is covered by a waited event whose
  * triggers all precede it by level, no event is waited for more often than it
  * is triggered, lists are level-sorted, and the counters' targets are
  * reachable.  MK_OK or MK_ERR_PLAN. */
-int mk_plan_validate(const mk_plan *plan);
+int mk_plan_validate(const mk_plan_t *plan);
 
 /* Bytes the caller must allocate: workspace (device, 256-byte aligned), KV
  * cache (bf16 [n_layers][2][max_batch][n_kv_heads][max_ctx][head_dim]; plane
  * 0 keys, plane 1 values), logits (fp32 [max_batch][vocab]). */
-int mk_plan_sizes(const mk_plan *plan, size_t *workspace_bytes, size_t *kv_cache_bytes,
+int mk_plan_sizes(const mk_plan_t *plan, size_t *workspace_bytes, size_t *kv_cache_bytes,
                   size_t *logits_bytes, size_t *n_instructions);
-int mk_plan_get_info(const mk_plan *plan, mk_plan_info *out);
+int mk_plan_get_info(const mk_plan_t *plan, mk_plan_info *out);
 /* Copy up to `cap` instruction descriptors into `out` (host array); *n_out
  * receives the total count. */
-int mk_plan_export(const mk_plan *plan, mk_instr_desc *out, size_t cap, size_t *n_out);
+int mk_plan_export(const mk_plan_t *plan, mk_instr_desc *out, size_t cap, size_t *n_out);
 /* Run the host-side schedule simulator: execute the plan's lists under
  * `n_trials` random interleavings (seeded) with no arithmetic, checking that
  * every wait is eventually satisfied and every read follows its producers.
  * MK_OK or MK_ERR_PLAN. */
-int mk_plan_simulate(const mk_plan *plan, int32_t n_trials, uint64_t seed);
-void mk_plan_destroy(mk_plan *plan);
+int mk_plan_simulate(const mk_plan_t *plan, int32_t n_trials, uint64_t seed);
+void mk_plan_destroy(mk_plan_t *plan);
 
 /* Bind a plan to caller-owned device workspace (d_workspace, at least the
  * size mk_plan_sizes reports, 256-byte aligned).  Enqueues the upload of the
  * instruction lists and RoPE table and the zeroing of the counters on
  * `stream`.  The plan may be destroyed afterwards. */
-int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t workspace_bytes, void *stream,
+int mk_ctx_create(const mk_plan_t *plan, void *d_workspace, size_t workspace_bytes, void *stream,
                   mk_ctx **out);
 
 /* Weight tensors, all bf16 device pointers, 16-byte aligned, row-major
@@ -172,12 +179,22 @@ typedef struct {
 } mk_weights;
 
 /* Check and record the weight pointers and enqueue their upload into the
- * workspace's pointer table on `stream`. */
+ * workspace's pointer table on `stream`; synchronises `stream` before
+ * returning.  The host binds what the GPU consumes, once: the megakernel
+ * page puts the host on the preparing side (section 2.5: the CPU builds the
+ * instruction lists and hands them over) and the persistent kernel on the
+ * consuming side (section 2.1).  Errors: MK_ERR_INVALID_ARG for a NULL
+ * context, table or tensor pointer (lm_head only when untied);
+ * MK_ERR_ALIGN when a tensor is not 16-byte aligned; MK_ERR_HIP when the
+ * upload fails.  On error the context keeps its previous binding. */
 int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
 
 #define MK_ADVANCE 1u  /* after the step: tokens[b] = next token, positions[b] += 1 */
 
-/* The hot path: one decoder forward pass for `batch` sequences.
+/* The hot path: one decoder forward pass for `batch` sequences, as the
+ * megakernel page defines the object (section 2.1: one persistent launch
+ * whose workgroups stay resident and resolve dependencies in global memory;
+ * section 2.5: the GPU consumes the lists the host prepared).
  * d_tokens[b] (int32) is read at position d_positions[b] (int32); the step
  * writes keys/values of that position into d_kv_cache for every layer,
  * attends over slots [0, positions[b]], writes fp32 logits d_logits[b][vocab]
@@ -186,8 +203,17 @@ int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
  * into d_tokens and increments d_positions on the device, so steps can be
  * enqueued back to back without the host.  Enqueued on `stream`; device-side
  * input errors (token or position out of range) and watchdog expiries are
- * reported by mk_get_device_error.  MK_EXEC_MEGA: exactly one kernel launch;
- * MK_EXEC_MULTI: one launch per dependency level. */
+ * reported by mk_get_device_error.  MK_EXEC_MEGA and MK_EXEC_FLAT: exactly
+ * one kernel launch; MK_EXEC_MULTI: one launch per dependency level.
+ * Layouts: d_tokens, d_positions int32[batch] (sequence b uses sequence
+ * slot b of the cache); d_kv_cache as mk_plan_sizes describes; d_logits
+ * fp32 [batch][vocab]; d_next_tokens int32[batch].  Sequence slots
+ * batch..max_batch-1 of the cache are neither read nor written.
+ * Host-side errors (nothing is enqueued): MK_ERR_INVALID_ARG (NULL context
+ * or buffer, unknown flag, weights not bound), MK_ERR_CTX_OVERFLOW (batch
+ * outside 1..max_batch), MK_ERR_ALIGN (d_kv_cache not 16-byte aligned or an
+ * int32/fp32 buffer not 4-byte aligned), MK_ERR_STATE (context poisoned),
+ * MK_ERR_HIP (launch failed). */
 int mk_decode_step(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
                    float *d_logits, int32_t *d_next_tokens, uint32_t flags, void *stream);
 
@@ -254,13 +280,13 @@ int mk_lds_stream_read(const void *d_buf, size_t bytes, uint32_t *d_out, int32_t
  * mk_plan_export writes them; slots, tickets and partial indices are
  * re-derived).  Used by tests that corrupt a plan on purpose; the plan is
  * then accepted only if mk_plan_validate passes.  Host only. */
-int mk_plan_set_instructions(mk_plan *plan, const mk_instr_desc *descs, size_t n);
+int mk_plan_set_instructions(mk_plan_t *plan, const mk_instr_desc *descs, size_t n);
 /* Byte offsets of the activation buffers inside the workspace, for tests
  * and debugging: out[0..7] = qkv, attn, xmid, hbuf, xout, end of the
  * activation block, attention partials, parity stride (bytes; 0 unless
  * sentinel mode).  Each activation buffer is fp32 [n_layers][max_batch][n]
  * with n = (n_q + 2 n_kv) head_dim, n_q head_dim, hidden, ffn, hidden. */
-int mk_plan_get_layout(const mk_plan *plan, uint64_t out[8]);
+int mk_plan_get_layout(const mk_plan_t *plan, uint64_t out[8]);
 /* Shorten the device watchdog of a context (microseconds) so tests can turn a
  * wait that cannot be met into MK_ERR_TIMEOUT quickly.  Synchronises stream. */
 int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
@@ -271,7 +297,9 @@ int mk_ctx_set_watchdog_us(mk_ctx *ctx, uint32_t us, void *stream);
  * role-specialised kernel the CU's cumulative ticks of loader waves blocked
  * on a free page and of compute waves waiting for a landed page, the
  * instruction's page count and when its compute waves finished (before the
- * sync wave's epilogue); else 0.  n_records must cover the plan's
+ * sync wave's epilogue); for a projection of the stream engine, when its
+ * input event was seen and when every streamer had finished its rows (words
+ * 4 and 5); else 0.  n_records must cover the plan's
  * instruction count.  NULL switches tracing off.  Synchronises stream. */
 int mk_ctx_set_trace(mk_ctx *ctx, void *d_trace, size_t n_records, void *stream);
 /* Overwrite the host-side step counter of a context.  Setting it ahead of the

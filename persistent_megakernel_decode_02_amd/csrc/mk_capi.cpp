@@ -14,11 +14,12 @@
 #include "planner.h"
 
 struct mk_ctx {
-  mk_plan plan;              // private copy
+  mk_plan_t plan;              // private copy
   char *ws = nullptr;        // device workspace base
   size_t ws_bytes = 0;
   MkProgram prog{};          // host image of the device MkProgram
   std::vector<MkLayerW> layers;
+  std::vector<MkRowTab> rowtab;  // stream engine row table (host staging)
   std::vector<float> rope;   // host staging kept alive for async uploads
   bool weights = false;
   bool poisoned = false;
@@ -30,7 +31,11 @@ static inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; 
 
 // The megakernel asks for more than half of a CU's 160 KiB LDS so that the
 // dispatcher can place only one of its workgroups on each CU.
-static inline int mega_lds(const mk_plan *p) { return std::max(p->lds_bytes, 80 * 1024 + 256); }
+static inline int mega_lds(const mk_plan_t *p) { return std::max(p->lds_bytes, 80 * 1024 + 256); }
+// dynamic LDS a plan's kernel is launched with
+static inline int launch_lds(const mk_plan_t *p) {
+  return p->opts.exec_mode == MK_EXEC_FLAT || p->opts.exec_mode == MK_EXEC_STREAM ? mega_lds(p) : p->lds_bytes;
+}
 
 extern "C" {
 
@@ -52,7 +57,7 @@ const char *mk_strerror(int code) {
   }
 }
 
-int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan **out) {
+int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan_t **out) {
   if (!shape || !opts || !out) return MK_ERR_INVALID_ARG;
   int n_cu = opts->num_cus;
   if (n_cu == 0) {
@@ -63,14 +68,18 @@ int mk_plan_create(const mk_model_shape *shape, const mk_plan_opts *opts, mk_pla
   return mk_plan_build(shape, opts, n_cu, out);
 }
 
-int mk_plan_validate(const mk_plan *p) { return p ? mk_plan_check(p, false, 0, 0) : MK_ERR_INVALID_ARG; }
+int mk_plan(const mk_model_shape *shape, const mk_plan_opts *opts, mk_plan_t **out) {
+  return mk_plan_create(shape, opts, out);
+}
 
-int mk_plan_simulate(const mk_plan *p, int32_t n_trials, uint64_t seed) {
+int mk_plan_validate(const mk_plan_t *p) { return p ? mk_plan_check(p, false, 0, 0) : MK_ERR_INVALID_ARG; }
+
+int mk_plan_simulate(const mk_plan_t *p, int32_t n_trials, uint64_t seed) {
   if (!p || n_trials < 0) return MK_ERR_INVALID_ARG;
   return mk_plan_check(p, true, n_trials, seed);
 }
 
-int mk_plan_sizes(const mk_plan *p, size_t *ws, size_t *kv, size_t *logits, size_t *n_instr) {
+int mk_plan_sizes(const mk_plan_t *p, size_t *ws, size_t *kv, size_t *logits, size_t *n_instr) {
   if (!p) return MK_ERR_INVALID_ARG;
   const mk_model_shape &s = p->shape;
   if (ws) *ws = p->lay.total;
@@ -80,7 +89,7 @@ int mk_plan_sizes(const mk_plan *p, size_t *ws, size_t *kv, size_t *logits, size
   return MK_OK;
 }
 
-int mk_plan_get_info(const mk_plan *p, mk_plan_info *o) {
+int mk_plan_get_info(const mk_plan_t *p, mk_plan_info *o) {
   if (!p || !o) return MK_ERR_INVALID_ARG;
   std::memset(o, 0, sizeof *o);
   o->num_cus = p->n_cu;
@@ -101,7 +110,7 @@ int mk_plan_get_info(const mk_plan *p, mk_plan_info *o) {
   return MK_OK;
 }
 
-int mk_plan_export(const mk_plan *p, mk_instr_desc *out, size_t cap, size_t *n_out) {
+int mk_plan_export(const mk_plan_t *p, mk_instr_desc *out, size_t cap, size_t *n_out) {
   if (!p) return MK_ERR_INVALID_ARG;
   if (n_out) *n_out = p->instr.size();
   if (!out) return MK_OK;
@@ -126,13 +135,13 @@ int mk_plan_export(const mk_plan *p, mk_instr_desc *out, size_t cap, size_t *n_o
   return MK_OK;
 }
 
-void mk_plan_destroy(mk_plan *p) { delete p; }
+void mk_plan_destroy(mk_plan_t *p) { delete p; }
 
 // Host-side test hook: replace the instruction list of a plan with `n`
 // descriptors (cu/slot/op/layer/level/rows/split/wait/signal as exported).
 // Slots, tickets and partial indices are re-derived; the plan is then only
 // as valid as mk_plan_validate says.
-int mk_plan_set_instructions(mk_plan *p, const mk_instr_desc *d, size_t n) {
+int mk_plan_set_instructions(mk_plan_t *p, const mk_instr_desc *d, size_t n) {
   if (!p || (!d && n)) return MK_ERR_INVALID_ARG;
   std::vector<std::pair<std::pair<int, int>, size_t>> order;
   for (size_t i = 0; i < n; ++i) order.push_back({{d[i].cu, d[i].slot}, i});
@@ -180,7 +189,7 @@ int mk_plan_set_instructions(mk_plan *p, const mk_instr_desc *d, size_t n) {
 
 // ------------------------------------------------------------------ ctx
 
-static void build_rope(const mk_plan &p, std::vector<float> &rope) {
+static void build_rope(const mk_plan_t &p, std::vector<float> &rope) {
   // angle(pos, i) = pos * theta^(-2i/d), evaluated in double, stored as fp32 (cos, sin)
   const int d = p.shape.head_dim, half = d / 2;
   rope.resize((size_t)p.max_ctx * d);
@@ -201,7 +210,69 @@ static int upload_prog(mk_ctx *c, hipStream_t st) {
       hipMemcpyAsync(c->ws + c->plan.lay.layers, c->layers.data(), sizeof(MkLayerW) * c->layers.size(),
                      hipMemcpyHostToDevice, st) != hipSuccess)
     return MK_ERR_HIP;
+  if (!c->rowtab.empty() &&
+      hipMemcpyAsync(c->ws + c->plan.lay.rowtab, c->rowtab.data(), sizeof(MkRowTab) * c->rowtab.size(),
+                     hipMemcpyHostToDevice, st) != hipSuccess)
+    return MK_ERR_HIP;
   return MK_OK;
+}
+
+// Row table of the stream engine: for every projection instruction, where its
+// virtual rows start in memory, their length, and the row rotation that
+// deals them to the streamer waves (carried along each CU's list, so every
+// streamer's share of the list stays within one row of the others').
+static void build_rowtab(mk_ctx *c) {
+  const mk_plan_t &p = c->plan;
+  const mk_model_shape &s = p.shape;
+  const int64_t H = s.hidden, qd = (int64_t)s.n_q_heads * s.head_dim, kd = (int64_t)s.n_kv_heads * s.head_dim,
+                I = s.ffn;
+  c->rowtab.assign(p.instr.size(), MkRowTab{});
+  for (int cu = 0; cu < p.n_cu; ++cu) {
+    int off = 0;
+    for (int i = p.cu_begin[cu]; i < p.cu_begin[cu + 1]; ++i) {
+      const MkInstr &in = p.instr[i];
+      MkRowTab &t = c->rowtab[i];
+      t.off = off;
+      if (in.op == MKOP_ATTN) continue;
+      const MkLayerW *W = in.op == MKOP_LMHEAD ? nullptr : &c->layers[in.layer];
+      const int64_t r0 = in.r0;
+      int64_t K = H;
+      const uint16_t *b0 = nullptr, *b1 = nullptr;
+      int n = in.r1 - in.r0;
+      switch (in.op) {
+        case MKOP_QKV:
+          b0 = r0 < qd ? W->wq + r0 * H : r0 < qd + kd ? W->wk + (r0 - qd) * H : W->wv + (r0 - qd - kd) * H;
+          break;
+        case MKOP_OPROJ:
+          K = qd;
+          b0 = W->wo + r0 * K;
+          break;
+        case MKOP_GATEUP:
+          b0 = W->wg + r0 * H;
+          b1 = W->wu + r0 * H;
+          n *= 2;
+          break;
+        case MKOP_DOWN:
+          K = I;
+          b0 = W->wd + r0 * I;
+          break;
+        default:  // MKOP_LMHEAD
+          b0 = c->prog.lm_head + r0 * H;
+          break;
+      }
+      t.b0 = (uint64_t)(uintptr_t)b0;
+      t.rb = (int32_t)(2 * K);
+      if (b1) {
+        t.b1 = (uint64_t)(uintptr_t)b1;
+        t.stride2 = t.rb;
+      } else {
+        t.b1 = t.b0 + (uint64_t)t.rb;
+        t.stride2 = 2 * t.rb;
+      }
+      t.n = n;
+      off = (off + n) % MK_STREAMERS;
+    }
+  }
 }
 
 static int zero_sync(mk_ctx *c, hipStream_t st) {
@@ -216,7 +287,7 @@ static int zero_sync(mk_ctx *c, hipStream_t st) {
   return MK_OK;
 }
 
-int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void *stream, mk_ctx **out) {
+int mk_ctx_create(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, void *stream, mk_ctx **out) {
   if (!plan || !d_workspace || !out) return MK_ERR_INVALID_ARG;
   *out = nullptr;
   if (((uintptr_t)d_workspace & 255u) != 0) return MK_ERR_ALIGN;
@@ -228,19 +299,19 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   if (plan->opts.exec_mode != MK_EXEC_MULTI) {
     int n_dev_cu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&n_dev_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_ERR_HIP;
-    const int occ = plan->opts.exec_mode == MK_EXEC_MEGA ? mk_occupancy_role(plan->lds_bytes, &per_cu)
-                                                          : mk_occupancy_mega(mega_lds(plan), &per_cu);
+    const int occ = mk_occupancy(plan->opts.exec_mode, launch_lds(plan), &per_cu);
     if (occ) return MK_ERR_HIP;
     // persistence: every workgroup of the grid must be resident at once
     if (per_cu < 1 || (int64_t)plan->n_cu > (int64_t)per_cu * n_dev_cu) return MK_ERR_NOT_RESIDENT;
   }
+  if (mk_prepare_launch(plan->opts.exec_mode, launch_lds(plan))) return MK_ERR_HIP;
   mk_ctx *c = new (std::nothrow) mk_ctx();
   if (!c) return MK_ERR_INVALID_ARG;
   c->plan = *plan;
   c->ws = (char *)d_workspace;
   c->ws_bytes = ws_bytes;
   c->device = dev;
-  const mk_plan &p = c->plan;
+  const mk_plan_t &p = c->plan;
   const MkLayout &y = p.lay;
   const mk_model_shape &s = p.shape;
   MkProgram &P = c->prog;
@@ -273,6 +344,9 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   P.n_pages = p.n_pages;
   P.lds_total = p.lds_bytes;
   P.par_stride = (int64_t)((y.act_end - y.qkv) / 4);
+  P.st_out = p.st_out;
+  P.st_resid = p.st_resid;
+  P.st_ctl = p.st_ctl;
   char *w = c->ws;
   P.instr = (const MkInstr *)(w + y.instr);
   P.cu_begin = (const int32_t *)(w + y.cu_begin);
@@ -282,6 +356,7 @@ int mk_ctx_create(const mk_plan *plan, void *d_workspace, size_t ws_bytes, void 
   P.ev_flag_base = (const int32_t *)(w + y.ev_flag_base);
   P.rope = (const float *)(w + y.rope);
   P.layers = (MkLayerW *)(w + y.layers);
+  P.rowtab = (const MkRowTab *)(w + y.rowtab);
   P.qkv = (float *)(w + y.qkv);
   P.attn = (float *)(w + y.attn);
   P.xmid = (float *)(w + y.xmid);
@@ -351,6 +426,7 @@ int mk_load_weights(mk_ctx *c, const mk_weights *wt, void *stream) {
   c->prog.embed = (const uint16_t *)wt->embed;
   c->prog.lm_head = (const uint16_t *)(s.tie_embeddings ? wt->embed : wt->lm_head);
   c->prog.final_norm = (const uint16_t *)wt->final_norm;
+  build_rowtab(c);
   hipStream_t st = (hipStream_t)stream;
   int rc = upload_prog(c, st);
   if (rc == MK_OK && hipStreamSynchronize(st) != hipSuccess) rc = MK_ERR_HIP;
@@ -386,6 +462,9 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
   } else if (mode == MK_EXEC_FLAT) {
     S.multi = 0;
     if (mk_launch_mega(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
+  } else if (mode == MK_EXEC_STREAM) {
+    S.multi = 0;
+    if (mk_launch_stream(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
   } else {
     S.multi = 1;
     for (int lv = 0; lv < c->plan.n_levels; ++lv) {
@@ -439,7 +518,7 @@ int mk_ctx_set_watchdog_us(mk_ctx *c, uint32_t us, void *stream) {
   return rc;
 }
 
-int mk_plan_get_layout(const mk_plan *p, uint64_t out[8]) {
+int mk_plan_get_layout(const mk_plan_t *p, uint64_t out[8]) {
   if (!p || !out) return MK_ERR_INVALID_ARG;
   const MkLayout &y = p->lay;
   out[0] = y.qkv;

@@ -89,6 +89,25 @@ MKD void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// LDS flags are plain ds instructions in inline assembly, with no fences.
+// A wave's LDS operations execute in program order and LDS is shared by the
+// whole workgroup, so a flag written after a wave's data writes (or after its
+// last reads of a page) is seen only once those have taken effect.  Compiled
+// atomics with workgroup fences would instead wait for every global access
+// still in flight (global->LDS loads write LDS and are counted by vmcnt; the
+// compiler cannot prove they do not overlap the flag), which puts a full
+// memory round trip on every page a compute wave frees after storing an
+// output.  Ordering against global memory is made explicit where it matters
+// (a vmcnt wait before a wave reports results that other CUs will read).
+MKD uint32_t lds_off(const lds_u32 *p) { return (uint32_t)(size_t)p; }
+MKD uint32_t lds_ld(lds_u32 *p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);  // one address for the wave: the value is uniform
+}
+MKD void lds_st(lds_u32 *p, uint32_t v) { asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
+MKD void lds_add(lds_u32 *p, uint32_t v) { asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory"); }
+
 // read-only program data (instruction lists, pointer tables) through the
 // constant address space: scalar loads, counted by lgkmcnt, never by vmcnt
 template <class T>

@@ -15,6 +15,7 @@
 #include "mk_launch.h"
 #include "mk_ops_batched.h"
 #include "mk_roles_ops.h"
+#include "mk_stream.h"
 
 // Role-specialised persistent kernel: one workgroup per CU runs the CU's
 // instruction list with loader / sync-storer / compute waves.
@@ -90,29 +91,115 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
   }
 }
 
+// Stream engine (one sequence per step): waves 0..MK_NSW-1 stream projection
+// weights through register rings, wave MK_NSW synchronises; the waves meet
+// only at attention instructions, which all of them run together.
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_stream_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  __shared__ int s_flag;
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const int cu = blockIdx.x;
+  const int i0 = cld(&P.cu_begin[cu]), i1 = cld(&P.cu_begin[cu + 1]);
+  const int wave = __builtin_amdgcn_readfirstlane(mk_tid() >> 6);
+  {
+    lds_u32 *ctl = (lds_u32 *)((lds_char *)mk_flat_lds + P.st_ctl);
+    if (mk_tid() < ST_CTL_WORDS) ctl[mk_tid()] = 0u;
+  }
+  __syncthreads();
+  uint64_t *const trace = P.trace;
+  int i = i0;
+  while (i < i1) {
+    const MkInstr in = cld(&P.instr[i]);
+    if (in.op == MKOP_ATTN) {
+      // joint instruction: every wave arrives with nothing of its own in flight
+      __syncthreads();
+      const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
+      uint64_t ts = 0;
+      auto wait = [&]() -> bool {
+        const bool ok = in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, &s_flag);
+        if (trace) ts = __builtin_amdgcn_s_memrealtime();
+        return ok;
+      };
+      const int st = op_attn_mfma(P, S, in, &s_flag, wait);
+      if (st == MK_ST_ABORT) return;
+      if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
+      __syncthreads();
+      if (trace && mk_tid() == 0) trace_record(trace, i, tw, ts, __builtin_amdgcn_s_memrealtime(), cu, S.epoch);
+      ++i;
+      continue;
+    }
+    int j = i + 1;  // this segment: projections up to the next attention instruction
+    while (j < i1 && cld(&P.instr[j].op) != MKOP_ATTN) ++j;
+    const bool ok = wave < MK_NSW ? st_streamer<MK_RING>(P, i, j, wave) : st_sync(P, S, i, j);
+    if (!ok) return;
+    i = j;
+  }
+}
+
 extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Dynamic-LDS limit of each kernel, as last set in this process.  Launches
+// compare against it and call hipFuncSetAttribute only when it differs (a
+// context binds it once; a later occupancy query may have changed it).
+static int g_lds_set[4] = {-1, -1, -1, -1};
+static int lds_slot(const void *fn) {
+  return fn == (const void *)mk_mega_kernel        ? 0
+         : fn == (const void *)mk_role_mega_kernel ? 1
+         : fn == (const void *)mk_stream_kernel    ? 3
+                                                   : 2;
+}
 static hipError_t set_lds(const void *fn, int lds) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  g_lds_set[lds_slot(fn)] = e == hipSuccess ? lds : -1;
+  return e;
+}
+static inline bool ensure_lds(const void *fn, int lds) {
+  return g_lds_set[lds_slot(fn)] == lds || set_lds(fn, lds) == hipSuccess;
+}
+
+// The dynamic-LDS limit of a kernel is set once, when a context is bound
+// (mk_prepare_launch), not on every step: the step path is only the launch.
+static const void *exec_kernel(int exec_mode) {
+  return exec_mode == MKEXEC_FLAT     ? (const void *)mk_mega_kernel
+         : exec_mode == MKEXEC_MEGA   ? (const void *)mk_role_mega_kernel
+         : exec_mode == MKEXEC_STREAM ? (const void *)mk_stream_kernel
+                                      : (const void *)mk_role_level_kernel;
+}
+
+int mk_prepare_launch(int exec_mode, int lds) { return set_lds(exec_kernel(exec_mode), lds) == hipSuccess ? 0 : -1; }
+
+int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
+  if (!ensure_lds((const void *)mk_stream_kernel, lds)) return -1;
+  hipLaunchKernelGGL(mk_stream_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_occupancy(int exec_mode, int lds, int *blocks_per_cu) {
+  const void *fn = exec_kernel(exec_mode);
+  if (set_lds(fn, lds) != hipSuccess) return -1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, MK_BLOCK, lds) != hipSuccess) return -1;
+  *blocks_per_cu = nb;
+  return 0;
 }
 
 int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
-  if (set_lds((const void *)mk_mega_kernel, lds) != hipSuccess) return -1;
+  if (!ensure_lds((const void *)mk_mega_kernel, lds)) return -1;
   hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
-  if (set_lds((const void *)mk_role_mega_kernel, lds) != hipSuccess) return -1;
+  if (!ensure_lds((const void *)mk_role_mega_kernel, lds)) return -1;
   hipLaunchKernelGGL(mk_role_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s) {
   if (n_blocks <= 0) return 0;
-  if (set_lds((const void *)mk_role_level_kernel, lds) != hipSuccess) return -1;
+  if (!ensure_lds((const void *)mk_role_level_kernel, lds)) return -1;
   hipLaunchKernelGGL(mk_role_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -23,6 +23,9 @@
 #define MK_LDS_TOTAL (160 * 1024)         // LDS of one gfx950 workgroup
 
 // batched projections of the homogeneous engine (bf16 MFMA, up to 16 sequences)
+// stream engine: streamer waves per workgroup (the last wave synchronises)
+#define MK_STREAMERS (MK_NWAVES - 1)
+
 #define MK_MFMA_MIN_BATCH 2                   // sequences from which projections run on MFMA
 #define MK_BKC 2048                           // input columns staged in LDS per chunk
 #define MK_BROW (MK_BKC * 2 + 16)             // bytes per sequence row of one bf16 plane (+16: bank skew)
@@ -40,7 +43,7 @@
 #define MK_FA_LDS (MK_FA_WP + MK_NWAVES * MK_MAX_GROUP * 130 * 4)
 
 enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
-enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2 };
+enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2, MKEXEC_STREAM = 3 };
 
 enum MkOp : int32_t {
   MKOP_QKV = 1,
@@ -64,6 +67,18 @@ struct MkInstr {
   int32_t level;
 };
 
+// Stream engine: where a projection instruction's rows are, built on the
+// host once the weights are bound.  Virtual row v of the instruction starts
+// at (v odd ? b1 : b0) + (v / 2) * stride2 bytes and is rb bytes long
+// (gate/up: b0 = first gate row, b1 = first up row, stride2 = rb; other
+// projections: b1 = b0 + rb, stride2 = 2 rb).  off: the row rotation of the
+// instruction in its CU's list (virtual row v belongs to streamer
+// (v + off) mod the streamer count).  Attention instructions have n = 0.
+struct MkRowTab {
+  uint64_t b0, b1;
+  int32_t n, rb, stride2, off;
+};
+
 struct MkLayerW {
   const uint16_t *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *wg, *wu, *wd;
 };
@@ -80,6 +95,9 @@ struct MkProgram {
   // role-engine LDS layout (byte offsets into dynamic LDS) and ring size
   int32_t lds_x, lds_resid, lds_out, lds_ring, n_pages, lds_total;
   int32_t out_stride;                 // floats per sequence in the per-row result area
+  // stream engine LDS layout (byte offsets into dynamic LDS; the staged
+  // input vector starts at 0): row results, residual rows, control block
+  int32_t st_out, st_resid, st_ctl;
   // activations occupy one contiguous block starting at qkv; in sentinel
   // mode a second copy (the other step parity) follows at +par_stride floats
   int64_t par_stride;
@@ -95,6 +113,7 @@ struct MkProgram {
   // tables and weights
   const float *rope;           // [max_ctx][d/2][2] (cos, sin), fp32
   MkLayerW *layers;            // [L]
+  const MkRowTab *rowtab;      // [n_instr] (stream engine)
   const uint16_t *embed, *lm_head, *final_norm;
 
   // activations (fp32), one buffer per layer so no slot is rewritten in a step

@@ -56,15 +56,18 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
   if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
-  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_FLAT) return MK_ERR_INVALID_ARG;
+  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_STREAM) return MK_ERR_INVALID_ARG;
   // data sentinels replace the events only inside one persistent launch
   if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA) return MK_ERR_UNSUPPORTED;
+  // the stream engine runs one sequence per step; its sync wave holds a
+  // normalised vector of at most 4096 floats in registers
+  if (o->exec_mode == MK_EXEC_STREAM && (o->max_batch != 1 || s->hidden > 4096)) return MK_ERR_UNSUPPORTED;
   return MK_OK;
 }
 
 // Role-engine LDS: control block | per-compute-wave scratch | residual rows |
 // staged input vectors | page ring (the rest of the workgroup's 160 KiB).
-static int role_lds_layout(mk_plan *p) {
+static int role_lds_layout(mk_plan_t *p) {
   const mk_model_shape &s = p->shape;
   const int B = p->B, d = s.head_dim, G = p->G;
   if (B > MK_RB_MAXB) return MK_ERR_UNSUPPORTED;
@@ -93,7 +96,7 @@ static int role_lds_layout(mk_plan *p) {
   return MK_OK;
 }
 
-static int lds_requirement(const mk_plan *p) {
+static int lds_requirement(const mk_plan_t *p) {
   const mk_model_shape &s = p->shape;
   const int B = p->B, d = s.head_dim;
   int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * d, (int64_t)s.ffn});
@@ -109,7 +112,40 @@ static int lds_requirement(const mk_plan *p) {
   return (int)std::max<int64_t>(gemv, MK_FA_LDS);
 }
 
-void mk_plan_finalize_lists(mk_plan *p) {
+// Stream engine LDS: the staged input vector at 0 (the widest projection
+// input), the row results of one instruction, the residual rows of an O or
+// down slice, then (past the attention instruction's own layout, which
+// overlays the first two while all waves run attention) the control block.
+static void stream_lds_layout(mk_plan_t *p) {
+  const mk_model_shape &s = p->shape;
+  // row results: one partial sum per 4 KiB unit of every row
+  auto nsub = [](int64_t K) { return (int)((2 * K + 4095) / 4096); };
+  int max_out = 1, max_res = 1;
+  for (const MkInstr &in : p->instr) {
+    const int n = in.r1 - in.r0;
+    switch (in.op) {
+      case MKOP_QKV:
+      case MKOP_LMHEAD: max_out = std::max(max_out, n * nsub(s.hidden)); break;
+      case MKOP_GATEUP: max_out = std::max(max_out, 2 * n * nsub(s.hidden)); break;
+      case MKOP_OPROJ: max_out = std::max(max_out, n * nsub((int64_t)s.n_q_heads * s.head_dim)); break;
+      case MKOP_DOWN: max_out = std::max(max_out, n * nsub(s.ffn)); break;
+      default: break;
+    }
+    if (in.op == MKOP_OPROJ || in.op == MKOP_DOWN) max_res = std::max(max_res, n);
+  }
+  const int64_t kmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.n_q_heads * s.head_dim, (int64_t)s.ffn});
+  // the input vector is staged in whole 2048-column units (zero tail)
+  int64_t o = align_up((size_t)(kmax + 2047) / 2048 * 2048 * 4, 256);
+  p->st_out = (int)o;
+  o = align_up((size_t)(o + (int64_t)max_out * 4), 256);
+  p->st_resid = (int)o;
+  o = align_up((size_t)(o + (int64_t)max_res * 4), 256);
+  o = std::max<int64_t>(o, align_up(MK_FA_LDS, 256));
+  p->st_ctl = (int)o;
+  p->lds_bytes = (int)(o + 256);
+}
+
+void mk_plan_finalize_lists(mk_plan_t *p) {
   // stable sort instructions by (cu, slot order as given), recompute cu_begin and level lists
   const int n = (int)p->instr.size();
   std::vector<int> order(n);
@@ -141,7 +177,7 @@ void mk_plan_finalize_lists(mk_plan *p) {
   }
 }
 
-void mk_plan_compute_layout(mk_plan *p) {
+void mk_plan_compute_layout(mk_plan_t *p) {
   const mk_model_shape &s = p->shape;
   const size_t L = s.n_layers, B = p->B, H = s.hidden, d = s.head_dim, nq = s.n_q_heads,
                nkv = s.n_kv_heads, I = s.ffn, R = (nq + 2 * nkv) * d;
@@ -161,6 +197,7 @@ void mk_plan_compute_layout(mk_plan *p) {
   y.ev_flag_base = take(4 * std::max(p->n_events, 1));
   y.rope = take(4 * (size_t)p->max_ctx * d);
   y.layers = take(sizeof(MkLayerW) * L);
+  y.rowtab = take(sizeof(MkRowTab) * std::max<size_t>(p->instr.size(), 1));
   y.qkv = take(4 * L * B * R);
   y.attn = take(4 * L * B * nq * d);
   y.xmid = take(4 * L * B * H);
@@ -180,14 +217,14 @@ void mk_plan_compute_layout(mk_plan *p) {
   y.total = o;
 }
 
-int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan **out) {
+int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan_t **out) {
   if (!out) return MK_ERR_INVALID_ARG;
   *out = nullptr;
   int rc = check_shape(shape, opts);
   if (rc) return rc;
   if (n_cu < 1 || n_cu > 4096) return MK_ERR_INVALID_ARG;
 
-  mk_plan *p = new (std::nothrow) mk_plan();
+  mk_plan_t *p = new (std::nothrow) mk_plan_t();
   if (!p) return MK_ERR_INVALID_ARG;
   p->shape = *shape;
   p->opts = *opts;
@@ -224,7 +261,9 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // gate/up stream the other CUs started during attention, and would hold
   // up the O and gate/up events
   int og_cus = n_cu;
-  if (opts->exec_mode == MK_EXEC_FLAT && B == 1 && (int64_t)B * nkv * S < n_cu / 2) og_cus = n_cu - B * nkv * S;
+  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_STREAM) && B == 1 &&
+      (int64_t)B * nkv * S < n_cu / 2)
+    og_cus = n_cu - B * nkv * S;
   const int rg = (int)((ceil_div(I, og_cus) + 3) / 4 * 4), ro = (int)ceil_div(H, og_cus);
   const int rd = (int)ceil_div(H, n_cu),
             rl = (int)ceil_div(V, n_cu);
@@ -414,7 +453,13 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     p->instr_cu.swap(cu2);
   }
   mk_plan_finalize_lists(p);
-  if (opts->exec_mode == MK_EXEC_FLAT) {
+  if (opts->exec_mode == MK_EXEC_STREAM) {
+    stream_lds_layout(p);
+    if (p->lds_bytes > MK_LDS_TOTAL) {
+      delete p;
+      return MK_ERR_UNSUPPORTED;
+    }
+  } else if (opts->exec_mode == MK_EXEC_FLAT) {
     p->lds_bytes = lds_requirement(p);
     // the one-sequence ops stage a normalised vector of at most 16 floats per thread
     if (p->lds_bytes > MK_LDS_TOTAL || shape->hidden > 16 * MK_BLOCK) {
@@ -451,9 +496,9 @@ struct Access {
 };
 
 struct Checker {
-  const mk_plan *p;
+  const mk_plan_t *p;
   int L, H, d, nq, nkv, I, V, R, B, G, S;
-  explicit Checker(const mk_plan *pp) : p(pp) {
+  explicit Checker(const mk_plan_t *pp) : p(pp) {
     const mk_model_shape &s = p->shape;
     L = s.n_layers;
     H = s.hidden;
@@ -522,7 +567,7 @@ struct Writer {
 
 }  // namespace
 
-int mk_plan_check(const mk_plan *p, bool simulate, int trials, uint64_t seed) {
+int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) {
   if (!p) return MK_ERR_INVALID_ARG;
   Checker ck(p);
   const int n = (int)p->instr.size();

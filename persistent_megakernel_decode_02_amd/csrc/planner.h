@@ -10,19 +10,20 @@
 #include "mk_program.h"
 
 struct MkLayout {  // byte offsets inside the caller's workspace
-  size_t prog, instr, cu_begin, level_begin, level_list, ev_count, ev_flag_base, rope, layers;
+  size_t prog, instr, cu_begin, level_begin, level_list, ev_count, ev_flag_base, rope, layers, rowtab;
   size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, err;
   size_t sync_begin, sync_end;  // [ctr .. err] zeroed on create/reset
   size_t total;
 };
 
-struct mk_plan {
+struct mk_plan_s {
   mk_model_shape shape;
   mk_plan_opts opts;
   int n_cu = 0, S = 1, B = 1, max_ctx = 0, G = 1;
   int n_levels = 0, n_events = 0, n_flags = 0, n_tickets = 0, n_lm_parts = 0;
   int lds_bytes = 0;
   int lds_x = 0, lds_resid = 0, lds_out = 0, lds_ring = 0, n_pages = 0, out_stride = 0;  // role engine
+  int st_out = 0, st_resid = 0, st_ctl = 0;  // stream engine
   std::vector<MkInstr> instr;  // CU-major
   std::vector<int32_t> instr_cu;
   std::vector<int32_t> cu_begin, level_begin, level_list, ev_count, ev_flag_base;
@@ -31,7 +32,7 @@ struct mk_plan {
   double weight_bytes = 0;
 };
 
-int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan **out);
-int mk_plan_check(const mk_plan *p, bool simulate, int trials, uint64_t seed);
-void mk_plan_finalize_lists(mk_plan *p);  // recompute cu_begin / level lists from instr + instr_cu
-void mk_plan_compute_layout(mk_plan *p);
+int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan_t **out);
+int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed);
+void mk_plan_finalize_lists(mk_plan_t *p);  // recompute cu_begin / level lists from instr + instr_cu
+void mk_plan_compute_layout(mk_plan_t *p);

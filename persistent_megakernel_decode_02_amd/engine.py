@@ -39,7 +39,7 @@ class Engine:
         self.shape = shape
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
-        self.plan = mk.mk_plan_create(shape_struct(shape), plan_opts(max_batch, max_ctx, kv_splits, sync_mode,
+        self.plan = mk.mk_plan(shape_struct(shape), plan_opts(max_batch, max_ctx, kv_splits, sync_mode,
                                                                      exec_mode))
         self.info = mk.mk_plan_get_info(self.plan)
         ws, self.kv_bytes, self.logits_bytes, self.n_instr = mk.mk_plan_sizes(self.plan)
@@ -67,6 +67,13 @@ class Engine:
                            w["final_norm"].data_ptr(), *[C.cast(arrays[k], mk._PPV) for k in _LAYER_KEYS])
         mk.mk_load_weights(self.ctx, ws, self.stream.cuda_stream)
         self._keep = (keep, arrays, w)
+
+    def workspace_view(self, byte_offset: int, n_floats: int) -> torch.Tensor:
+        """fp32 view of n_floats of the workspace at byte_offset (a layout
+        offset from mk_plan_get_layout): lets tests read activations back."""
+        start = self.ws_ptr - self._ws.data_ptr() + byte_offset
+        assert start % 4 == 0 and start + 4 * n_floats <= self._ws.numel()
+        return self._ws[start:start + 4 * n_floats].view(torch.float32)
 
     def kv_cache(self) -> torch.Tensor:
         s = self.shape

@@ -28,7 +28,7 @@ MK_ERR_STATE = -10
 MK_ERR_UNSUPPORTED = -11
 
 MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
-MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT = 0, 1, 2
+MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM = 0, 1, 2, 3
 MK_ADVANCE = 1
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6
 
@@ -89,6 +89,7 @@ _lib = None
 # name -> (restype, argtypes) for every symbol include/mk.h declares
 SIGNATURES = {
     "mk_strerror": (C.c_char_p, [C.c_int]),
+    "mk_plan": (C.c_int, [C.POINTER(mk_model_shape), C.POINTER(mk_plan_opts), C.POINTER(C.c_void_p)]),
     "mk_plan_create": (C.c_int, [C.POINTER(mk_model_shape), C.POINTER(mk_plan_opts), C.POINTER(C.c_void_p)]),
     "mk_plan_validate": (C.c_int, [C.c_void_p]),
     "mk_plan_sizes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
@@ -143,6 +144,12 @@ def mk_strerror(code: int) -> str:
 
 
 # ------------------------------------------------------------------ plans
+
+def mk_plan(shape: mk_model_shape, opts: mk_plan_opts) -> C.c_void_p:
+    out = C.c_void_p()
+    _check(load_library().mk_plan(C.byref(shape), C.byref(opts), C.byref(out)), "mk_plan")
+    return out
+
 
 def mk_plan_create(shape: mk_model_shape, opts: mk_plan_opts) -> C.c_void_p:
     out = C.c_void_p()
