@@ -28,17 +28,17 @@ HBM_PEAK_GBS = 8000.0
 
 def bytes_per_pass(shape, passes):
     """Algorithmic HBM bytes of one pass, averaged over `passes` (each the
-    list of the batch's positions in that pass): every bf16 parameter once
-    for the whole batch (the embedding matrix once, as the tied LM head; one
-    embedding row per sequence otherwise extra); per sequence, the keys and
-    values of its cached positions read, the new position's keys/values
-    written, fp32 logits written and the token's embedding row read."""
+    list of the batch's positions in that pass): every bf16 parameter the
+    pass streams, once for the whole batch (one vocab x hidden matrix: the
+    LM head, which is the embedding matrix when tied; an untied embedding
+    matrix is not streamed, only one row per sequence is gathered); per
+    sequence, the keys and values of its cached positions read, the new
+    position's keys/values written, fp32 logits written and the token's
+    embedding row read."""
     s = shape
     d, L, H = s.head_dim, s.n_layers, s.hidden
     params = L * (H * (s.n_q_heads + 2 * s.n_kv_heads) * d + s.n_q_heads * d * H + 3 * H * s.ffn + 2 * H) \
         + s.vocab * H + H
-    if not s.tied:
-        params += s.vocab * H  # separate LM head; the embedding contributes one row below
     kv_b = L * s.n_kv_heads * d * 2 * 2  # bytes per cached position (keys + values)
     total = 0.0
     for ps in passes:
@@ -47,6 +47,25 @@ def bytes_per_pass(shape, passes):
 
 
 COPY_PROBE_BYTES = 256 << 20
+
+
+def host_facts():
+    """CPU model, logical CPU count and RAM of the host the baseline ran on."""
+    model, mem_kb = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    mem_kb = int(line.split()[1])
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "ram_gib": round(mem_kb / 2 ** 20, 1)}
 
 
 def kernel_source_digest() -> str:
@@ -132,7 +151,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
-                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag"],
+                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
+                             "stream-counter", "stream-flag"],
                     help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
                          "homogeneous engine with flag events)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
@@ -237,7 +257,9 @@ def main():
     modes = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
              "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL),
              "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
-             "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG)}
+             "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
+             "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
+             "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
     ms, info = timed(*modes[args.mode], K, W)
     log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
     ms_per = ms / K
@@ -246,7 +268,8 @@ def main():
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
-            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel", "flat-flag": "mk_mega_kernel"}.get(
+            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel", "flat-flag": "mk_mega_kernel",
+                       "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(
                 args.mode, "mk_role_mega_kernel"),
             "bytes_per_launch": bpp if args.mode != "multi" else None}
 
@@ -254,7 +277,8 @@ def main():
                        "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
                        "block_threads": info.block_threads}}
     if not args.no_extras:
-        for name in [m for m in modes if m != args.mode and (B <= 4 or m.startswith("flat"))]:
+        for name in [m for m in modes if m != args.mode and (B <= 4 or m.startswith("flat"))
+                     and (B == 1 or not m.startswith("stream"))]:
             ms2, _ = timed(*modes[name], K, W)
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -326,6 +350,7 @@ def main():
         cpu = {"value": round(n_done / el, 4), "unit": "passes/s", "cores": orc.num_threads(), "kind": "oracle",
                "sample": f"{n_done} greedy passes of {args.workload} from position {pos0[0]} (fp64 oracle, "
                          f"OpenMP over output rows), {el:.1f} s"}
+        cpu.update(host_facts())
         log(f"[bench] cpu oracle {cpu}")
 
     line = {

@@ -268,3 +268,61 @@ def test_sizes_match_layouts():
         assert ws < 64 << 20
     finally:
         mk.mk_plan_destroy(plan)
+
+
+def test_misaligned_or_short_workspace_is_refused_before_any_device_call():
+    # both checks come before the context touches a device, so no GPU is needed
+    plan = mk.mk_plan(shape_struct(si.TINY), plan_opts(1, 128, exec_mode=mk.MK_EXEC_FLAT, num_cus=8))
+    try:
+        ws, _, _, _ = mk.mk_plan_sizes(plan)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_ctx_create(plan, 0x10000 + 16, ws, 0)
+        assert e.value.code == mk.MK_ERR_ALIGN
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_ctx_create(plan, 0x10000, ws - 256, 0)
+        assert e.value.code == mk.MK_ERR_CTX_OVERFLOW
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_mk_plan_and_mk_plan_create_build_the_same_plan():
+    opts = plan_opts(1, 1152, exec_mode=mk.MK_EXEC_FLAT, sync_mode=mk.MK_SYNC_FLAG, num_cus=256)
+    a = mk.mk_plan(shape_struct(si.LLAMA_1B), opts)
+    b = mk.mk_plan_create(shape_struct(si.LLAMA_1B), opts)
+    try:
+        da, db = mk.mk_plan_export(a), mk.mk_plan_export(b)
+        assert len(da) == len(db)
+        fields = [f for f, _ in mk.mk_instr_desc._fields_]
+        assert all(getattr(x, f) == getattr(y, f) for x, y in zip(da, db) for f in fields)
+    finally:
+        mk.mk_plan_destroy(a)
+        mk.mk_plan_destroy(b)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama1b_pos1024", "llama1b_pos8192", "llama8b_pos2048"])
+@pytest.mark.parametrize("sync_mode", [mk.MK_SYNC_COUNTER, mk.MK_SYNC_FLAG])
+def test_stream_engine_plans(name, sync_mode):
+    # one sequence per step; its LDS holds the widest input vector, the row
+    # results and the attention instruction's own layout
+    shape, batch, max_ctx = SHAPES[name]
+    plan = mk.mk_plan(shape_struct(shape), plan_opts(1, max_ctx, num_cus=256, exec_mode=mk.MK_EXEC_STREAM,
+                                                       sync_mode=sync_mode))
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        info = mk.mk_plan_get_info(plan)
+        kmax = max(shape.hidden, shape.n_q_heads * shape.head_dim, shape.ffn)
+        assert kmax * 4 < info.lds_bytes <= 160 * 1024
+        assert mk.mk_plan_simulate(plan, 3, 7) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_stream_engine_limits():
+    s = si.WORKLOADS["llama1b_pos1024"].shape
+    with pytest.raises(mk.MkError) as e:  # one sequence per step only
+        mk.mk_plan(shape_struct(s), plan_opts(2, 1152, num_cus=256, exec_mode=mk.MK_EXEC_STREAM))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED
+    with pytest.raises(mk.MkError) as e:  # data sentinels are the role engine's
+        mk.mk_plan(shape_struct(s), plan_opts(1, 1152, num_cus=256, exec_mode=mk.MK_EXEC_STREAM,
+                                              sync_mode=mk.MK_SYNC_SENTINEL))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED

@@ -1,11 +1,14 @@
 """GPU parity of the decode path against the CPU oracle, through the C ABI.
 
 Tiny model: all 47 passes (16 teacher-forced prompt tokens, then greedy),
-in every execution and synchronisation mode, plus forced key-range splits.
-Llama-1B shape at position 1024 and 8192: full-logit parity on the first
-passes of the benchmarked configuration (same plan and launch shape as
-bench.py).  Modes must agree bit for bit with each other (same ops, same
-reduction orders)."""
+in every execution and synchronisation mode, plus forced key-range splits,
+host-driven positions, a NaN-filled cache and a batch below the plan's bound.
+Llama-1B shape: every pass of the benchmarked sequences (128 from position
+1024 in every engine, 64 from 8192 with split attention), and 8 passes of
+16 sequences with context lengths 512..4096, in the plan and launch shape
+bench.py times.  Modes of one engine must agree bit for bit with each other
+(same ops, same reduction orders).  Error paths: bad inputs, the watchdog, a
+grid wider than the device, misaligned pointers."""
 import numpy as np
 import pytest
 import torch
@@ -43,7 +46,9 @@ def test_device_is_mi355x():
 
 MODES = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
          "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
-         "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG)}
+         "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
+         "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
+         "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
 
 
 @pytest.mark.parametrize("mode", list(MODES.values()), ids=list(MODES))
@@ -54,12 +59,12 @@ def test_tiny_decode_matches_oracle(tiny_setup, mode):
     assert res.max_rel_err <= LOGIT_TOL
     assert res.max_rel_err <= 1e-4  # fp32 accumulation is far tighter than the bound
     assert res.near_ties == 0
-    exact = check_kv(res)
-    print(f"kv exact fraction {exact:.6f}")
+    print(f"kv exact fraction {check_kv(res):.6f}")
 
 
 @pytest.mark.parametrize("group", [("mega-counter", "mega-flag", "mega-sentinel", "multi"),
-                                   ("flat-counter", "flat-flag")], ids=["roles", "flat"])
+                                   ("flat-counter", "flat-flag"), ("stream-counter", "stream-flag")],
+                         ids=["roles", "flat", "stream"])
 def test_tiny_modes_bit_identical(tiny_setup, group):
     # the same ops under different synchronisation / launch schemes give the same bits
     runs = [_run_tiny(tiny_setup, exec_mode=MODES[m][0], sync_mode=MODES[m][1]) for m in group]
@@ -70,8 +75,9 @@ def test_tiny_modes_bit_identical(tiny_setup, group):
 
 
 @pytest.mark.parametrize("splits", [2, 5, 16])
-def test_tiny_split_attention_matches_oracle(tiny_setup, splits):
-    res = _run_tiny(tiny_setup, kv_splits=splits)
+@pytest.mark.parametrize("mode", ["mega-counter", "stream-flag"])
+def test_tiny_split_attention_matches_oracle(tiny_setup, splits, mode):
+    res = _run_tiny(tiny_setup, kv_splits=splits, exec_mode=MODES[mode][0], sync_mode=MODES[mode][1])
     assert res.max_rel_err <= 1e-4, res.max_rel_err
     assert res.near_ties == 0
     check_kv(res)
@@ -84,6 +90,17 @@ def test_tiny_host_driven_positions(tiny_setup):
     check_kv(res)
 
 
+# Tiny model with every not-yet-written cache slot holding a NaN bit
+# pattern: attention reads only slots [0, p]; padding rows of a key block
+# must not carry the stale NaN of slot p into the value product.
+@pytest.mark.parametrize("mode", ["flat-flag", "mega-counter", "stream-flag"])
+def test_tiny_nan_filled_cache(tiny_setup, mode):
+    res = _run_tiny(tiny_setup, exec_mode=MODES[mode][0], sync_mode=MODES[mode][1], kv_fill=0x7FC1)
+    assert np.isfinite(res.logits_last).all()
+    assert res.max_rel_err <= 1e-4
+    check_kv(res)
+
+
 @pytest.fixture(scope="module")
 def llama1b():
     wl = si.WORKLOADS["llama1b_pos1024"]
@@ -91,36 +108,46 @@ def llama1b():
     return w, engine.to_gpu(w), orc.Model(wl.shape, w)
 
 
-@pytest.mark.parametrize("mode", ["flat-flag", "flat-counter", "mega-counter", "mega-sentinel"])
-def test_llama1b_pos1024_first_passes(llama1b, mode):
+# Llama-1B shape at position 1024: every generated token of the benchmarked
+# sequence (128 passes), in every engine; the oracle trajectory is computed
+# once and shared by the modes whose tokens agree.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", ["stream-flag", "stream-counter", "flat-flag", "flat-counter", "mega-counter",
+                                  "mega-flag", "mega-sentinel", "multi"])
+def test_llama1b_pos1024_full_sequence(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
     w, gw, model = llama1b
-    res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+    res = run_decode(wl, wl.steps, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
                      sync_mode=MODES[mode][1])
-    print(f"llama1b@1024 {mode}: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
+    print(f"llama1b@1024 {mode}: {wl.steps} passes, max err {res.max_rel_err:.2e}, near ties {res.near_ties}, "
+          f"tokens {[t[0] for t in res.tokens[:8]]}...")
     assert res.max_rel_err <= LOGIT_TOL
     assert res.max_rel_err <= 1e-3
-    check_kv(res)
+    assert res.near_ties == 0
+    print(f"kv exact fraction {check_kv(res):.6f}")
 
 
-@pytest.mark.parametrize("mode", ["flat-flag", "mega-sentinel"])
-def test_llama1b_pos8192_split_attention(llama1b, mode):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", ["stream-flag", "flat-flag", "mega-sentinel"])
+def test_llama1b_pos8192_full_sequence(llama1b, mode):
+    # long context: split attention over the key range, 64 passes
     wl = si.WORKLOADS["llama1b_pos8192"]
     w, gw, model = llama1b
-    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+    res = run_decode(wl, wl.steps, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
                      sync_mode=MODES[mode][1])
-    print(f"llama1b@8192: errs {['%.2e' % e for e in res.per_step_err]} tokens {res.tokens}")
+    print(f"llama1b@8192 {mode}: max err {res.max_rel_err:.2e}, near ties {res.near_ties}")
     assert res.max_rel_err <= 1e-3
-    check_kv(res)
+    assert res.near_ties == 0
+    print(f"kv exact fraction {check_kv(res):.6f}")
 
 
 # Batched decode (projections on the matrix cores): per-sequence context
 # lengths drawn uniformly, every sequence checked against the oracle.
 TINY_BATCHED = {b: si.Workload(f"tiny_b{b}", TINY.shape, batch=b, steps=6, start_pos=-1, len_lo=1, len_hi=100,
-                               max_ctx=TINY.max_ctx) for b in (2, 5, 16)}
+                               max_ctx=TINY.max_ctx) for b in (2, 4, 5, 16)}
 
 
-@pytest.mark.parametrize("batch", sorted(TINY_BATCHED))
+@pytest.mark.parametrize("batch", [2, 5, 16])
 @pytest.mark.parametrize("mode", ["flat-counter", "flat-flag"])
 def test_tiny_batched_decode_matches_oracle(tiny_setup, batch, mode):
     wl = TINY_BATCHED[batch]
@@ -130,7 +157,7 @@ def test_tiny_batched_decode_matches_oracle(tiny_setup, batch, mode):
     print(f"tiny b={batch} {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}")
     assert res.max_rel_err <= 1e-3
     assert res.near_ties == 0
-    check_kv(res)
+    print(f"kv exact fraction {check_kv(res, max_rel_err=1e-3):.5f}")
 
 
 def test_tiny_batched_split_attention(tiny_setup):
@@ -138,21 +165,50 @@ def test_tiny_batched_split_attention(tiny_setup):
     w, gw, model = tiny_setup
     res = run_decode(wl, 3, weights=w, gpu_weights=gw, model=model, exec_mode=mk.MK_EXEC_FLAT, kv_splits=4)
     assert res.max_rel_err <= 1e-3
-    check_kv(res)
+    check_kv(res, max_rel_err=1e-3)
 
 
-def test_llama1b_batch16_first_passes(llama1b):
+def test_tiny_batched_nan_filled_cache(tiny_setup):
+    wl = TINY_BATCHED[5]
+    w, gw, model = tiny_setup
+    res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model, exec_mode=mk.MK_EXEC_FLAT,
+                     sync_mode=mk.MK_SYNC_FLAG, kv_fill=0xFFC3)
+    assert np.isfinite(res.logits_last).all()
+    assert res.max_rel_err <= 1e-3
+    check_kv(res, max_rel_err=1e-3)
+
+
+# A plan for 4 sequences stepped with 2: the sequence slots past the batch
+# are neither read nor written (their caches stay byte-identical).
+@pytest.mark.parametrize("mode", ["flat-flag", "flat-counter", "mega-counter", "mega-sentinel"])
+def test_batch_below_plan_bound_leaves_other_slots_alone(tiny_setup, mode):
+    wl = TINY_BATCHED[4]
+    w, gw, model = tiny_setup
+    for splits in (0, 3):
+        res = run_decode(wl, 4, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                         sync_mode=MODES[mode][1], batch=2, max_batch=4, kv_splits=splits)
+        assert res.max_rel_err <= 1e-3
+        assert res.near_ties == 0
+        check_kv(res, max_rel_err=1e-3)
+        assert np.array_equal(res.kv_gpu[:, :, 2:], res.kv_before[:, :, 2:])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", ["flat-flag", "flat-counter"])
+def test_llama1b_batch16(llama1b, mode):
     # the batched configuration as the benchmark runs it: 16 sequences with
-    # context lengths 512..4096, FLAT engine, projections on MFMA
+    # context lengths 512..4096, projections on MFMA; 8 passes
     wl = si.WORKLOADS["llama1b_b16"]
     w, gw, model = llama1b
-    res = run_decode(wl, 2, weights=w, gpu_weights=gw, model=model, exec_mode=mk.MK_EXEC_FLAT)
-    print(f"llama1b b16: errs max {res.max_rel_err:.2e} near ties {res.near_ties} tokens {res.tokens}")
+    res = run_decode(wl, 8, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                     sync_mode=MODES[mode][1])
+    print(f"llama1b b16 {mode}: errs max {res.max_rel_err:.2e} near ties {res.near_ties}")
     assert res.max_rel_err <= 1e-3
-    print(f"kv exact fraction {check_kv(res, min_exact=0.97):.5f}")
+    assert res.near_ties == 0
+    print(f"kv exact fraction {check_kv(res, max_rel_err=1e-3):.5f}")
 
 
-@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter"])
+@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter", "stream-flag"])
 def test_invalid_token_reports_input_error_and_poisons(tiny_setup, mode):
     w, gw, model = tiny_setup
     s = TINY.shape
@@ -180,7 +236,7 @@ def test_invalid_token_reports_input_error_and_poisons(tiny_setup, mode):
         eng.close()
 
 
-@pytest.mark.parametrize("mode", ["mega-counter", "flat-counter"])
+@pytest.mark.parametrize("mode", ["mega-counter", "flat-counter", "stream-counter"])
 def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup, mode):
     # the host claims more steps ran than the device counted, so the first
     # counter wait can never be met; a 2 ms watchdog ends the step cleanly.
@@ -202,6 +258,59 @@ def test_watchdog_turns_unmet_wait_into_timeout(tiny_setup, mode):
         assert rc == mk.MK_ERR_TIMEOUT, rc
         eng.reset()
         mk.mk_ctx_set_watchdog_us(eng.ctx, 2_000_000, eng.stream.cuda_stream)
+        eng.step(tok, pos, kv, logits)
+        assert eng.device_error()[0] == 0
+    finally:
+        eng.close()
+
+
+@pytest.mark.parametrize("exec_mode", [mk.MK_EXEC_FLAT, mk.MK_EXEC_MEGA, mk.MK_EXEC_STREAM])
+def test_plan_wider_than_the_device_is_refused(exec_mode):
+    # persistence needs every workgroup resident at once: a plan for twice
+    # the device's CUs must be refused before anything is launched
+    info = mk.mk_device_query(0)
+    s = TINY.shape
+    plan = mk.mk_plan(engine.shape_struct(s), engine.plan_opts(1, TINY.max_ctx, exec_mode=exec_mode,
+                                                               num_cus=2 * info.num_cus))
+    try:
+        ws, _, _, _ = mk.mk_plan_sizes(plan)
+        buf = torch.empty(ws + 256, dtype=torch.uint8, device="cuda:0")
+        base = (buf.data_ptr() + 255) // 256 * 256
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_ctx_create(plan, base, ws, torch.cuda.current_stream().cuda_stream)
+        assert e.value.code == mk.MK_ERR_NOT_RESIDENT
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_misaligned_pointers_are_refused(tiny_setup):
+    w, gw, model = tiny_setup
+    s = TINY.shape
+    eng = engine.Engine(s, gw, max_batch=1, max_ctx=TINY.max_ctx, exec_mode=mk.MK_EXEC_FLAT,
+                        sync_mode=mk.MK_SYNC_FLAG)
+    try:
+        st = eng.stream.cuda_stream
+        # a weight tensor 2 bytes off its 16-byte alignment
+        raw = torch.empty(gw["layers"][0]["wq"].numel() + 8, dtype=torch.bfloat16, device="cuda:0")
+        shifted = raw[1:1 + gw["layers"][0]["wq"].numel()].view(gw["layers"][0]["wq"].shape)
+        bad = dict(gw)
+        bad["layers"] = [dict(ld) for ld in gw["layers"]]
+        bad["layers"][1]["wq"] = shifted
+        with pytest.raises(mk.MkError) as e:
+            eng._bind(bad)
+        assert e.value.code == mk.MK_ERR_ALIGN
+        eng._bind(gw)  # the previous binding still works
+        kv = eng.kv_cache()
+        kv_raw = torch.zeros(kv.numel() + 8, dtype=torch.bfloat16, device="cuda:0")
+        logits = torch.empty((1, s.vocab), dtype=torch.float32, device="cuda:0")
+        pos = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        tok = torch.tensor([3], dtype=torch.int32, device="cuda:0")
+        rc = mk.mk_decode_step(eng.ctx, tok.data_ptr(), pos.data_ptr(), 1, kv_raw.data_ptr() + 2, logits.data_ptr(),
+                               None, 0, st)
+        assert rc == mk.MK_ERR_ALIGN
+        rc = mk.mk_decode_step(eng.ctx, tok.data_ptr(), pos.data_ptr(), 1, kv.data_ptr(), logits.data_ptr() + 2,
+                               None, 0, st)
+        assert rc == mk.MK_ERR_ALIGN
         eng.step(tok, pos, kv, logits)
         assert eng.device_error()[0] == 0
     finally:
