@@ -49,6 +49,7 @@ extern "C" {
 #define MK_ERR_PLAN (-9)          /* plan validation failed */
 #define MK_ERR_STATE (-10)        /* context poisoned by a device error; reset it */
 #define MK_ERR_UNSUPPORTED (-11)  /* option combination not built */
+#define MK_ERR_SCRATCH (-12)      /* workspace larger than the static scratch */
 
 /* ------------------------------------------------------------ model shape */
 /* Standard Llama decoder, nn.Linear weight convention W[out][in], bf16.
@@ -159,6 +160,21 @@ void mk_plan_destroy(mk_plan_t *plan);
 int mk_ctx_create(const mk_plan_t *plan, void *d_workspace, size_t workspace_bytes, void *stream,
                   mk_ctx **out);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * as mk_ctx_create, with the workspace taken from the library's static
+ * device scratch array (32 MiB, MK_SCRATCH_BYTES in the library; each
+ * device the library runs on holds it until the process ends) instead of a
+ * caller buffer.  Calls no device allocator.  The caller still owns the
+ * weights, KV cache, logits, tokens and positions.  Errors: MK_ERR_SCRATCH
+ * when the plan's workspace (mk_plan_sizes) exceeds 32 MiB, plus those of
+ * mk_ctx_create.  Every scratch context on a device shares the one array:
+ * creating one re-initialises it (counters and flags cleared with a fill
+ * kernel) and ends the previous scratch context on that device, whose later
+ * mk_decode_step calls return MK_ERR_STATE; calls on two scratch contexts
+ * that overlap on one device would race. */
+int mk_ctx_create_scratch(const mk_plan_t *plan, void *stream, mk_ctx **out);
+
 /* Weight tensors, all bf16 device pointers, 16-byte aligned, row-major
  * W[out][in].  Per-layer tensors come as host arrays of n_layers device
  * pointers.  lm_head is ignored (may be NULL) when the shape ties
@@ -213,7 +229,8 @@ int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
  * or buffer, unknown flag, weights not bound), MK_ERR_CTX_OVERFLOW (batch
  * outside 1..max_batch), MK_ERR_ALIGN (d_kv_cache not 16-byte aligned or an
  * int32/fp32 buffer not 4-byte aligned), MK_ERR_STATE (context poisoned),
- * MK_ERR_HIP (launch failed). */
+ * MK_ERR_HIP (launch failed); MK_ERR_STATE also for a scratch context
+ * that a newer one on the same device replaced. */
 int mk_decode_step(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
                    float *d_logits, int32_t *d_next_tokens, uint32_t flags, void *stream);
 

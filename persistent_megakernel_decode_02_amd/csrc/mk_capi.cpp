@@ -25,6 +25,7 @@ struct mk_ctx {
   bool poisoned = false;
   int64_t epoch = 0;
   int device = 0;
+  uint64_t scratch_gen = 0;  // non-zero: the workspace is the library's static scratch
 };
 
 static inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -53,6 +54,7 @@ const char *mk_strerror(int code) {
     case MK_ERR_PLAN: return "plan validation failed";
     case MK_ERR_STATE: return "context poisoned by an earlier device error; reset it";
     case MK_ERR_UNSUPPORTED: return "option combination not supported";
+    case MK_ERR_SCRATCH: return "plan workspace exceeds the library's static scratch (32 MiB)";
     default: return "unknown error";
   }
 }
@@ -287,15 +289,37 @@ static int zero_sync(mk_ctx *c, hipStream_t st) {
   return MK_OK;
 }
 
+// Bind a plan to workspace ws on device dev (the shared body of both
+// context constructors).
+static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, int dev, hipStream_t st,
+                         uint64_t scratch_gen, mk_ctx **out);
+
 int mk_ctx_create(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, void *stream, mk_ctx **out) {
   if (!plan || !d_workspace || !out) return MK_ERR_INVALID_ARG;
   *out = nullptr;
   if (((uintptr_t)d_workspace & 255u) != 0) return MK_ERR_ALIGN;
   if (ws_bytes < plan->lay.total) return MK_ERR_CTX_OVERFLOW;
   if (mk_plan_check(plan, false, 0, 0) != MK_OK) return MK_ERR_PLAN;
-  hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MK_ERR_HIP;
+  return ctx_create_on(plan, d_workspace, ws_bytes, dev, (hipStream_t)stream, 0, out);
+}
+
+int mk_ctx_create_scratch(const mk_plan_t *plan, void *stream, mk_ctx **out) {
+  if (!plan || !out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (plan->lay.total > MK_SCRATCH_BYTES) return MK_ERR_SCRATCH;
+  if (mk_plan_check(plan, false, 0, 0) != MK_OK) return MK_ERR_PLAN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_ERR_HIP;
+  void *ws = nullptr;
+  uint64_t gen = 0;
+  if (mk_scratch_acquire(dev, &ws, &gen)) return MK_ERR_HIP;
+  return ctx_create_on(plan, ws, MK_SCRATCH_BYTES, dev, (hipStream_t)stream, gen, out);
+}
+
+static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, int dev, hipStream_t st,
+                         uint64_t scratch_gen, mk_ctx **out) {
   if (plan->opts.exec_mode != MK_EXEC_MULTI) {
     int n_dev_cu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&n_dev_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_ERR_HIP;
@@ -311,6 +335,7 @@ int mk_ctx_create(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, voi
   c->ws = (char *)d_workspace;
   c->ws_bytes = ws_bytes;
   c->device = dev;
+  c->scratch_gen = scratch_gen;
   const mk_plan_t &p = c->plan;
   const MkLayout &y = p.lay;
   const mk_model_shape &s = p.shape;
@@ -439,6 +464,8 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
   if (!c || !d_tokens || !d_positions || !d_kv || !d_logits) return MK_ERR_INVALID_ARG;
   if (c->poisoned) return MK_ERR_STATE;
   if (!c->weights) return MK_ERR_INVALID_ARG;
+  // a newer scratch context on this device has re-initialised the array
+  if (c->scratch_gen && !mk_scratch_current(c->device, c->scratch_gen)) return MK_ERR_STATE;
   if (batch < 1 || batch > c->plan.B) return MK_ERR_CTX_OVERFLOW;
   if (flags & ~MK_ADVANCE) return MK_ERR_INVALID_ARG;
   if (!aligned16(d_kv) || ((uintptr_t)d_logits & 3u) || ((uintptr_t)d_tokens & 3u) || ((uintptr_t)d_positions & 3u))

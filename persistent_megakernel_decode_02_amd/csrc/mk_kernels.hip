@@ -12,6 +12,8 @@
 // one persistent launch).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mk_launch.h"
 #include "mk_ops_batched.h"
 #include "mk_roles_ops.h"
@@ -134,6 +136,41 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_stream_kernel(const Mk
     if (!ok) return;
     i = j;
   }
+}
+
+// ------------------------------------------------------ static scratch
+//
+// Workspace of contexts created by mk_ctx_create_scratch: a file-scope device
+// array, so those contexts allocate no device memory.  In host code the
+// array's name is only a stand-in; its device address is looked up once per
+// device (with that device current) and kept.  Every scratch context on a
+// device shares the one array: creating a context re-initialises it, which
+// ends the previous scratch context on that device (its generation is no
+// longer current, and mk_decode_step refuses it).
+static __device__ __align__(256) char scratch[MK_SCRATCH_BYTES];
+
+#define MK_SCRATCH_DEVICES 64
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[MK_SCRATCH_DEVICES];
+static uint64_t g_scratch_gen[MK_SCRATCH_DEVICES];
+
+int mk_scratch_acquire(int dev, void **ptr, uint64_t *gen) {
+  if (dev < 0 || dev >= MK_SCRATCH_DEVICES) return -1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -1;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *gen = ++g_scratch_gen[dev];
+  return 0;
+}
+
+bool mk_scratch_current(int dev, uint64_t gen) {
+  if (dev < 0 || dev >= MK_SCRATCH_DEVICES) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_gen[dev] == gen;
 }
 
 extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {

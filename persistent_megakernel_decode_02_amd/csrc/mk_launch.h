@@ -6,6 +6,12 @@
 
 #include "mk_program.h"
 
+// static scratch (allocation-free contexts): the array's device address on
+// device `dev` and a new generation number; whether `gen` is still current
+#define MK_SCRATCH_BYTES (32u << 20)
+int mk_scratch_acquire(int dev, void **ptr, uint64_t *gen);
+bool mk_scratch_current(int dev, uint64_t gen);
+
 int mk_prepare_launch(int exec_mode, int lds);  // once per context: dynamic LDS limit
 int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
 int mk_occupancy(int exec_mode, int lds, int *blocks_per_cu);  // persistent kernels of the exec modes

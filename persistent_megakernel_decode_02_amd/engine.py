@@ -32,10 +32,12 @@ def plan_opts(max_batch: int, max_ctx: int, kv_splits: int = 0, sync_mode: int =
 class Engine:
     def __init__(self, shape, gpu_weights: Dict[str, object], max_batch: int, max_ctx: int, kv_splits: int = 0,
                  sync_mode: int = mk.MK_SYNC_COUNTER, exec_mode: int = mk.MK_EXEC_MEGA,
-                 stream: Optional[torch.cuda.Stream] = None, device: str = "cuda:0"):
+                 stream: Optional[torch.cuda.Stream] = None, device: str = "cuda:0", scratch: bool = False):
         """gpu_weights: {"embed", "lm_head" (None when tied), "final_norm",
         "layers": [{attn_norm, wq, wk, wv, wo, mlp_norm, wg, wu, wd}]}, every
-        tensor bf16, contiguous, on `device`."""
+        tensor bf16, contiguous, on `device`.  scratch: take the workspace
+        from the library's static device array (mk_ctx_create_scratch)
+        instead of allocating one."""
         self.shape = shape
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
@@ -44,10 +46,15 @@ class Engine:
         self.info = mk.mk_plan_get_info(self.plan)
         ws, self.kv_bytes, self.logits_bytes, self.n_instr = mk.mk_plan_sizes(self.plan)
         self.ws_bytes = ws
-        self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
-        base = self._ws.data_ptr()
-        self.ws_ptr = (base + 255) // 256 * 256
-        self.ctx = mk.mk_ctx_create(self.plan, self.ws_ptr, ws, self.stream.cuda_stream)
+        if scratch:
+            self._ws = None
+            self.ws_ptr = None
+            self.ctx = mk.mk_ctx_create_scratch(self.plan, self.stream.cuda_stream)
+        else:
+            self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+            base = self._ws.data_ptr()
+            self.ws_ptr = (base + 255) // 256 * 256
+            self.ctx = mk.mk_ctx_create(self.plan, self.ws_ptr, ws, self.stream.cuda_stream)
         self._bind(gpu_weights)
 
     def _bind(self, w):
@@ -71,6 +78,7 @@ class Engine:
     def workspace_view(self, byte_offset: int, n_floats: int) -> torch.Tensor:
         """fp32 view of n_floats of the workspace at byte_offset (a layout
         offset from mk_plan_get_layout): lets tests read activations back."""
+        assert self._ws is not None, "a scratch context's workspace is the library's own"
         start = self.ws_ptr - self._ws.data_ptr() + byte_offset
         assert start % 4 == 0 and start + 4 * n_floats <= self._ws.numel()
         return self._ws[start:start + 4 * n_floats].view(torch.float32)

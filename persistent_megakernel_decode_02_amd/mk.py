@@ -26,6 +26,7 @@ MK_ERR_INPUT = -8
 MK_ERR_PLAN = -9
 MK_ERR_STATE = -10
 MK_ERR_UNSUPPORTED = -11
+MK_ERR_SCRATCH = -12
 
 MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
 MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM = 0, 1, 2, 3
@@ -100,6 +101,7 @@ SIGNATURES = {
     "mk_plan_destroy": (None, [C.c_void_p]),
     "mk_plan_set_instructions": (C.c_int, [C.c_void_p, C.POINTER(mk_instr_desc), C.c_size_t]),
     "mk_ctx_create": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]),
+    "mk_ctx_create_scratch": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
     "mk_load_weights": (C.c_int, [C.c_void_p, C.POINTER(mk_weights), C.c_void_p]),
     "mk_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_uint32, C.c_void_p]),
@@ -208,6 +210,12 @@ def mk_ctx_create(plan, d_workspace: int, workspace_bytes: int, stream: int) -> 
     out = C.c_void_p()
     _check(load_library().mk_ctx_create(plan, C.c_void_p(d_workspace), workspace_bytes, C.c_void_p(stream),
                                         C.byref(out)), "mk_ctx_create")
+    return out
+
+
+def mk_ctx_create_scratch(plan, stream: int) -> C.c_void_p:
+    out = C.c_void_p()
+    _check(load_library().mk_ctx_create_scratch(plan, C.c_void_p(stream), C.byref(out)), "mk_ctx_create_scratch")
     return out
 
 
