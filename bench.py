@@ -151,7 +151,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
-                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
+                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag", "flat-sentinel",
                              "stream-counter", "stream-flag"],
                     help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
                          "homogeneous engine with flag events)")
@@ -258,6 +258,7 @@ def main():
              "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL),
              "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
              "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
+             "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
              "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
              "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
     ms, info = timed(*modes[args.mode], K, W)
@@ -269,7 +270,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
             "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel", "flat-flag": "mk_mega_kernel",
-                       "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(
+                       "flat-sentinel": "mk_mega_kernel", "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(
                 args.mode, "mk_role_mega_kernel"),
             "bytes_per_launch": bpp if args.mode != "multi" else None}
 

@@ -18,6 +18,7 @@ struct mk_ctx {
   char *ws = nullptr;        // device workspace base
   size_t ws_bytes = 0;
   MkProgram prog{};          // host image of the device MkProgram
+  MkProgram prog_odd{};      // sentinel mode: the odd-step record of the homogeneous engine
   std::vector<MkLayerW> layers;
   std::vector<MkRowTab> rowtab;  // stream engine row table (host staging)
   std::vector<float> rope;   // host staging kept alive for async uploads
@@ -205,9 +206,29 @@ static void build_rope(const mk_plan_t &p, std::vector<float> &rope) {
     }
 }
 
+// Upload the program record(s).  In sentinel mode the activations have two
+// copies (one per step parity); the role engine offsets into them itself,
+// while the homogeneous engine gets a second record whose activation
+// pointers name the odd copy.  Each record's act_other is the copy its steps
+// reset for the step after.
 static int upload_prog(mk_ctx *c, hipStream_t st) {
-  if (hipMemcpyAsync(c->ws + c->plan.lay.prog, &c->prog, sizeof(MkProgram), hipMemcpyHostToDevice, st) != hipSuccess)
+  MkProgram &P = c->prog;
+  const int64_t ps = P.par_stride;
+  if (c->plan.opts.sync_mode == MK_SYNC_SENTINEL) P.act_other = P.qkv + ps;
+  if (hipMemcpyAsync(c->ws + c->plan.lay.prog, &P, sizeof(MkProgram), hipMemcpyHostToDevice, st) != hipSuccess)
     return MK_ERR_HIP;
+  if (c->plan.opts.sync_mode == MK_SYNC_SENTINEL) {
+    MkProgram &Q = c->prog_odd;
+    Q = P;
+    Q.qkv += ps;
+    Q.attn += ps;
+    Q.xmid += ps;
+    Q.hbuf += ps;
+    Q.xout += ps;
+    Q.act_other = P.qkv;
+    if (hipMemcpyAsync(c->ws + c->plan.lay.prog_odd, &Q, sizeof(MkProgram), hipMemcpyHostToDevice, st) != hipSuccess)
+      return MK_ERR_HIP;
+  }
   if (!c->layers.empty() &&
       hipMemcpyAsync(c->ws + c->plan.lay.layers, c->layers.data(), sizeof(MkLayerW) * c->layers.size(),
                      hipMemcpyHostToDevice, st) != hipSuccess)
@@ -323,12 +344,12 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   if (plan->opts.exec_mode != MK_EXEC_MULTI) {
     int n_dev_cu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&n_dev_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_ERR_HIP;
-    const int occ = mk_occupancy(plan->opts.exec_mode, launch_lds(plan), &per_cu);
+    const int occ = mk_occupancy(plan->opts.exec_mode, plan->opts.sync_mode, launch_lds(plan), &per_cu);
     if (occ) return MK_ERR_HIP;
     // persistence: every workgroup of the grid must be resident at once
     if (per_cu < 1 || (int64_t)plan->n_cu > (int64_t)per_cu * n_dev_cu) return MK_ERR_NOT_RESIDENT;
   }
-  if (mk_prepare_launch(plan->opts.exec_mode, launch_lds(plan))) return MK_ERR_HIP;
+  if (mk_prepare_launch(plan->opts.exec_mode, plan->opts.sync_mode, launch_lds(plan))) return MK_ERR_HIP;
   mk_ctx *c = new (std::nothrow) mk_ctx();
   if (!c) return MK_ERR_INVALID_ARG;
   c->plan = *plan;
@@ -488,7 +509,9 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
     if (mk_launch_role_mega(dp, S, c->plan.n_cu, c->plan.lds_bytes, st)) return MK_ERR_HIP;
   } else if (mode == MK_EXEC_FLAT) {
     S.multi = 0;
-    if (mk_launch_mega(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
+    const bool sent = c->plan.opts.sync_mode == MK_SYNC_SENTINEL;
+    if (sent && (c->epoch & 1)) dp = (const MkProgram *)(c->ws + c->plan.lay.prog_odd);
+    if (mk_launch_mega(dp, S, c->plan.n_cu, mega_lds(&c->plan), sent, st)) return MK_ERR_HIP;
   } else if (mode == MK_EXEC_STREAM) {
     S.multi = 0;
     if (mk_launch_stream(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;

@@ -286,6 +286,59 @@ MKD void mk_raise(const PT &P, int code, int detail) {
 template <class PT>
 MKD bool mk_aborted(const PT &P) { return __builtin_amdgcn_readfirstlane(ldci(P.err + 2)) != 0; }
 
+// ----------------------------------------------- data-sentinel polling
+//
+// With MKSYNC_SENTINEL the homogeneous engine has no events between levels:
+// an activation word starts each step as MK_SENTINEL and is written once by
+// its producer, so a consumer's staging load is also its poll.  These
+// loads repeat (per lane) until no word holds the sentinel, bounded by the
+// watchdog; `ok` turns false on a timeout or abort (the error is raised).
+MKD bool has_sent(const mk_u32x4 &v) {
+  return v.x == MK_SENTINEL || v.y == MK_SENTINEL || v.z == MK_SENTINEL || v.w == MK_SENTINEL;
+}
+template <class PT>
+MKD bool poll_fail(const PT &P, uint32_t &spins, uint64_t &t0, int detail) {
+  if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_s_sleep(1);
+  if ((++spins & 63u) == 0) {
+    if (mk_aborted(P)) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)P.watchdog_ticks) {
+      mk_raise(P, MK_E_TIMEOUT, detail);
+      return true;
+    }
+  }
+  return false;
+}
+// finish a 16-byte device-coherent load v (issued at byte offset off of r)
+template <class PT>
+MKD mk_u32x4 poll16(const PT &P, __amdgpu_buffer_rsrc_t r, int off, mk_u32x4 v, bool &ok) {
+  uint32_t spins = 0;
+  uint64_t t0 = 0;
+  while (ok && has_sent(v)) {
+    if (poll_fail(P, spins, t0, 0x30000)) {
+      ok = false;
+      break;
+    }
+    v = ldc16(r, off);
+  }
+  return v;
+}
+template <class PT>
+MKD float ldcp(const PT &P, const float *p, bool sent, bool &ok) {
+  float v = ldc(p);
+  if (!sent) return v;
+  uint32_t spins = 0;
+  uint64_t t0 = 0;
+  while (ok && __float_as_uint(v) == MK_SENTINEL) {
+    if (poll_fail(P, spins, t0, 0x30001)) {
+      ok = false;
+      break;
+    }
+    v = ldc(p);
+  }
+  return v;
+}
+
 // Wait for event `ev` of this step (global loads issued before the wait stay
 // in flight: the workgroup barriers wait for LDS traffic only).  Counter mode: one lane polls the
 // monotonic counter until it reaches (epoch+1) * triggers.  Flag mode: one

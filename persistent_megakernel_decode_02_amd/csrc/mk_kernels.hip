@@ -57,12 +57,21 @@ __device__ __forceinline__ void trace_record(uint64_t *trace, int i, uint64_t tw
   r[4] = r[5] = r[6] = r[7] = 0;
 }
 
-extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_flag;
-  const MkProgram &P = *Pp;
+// Homogeneous engine: every workgroup walks its CU's instruction list.  SENT:
+// data-sentinel synchronisation (the ops poll their inputs; no events), a
+// build of its own so the event build keeps its register allocation.
+template <bool SENT>
+MKD void mega_body(const MkProgram &P, const MkStep &S, float *smem, int *s_flag) {
   if (mk_aborted(P)) return;
   const int cu = blockIdx.x;
+  if constexpr (SENT) {
+    // this CU's share of the other parity's activations (read by the next
+    // step, written by no one in this one) goes back to the sentinel
+    const size_t n = (size_t)P.par_stride, per = (n + P.n_cu - 1) / P.n_cu;
+    const size_t lo = (size_t)cu * per, hi = min(lo + per, n);
+    uint32_t *o = reinterpret_cast<uint32_t *>(P.act_other);
+    for (size_t i = lo + threadIdx.x; i < hi; i += MK_BLOCK) stcu(o + i, MK_SENTINEL);
+  }
   const int i0 = cld(&P.cu_begin[cu]), i1 = cld(&P.cu_begin[cu + 1]);  // scalar: the list walk stays uniform
   uint64_t *const trace = P.trace;
   for (int i = i0; i < i1; ++i) {
@@ -73,9 +82,9 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
       const MkInstr nx = cld(&P.instr[i + 1]);
       if (nx.op == MKOP_GATEUP && nx.layer == in.layer) {  // O and gate/up as one unit
         uint64_t te_o = 0, ts_g = 0;
-        const int st = run_o_gateup(P, S, in, nx, smem, &s_flag, trace != nullptr, ts, te_o, ts_g);
+        const int st = run_o_gateup<SENT>(P, S, in, nx, smem, s_flag, trace != nullptr, ts, te_o, ts_g);
         if (st == MK_ST_ABORT) return;
-        if (st == MK_ST_SIGNAL && nx.sig_ev >= 0) mk_signal(P, S, nx.sig_ev, nx.sig_slot);
+        if (!SENT && st == MK_ST_SIGNAL && nx.sig_ev >= 0) mk_signal(P, S, nx.sig_ev, nx.sig_slot);
         __syncthreads();
         if (trace && threadIdx.x == 0) {
           trace_record(trace, i, tw, ts, te_o, cu, S.epoch);
@@ -85,12 +94,24 @@ extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkPr
         continue;
       }
     }
-    const int st = run_instr(P, S, in, smem, &s_flag, trace != nullptr, ts);
+    const int st = run_instr<SENT>(P, S, in, smem, s_flag, trace != nullptr, ts);
     if (st == MK_ST_ABORT) return;
-    if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
+    if (!SENT && st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
     if (trace && threadIdx.x == 0) trace_record(trace, i, tw, ts, __builtin_amdgcn_s_memrealtime(), cu, S.epoch);
   }
+}
+
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag;
+  mega_body<false>(*Pp, S, smem, &s_flag);
+}
+
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_sent_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag;
+  mega_body<true>(*Pp, S, smem, &s_flag);
 }
 
 // Stream engine (one sequence per step): waves 0..MK_NSW-1 stream projection
@@ -180,11 +201,12 @@ extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
 // Dynamic-LDS limit of each kernel, as last set in this process.  Launches
 // compare against it and call hipFuncSetAttribute only when it differs (a
 // context binds it once; a later occupancy query may have changed it).
-static int g_lds_set[4] = {-1, -1, -1, -1};
+static int g_lds_set[5] = {-1, -1, -1, -1, -1};
 static int lds_slot(const void *fn) {
   return fn == (const void *)mk_mega_kernel        ? 0
          : fn == (const void *)mk_role_mega_kernel ? 1
          : fn == (const void *)mk_stream_kernel    ? 3
+         : fn == (const void *)mk_mega_sent_kernel ? 4
                                                    : 2;
 }
 static hipError_t set_lds(const void *fn, int lds) {
@@ -198,14 +220,17 @@ static inline bool ensure_lds(const void *fn, int lds) {
 
 // The dynamic-LDS limit of a kernel is set once, when a context is bound
 // (mk_prepare_launch), not on every step: the step path is only the launch.
-static const void *exec_kernel(int exec_mode) {
+static const void *exec_kernel(int exec_mode, int sync_mode) {
+  if (exec_mode == MKEXEC_FLAT && sync_mode == MKSYNC_SENTINEL) return (const void *)mk_mega_sent_kernel;
   return exec_mode == MKEXEC_FLAT     ? (const void *)mk_mega_kernel
          : exec_mode == MKEXEC_MEGA   ? (const void *)mk_role_mega_kernel
          : exec_mode == MKEXEC_STREAM ? (const void *)mk_stream_kernel
                                       : (const void *)mk_role_level_kernel;
 }
 
-int mk_prepare_launch(int exec_mode, int lds) { return set_lds(exec_kernel(exec_mode), lds) == hipSuccess ? 0 : -1; }
+int mk_prepare_launch(int exec_mode, int sync_mode, int lds) {
+  return set_lds(exec_kernel(exec_mode, sync_mode), lds) == hipSuccess ? 0 : -1;
+}
 
 int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
   if (!ensure_lds((const void *)mk_stream_kernel, lds)) return -1;
@@ -213,8 +238,8 @@ int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int ld
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int mk_occupancy(int exec_mode, int lds, int *blocks_per_cu) {
-  const void *fn = exec_kernel(exec_mode);
+int mk_occupancy(int exec_mode, int sync_mode, int lds, int *blocks_per_cu) {
+  const void *fn = exec_kernel(exec_mode, sync_mode);
   if (set_lds(fn, lds) != hipSuccess) return -1;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, MK_BLOCK, lds) != hipSuccess) return -1;
@@ -222,9 +247,11 @@ int mk_occupancy(int exec_mode, int lds, int *blocks_per_cu) {
   return 0;
 }
 
-int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
-  if (!ensure_lds((const void *)mk_mega_kernel, lds)) return -1;
-  hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, bool sentinel, hipStream_t s) {
+  const void *fn = sentinel ? (const void *)mk_mega_sent_kernel : (const void *)mk_mega_kernel;
+  if (!ensure_lds(fn, lds)) return -1;
+  if (sentinel) hipLaunchKernelGGL(mk_mega_sent_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  else hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -12,10 +12,10 @@
 int mk_scratch_acquire(int dev, void **ptr, uint64_t *gen);
 bool mk_scratch_current(int dev, uint64_t gen);
 
-int mk_prepare_launch(int exec_mode, int lds);  // once per context: dynamic LDS limit
+int mk_prepare_launch(int exec_mode, int sync_mode, int lds);  // once per context: dynamic LDS limit
 int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
-int mk_occupancy(int exec_mode, int lds, int *blocks_per_cu);  // persistent kernels of the exec modes
-int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
+int mk_occupancy(int exec_mode, int sync_mode, int lds, int *blocks_per_cu);  // persistent kernels of the exec modes
+int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, bool sentinel, hipStream_t s);
 int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_occupancy_role(int lds, int *blocks_per_cu);

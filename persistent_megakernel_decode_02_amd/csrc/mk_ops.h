@@ -133,7 +133,9 @@ MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr
 // no load sits under a branch.  n is a multiple of 4.
 #define MK_OOB 0x40000000  // byte offset past every descriptor's range
 
-MKD void stage_vec(float *xs, const float *src, int n) {
+// sent: poll each chunk until its producer has written it (data-sentinel
+// mode); ok turns false on a timeout or abort.
+MKD void stage_vec(const MkProgram &P, float *xs, const float *src, int n, bool sent, bool &ok) {
   const int tid = mk_tid(), nc = n >> 2;
   const __amdgpu_buffer_rsrc_t r = mk_rsrc(src, (uint32_t)n * 4u);
   for (int c0 = 0; c0 < nc; c0 += 4 * MK_BLOCK) {
@@ -146,6 +148,7 @@ MKD void stage_vec(float *xs, const float *src, int n) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + tid + k * MK_BLOCK;
+      if (sent) v[k] = poll16(P, r, c < nc ? c * 16 : MK_OOB, v[k], ok);
       if (c < nc) *reinterpret_cast<mk_u32x4 *>(xs + 4 * c) = v[k];
     }
   }
@@ -171,8 +174,8 @@ MKD void load_gain(NormGain &g, const uint16_t *gain, int n) {
 // Stage x[n] (fp32 from coherent memory, or the bf16 embedding row when
 // `emb` is set) into xs as x * (1 / sqrt(mean(x^2) + eps)) * gain.  The sum
 // of squares comes from the registers the loads filled; ends with a barrier.
-MKD void stage_norm(float *xs, const float *src, const uint16_t *emb, int n, const NormGain &g, float eps,
-                    float *red) {
+MKD void stage_norm(const MkProgram &P, float *xs, const float *src, const uint16_t *emb, int n, const NormGain &g,
+                    float eps, float *red, bool sent, bool &ok) {
   const int tid = mk_tid(), nc = n >> 2;
   float4 x[4];
   if (emb) {
@@ -185,11 +188,18 @@ MKD void stage_norm(float *xs, const float *src, const uint16_t *emb, int n, con
     }
   } else {
     const __amdgpu_buffer_rsrc_t r = mk_rsrc(src, (uint32_t)n * 4u);
+    mk_u32x4 v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = tid + k * MK_BLOCK;
-      const mk_u32x4 v = ldc16(r, c < nc ? c * 16 : MK_OOB);
-      x[k] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+      v[k] = ldc16(r, c < nc ? c * 16 : MK_OOB);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = tid + k * MK_BLOCK;
+      if (sent) v[k] = poll16(P, r, c < nc ? c * 16 : MK_OOB, v[k], ok);
+      x[k] = make_float4(__uint_as_float(v[k].x), __uint_as_float(v[k].y), __uint_as_float(v[k].z),
+                         __uint_as_float(v[k].w));
     }
   }
   float ss = 0.f;
@@ -215,9 +225,18 @@ MKD void stage_norm(float *xs, const float *src, const uint16_t *emb, int n, con
 
 // Residual-stream input of layer l for sequence b, element i: the embedding
 // row of the token for layer 0, else the previous layer's output.
-MKD float resid_in(const MkProgram &P, const MkStep &S, int l, int b, int i, int tok) {
+MKD float resid_in(const MkProgram &P, const MkStep &S, int l, int b, int i, int tok, bool sent, bool &ok) {
   if (l == 0) return bf2f(P.embed[(size_t)tok * P.H + i]);
-  return ldc(P.xout + ((size_t)(l - 1) * P.B_max + b) * P.H + i);
+  return ldcp(P, P.xout + ((size_t)(l - 1) * P.B_max + b) * P.H + i, sent, ok);
+}
+
+// After staging: true (block-uniform) when some thread's poll failed (data
+// sentinels); with events, only the barrier the caller asks for (bar).
+template <bool SENT>
+MKD bool block_failed(bool ok, bool bar) {
+  if constexpr (SENT) return __syncthreads_or(!ok) != 0;
+  if (bar) __syncthreads();
+  return false;
 }
 
 MKD bool token_ok(const MkProgram &P, const MkStep &S, int b, int *tok) {
@@ -233,7 +252,8 @@ enum { MK_ST_ABORT = -1, MK_ST_QUIET = 0, MK_ST_SIGNAL = 1 };
 // Every op issues its first weight batches, then runs `wait` (the
 // instruction's dependency, for the first sequence only) and stages its
 // input vector; the weights load meanwhile.
-template <class Wait>
+// SENT: inputs are polled for data sentinels (no events between levels).
+template <bool SENT = false, class Wait>
 MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer;
   const int R = (P.nq + 2 * P.nkv) * P.d;
@@ -257,9 +277,10 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
       NormGain g;
       load_gain(g, W.attn_norm, H);
       if (b == 0 && !wait()) return false;
-      stage_norm(xs, l > 0 ? P.xout + ((size_t)(l - 1) * P.B_max + b) * H : nullptr,
-                 l == 0 ? P.embed + (size_t)tok * H : nullptr, H, g, P.eps, red);
-      return true;
+      bool ok = true;
+      stage_norm(P, xs, l > 0 ? P.xout + ((size_t)(l - 1) * P.B_max + b) * H : nullptr,
+                 l == 0 ? P.embed + (size_t)tok * H : nullptr, H, g, P.eps, red, SENT, ok);
+      return !block_failed<SENT>(ok, false);
     }, [&](int g0, const float *acc) {
       if ((mk_tid() & 63) == 0)
 #pragma unroll
@@ -275,7 +296,7 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
 // ------------------------------------------------------ O projection + add
 // U: 16-byte pieces per row and lane in one load batch (1 when the op runs
 // inside the gate/up instruction's prologue and must leave registers free)
-template <int U = 4, class Wait>
+template <bool SENT = false, int U = 4, class Wait>
 MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.nq * P.d;
   float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
@@ -292,10 +313,13 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
     const bool ok = gemv_rows<4, U>(K, n, xs, xs + K + 64, [&](int r) { return W.wo + (size_t)(r0 + r) * K; },
                                     [&]() -> bool {
                                       if (b == 0 && !wait()) return false;
-                                      for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = resid_in(P, S, l, b, r0 + i, tok);
-                                      stage_vec(xs, a, K);
-                                      __syncthreads();
-                                      return true;
+                                      bool ok2 = true;
+                                      stage_vec(P, xs, a, K, SENT, ok2);
+                                      // the residual rows are written before the attention output
+                                      // they are added to exists, but are polled all the same
+                                      for (int i = mk_tid(); i < n; i += MK_BLOCK)
+                                        res[i] = resid_in(P, S, l, b, r0 + i, tok, SENT, ok2);
+                                      return !block_failed<SENT>(ok2, true);
                                     },
                                     [&](int g0, const float *acc) {
                                       if ((mk_tid() & 63) == 0)
@@ -312,7 +336,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
 // ------------------------------------------- gate/up + SiLU (norm prologue)
 // before(): runs once the first weight batches are in flight and before the
 // wait (false aborts); the paired O projection runs there.
-template <class Wait, class Before>
+template <bool SENT = false, class Wait, class Before>
 MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait, Before &before) {
   const int H = P.H, l = in.layer;
   float *xs = smem, *red = smem + H;
@@ -329,8 +353,9 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
           load_gain(g, W.mlp_norm, H);
           if (b == 0 && !before()) return false;
           if (b == 0 && !wait()) return false;
-          stage_norm(xs, x, nullptr, H, g, P.eps, red);
-          return true;
+          bool ok2 = true;
+          stage_norm(P, xs, x, nullptr, H, g, P.eps, red, SENT, ok2);
+          return !block_failed<SENT>(ok2, false);
         },
         [&](int g0, const float *acc) {
           if ((mk_tid() & 63) == 0)
@@ -348,7 +373,7 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
 }
 
 // ------------------------------------------------ down projection + add
-template <class Wait>
+template <bool SENT = false, class Wait>
 MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer, K = P.I;
   float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
@@ -361,10 +386,10 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
     const bool ok = gemv_rows<4, 4>(K, n, xs, xs + K + 64, [&](int r) { return W.wd + (size_t)(r0 + r) * K; },
                                     [&]() -> bool {
                                       if (b == 0 && !wait()) return false;
-                                      for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = ldc(xm + r0 + i);
-                                      stage_vec(xs, h, K);
-                                      __syncthreads();
-                                      return true;
+                                      bool ok2 = true;
+                                      stage_vec(P, xs, h, K, SENT, ok2);
+                                      for (int i = mk_tid(); i < n; i += MK_BLOCK) res[i] = ldcp(P, xm + r0 + i, SENT, ok2);
+                                      return !block_failed<SENT>(ok2, true);
                                     },
                                     [&](int g0, const float *acc) {
                                       if ((mk_tid() & 63) == 0)
@@ -427,7 +452,7 @@ MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   return MK_ST_QUIET;
 }
 
-template <class Wait>
+template <bool SENT = false, class Wait>
 MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, Wait &wait) {
   const int H = P.H, L = P.L, V = P.V;
   const int tid = mk_tid(), lane = tid & 63, wave = tid >> 6;
@@ -445,8 +470,9 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
       NormGain g;
       load_gain(g, P.final_norm, H);
       if (b == 0 && !wait()) return false;
-      stage_norm(xs, x, nullptr, H, g, P.eps, red);
-      return true;
+      bool ok2 = true;
+      stage_norm(P, xs, x, nullptr, H, g, P.eps, red, SENT, ok2);
+      return !block_failed<SENT>(ok2, false);
     };
     const bool ok = gemv_rows<4, 4>(H, n, xs, xs + H + 64, [&](int r) { return Wlm + (size_t)(r0 + r) * H; }, pro,
                                     [&](int g0, const float *acc) {

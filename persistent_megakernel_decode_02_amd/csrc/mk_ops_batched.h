@@ -498,7 +498,7 @@ MKD bool attn_ticket(const MkProgram &P, const MkStep &S, const MkInstr &in, int
   return last != 0;
 }
 
-template <int D, class Wait>
+template <int D, bool SENT, class Wait>
 MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait &wait) {
   constexpr int KS = D / 32, NT = D / 16, DQ = D / 4, HALF = D / 2, CPR = D / 8, CPL = D / 16;
   constexpr int VROW = 2 * D + 16;  // bytes per value row in LDS (+16: the gathers' four rows hit distinct banks)
@@ -540,23 +540,26 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   // RoPE on the group's queries (scaled) and the new key; the new value
   const float *cs = P.rope + (size_t)p * D;  // (cos, sin) pairs
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  // (sentinel mode: each word is polled until its producer has written it)
+  constexpr bool sent = SENT;
+  bool ok = true;
   for (int e = tid; e < G * HALF; e += MK_BLOCK) {
     const int j = e / HALF, i = e - j * HALF;
     const float *qh = qkv + (size_t)(g * G + j) * D;
-    const float a = ldc(qh + i), c = ldc(qh + i + HALF);
+    const float a = ldcp(P, qh + i, sent, ok), c = ldcp(P, qh + i + HALF, sent, ok);
     const float co = cs[2 * i], si = cs[2 * i + 1];
     qs[j * D + i] = (a * co - c * si) * qscale;
     qs[j * D + i + HALF] = (c * co + a * si) * qscale;
   }
   for (int i = tid; i < HALF; i += MK_BLOCK) {
     const float *kh = qkv + (size_t)(nq + g) * D;
-    const float a = ldc(kh + i), c = ldc(kh + i + HALF);
+    const float a = ldcp(P, kh + i, sent, ok), c = ldcp(P, kh + i + HALF, sent, ok);
     const float co = cs[2 * i], si = cs[2 * i + 1];
     kn[i] = f2bf(a * co - c * si);
     kn[i + HALF] = f2bf(c * co + a * si);
   }
-  for (int i = tid; i < D; i += MK_BLOCK) vn[i] = f2bf(ldc(qkv + (size_t)(nq + nkv + g) * D + i));
-  __syncthreads();
+  for (int i = tid; i < D; i += MK_BLOCK) vn[i] = f2bf(ldcp(P, qkv + (size_t)(nq + nkv + g) * D + i, sent, ok));
+  if (block_failed<SENT>(ok, true)) return MK_ST_ABORT;
 
   if (t0 <= p && p < t1)
     for (int i = tid; i < D; i += MK_BLOCK) {
@@ -709,9 +712,9 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   return MK_ST_SIGNAL;
 }
 
-template <class Wait>
+template <bool SENT = false, class Wait>
 MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait &wait) {
-  return P.d == 64 ? op_attn_d<64>(P, S, in, s_flag, wait) : op_attn_d<128>(P, S, in, s_flag, wait);
+  return P.d == 64 ? op_attn_d<64, SENT>(P, S, in, s_flag, wait) : op_attn_d<128, SENT>(P, S, in, s_flag, wait);
 }
 
 // ----------------------------------------------------------------- dispatch
@@ -719,15 +722,18 @@ MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int
 // Run one instruction.  Every op starts the loads that do not depend on the
 // instruction's input event (weights; attention's cached keys and values),
 // then waits for the event inside.  `ts`
-// receives the time the wait ended when `timed`.
+// receives the time the wait ended when `timed`.  SENT: data-sentinel
+// synchronisation (one sequence per step; the ops poll their inputs and no
+// event is waited for).
+template <bool SENT>
 MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, bool timed,
                   uint64_t &ts) {
   auto wait = [&]() -> bool {
-    const bool ok = in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, s_flag);
+    const bool ok = SENT || in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, s_flag);
     if (timed) ts = __builtin_amdgcn_s_memrealtime();
     return ok;
   };
-  if (S.batch >= MK_MFMA_MIN_BATCH) {
+  if (!SENT && S.batch >= MK_MFMA_MIN_BATCH) {
     switch (in.op) {
       case MKOP_QKV: return op_qkv_b(P, S, in, wait);
       case MKOP_OPROJ: return op_oproj_b(P, S, in, wait);
@@ -738,15 +744,15 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
     }
   }
   switch (in.op) {
-    case MKOP_QKV: return op_qkv(P, S, in, smem, wait);
-    case MKOP_OPROJ: return op_oproj(P, S, in, smem, wait);
+    case MKOP_QKV: return op_qkv<SENT>(P, S, in, smem, wait);
+    case MKOP_OPROJ: return op_oproj<SENT>(P, S, in, smem, wait);
     case MKOP_GATEUP: {
       auto none = []() -> bool { return true; };
-      return op_gateup(P, S, in, smem, wait, none);
+      return op_gateup<SENT>(P, S, in, smem, wait, none);
     }
-    case MKOP_DOWN: return op_down(P, S, in, smem, wait);
-    case MKOP_LMHEAD: return op_lmhead(P, S, in, smem, s_flag, wait);
-    case MKOP_ATTN: return op_attn_mfma(P, S, in, s_flag, wait);
+    case MKOP_DOWN: return op_down<SENT>(P, S, in, smem, wait);
+    case MKOP_LMHEAD: return op_lmhead<SENT>(P, S, in, smem, s_flag, wait);
+    case MKOP_ATTN: return op_attn_mfma<SENT>(P, S, in, s_flag, wait);
     default: return MK_ST_ABORT;
   }
 }
@@ -758,25 +764,26 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
 // and O levels, which move little data.  Returns gate/up's status; O's
 // status is signalled here.  ts_o / te_o / ts_g: end of O's wait, end of O,
 // end of gate/up's wait (when `timed`).
+template <bool SENT>
 MKD int run_o_gateup(const MkProgram &P, const MkStep &S, const MkInstr &io, const MkInstr &ig, float *smem, int *s_flag,
                      bool timed, uint64_t &ts_o, uint64_t &te_o, uint64_t &ts_g) {
   auto wait_o = [&]() -> bool {
-    const bool ok = io.wait_ev < 0 || mk_wait(P, S, io.wait_ev, s_flag);
+    const bool ok = SENT || io.wait_ev < 0 || mk_wait(P, S, io.wait_ev, s_flag);
     if (timed) ts_o = __builtin_amdgcn_s_memrealtime();
     return ok;
   };
   auto wait_g = [&]() -> bool {
-    const bool ok = ig.wait_ev < 0 || mk_wait(P, S, ig.wait_ev, s_flag);
+    const bool ok = SENT || ig.wait_ev < 0 || mk_wait(P, S, ig.wait_ev, s_flag);
     if (timed) ts_g = __builtin_amdgcn_s_memrealtime();
     return ok;
   };
   auto o_first = [&]() -> bool {
-    const int st = op_oproj<1>(P, S, io, smem, wait_o);
+    const int st = op_oproj<SENT, 1>(P, S, io, smem, wait_o);
     if (st == MK_ST_ABORT) return false;
-    if (st == MK_ST_SIGNAL && io.sig_ev >= 0) mk_signal(P, S, io.sig_ev, io.sig_slot);
+    if (!SENT && st == MK_ST_SIGNAL && io.sig_ev >= 0) mk_signal(P, S, io.sig_ev, io.sig_slot);
     __syncthreads();
     if (timed) te_o = __builtin_amdgcn_s_memrealtime();
     return true;
   };
-  return op_gateup(P, S, ig, smem, wait_g, o_first);
+  return op_gateup<SENT>(P, S, ig, smem, wait_g, o_first);
 }

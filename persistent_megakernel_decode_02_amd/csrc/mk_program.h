@@ -23,6 +23,10 @@
 #define MK_LDS_TOTAL (160 * 1024)         // LDS of one gfx950 workgroup
 
 // batched projections of the homogeneous engine (bf16 MFMA, up to 16 sequences)
+// data-sentinel synchronisation: activation words hold this quiet-NaN
+// payload (which no arithmetic produces) until their producer writes them
+#define MK_SENTINEL 0x7FBADBADu
+
 // stream engine: streamer waves per workgroup (the last wave synchronises)
 #define MK_STREAMERS (MK_NWAVES - 1)
 
@@ -101,6 +105,10 @@ struct MkProgram {
   // activations occupy one contiguous block starting at qkv; in sentinel
   // mode a second copy (the other step parity) follows at +par_stride floats
   int64_t par_stride;
+  // homogeneous engine, sentinel mode: this record is the one for steps of
+  // one parity; `act_other` is the other parity's activation block, which a
+  // step resets to the sentinel for the step after it
+  float *act_other;
 
   // lists (device pointers into the workspace)
   const MkInstr *instr;        // CU-major

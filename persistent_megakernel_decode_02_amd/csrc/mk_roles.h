@@ -39,7 +39,6 @@
 
 #define MK_SYNCW MK_NLW                   // the sync/storer wave
 #define MK_QMAX 12                        // pages a loader keeps in flight (4 loads each, vmcnt <= 63)
-#define MK_SENTINEL 0x7FBADBADu           // quiet NaN payload the arithmetic never produces
 
 
 // LDS control block (start of dynamic LDS)

@@ -57,8 +57,11 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
   if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
   if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_STREAM) return MK_ERR_INVALID_ARG;
-  // data sentinels replace the events only inside one persistent launch
-  if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA) return MK_ERR_UNSUPPORTED;
+  // data sentinels replace the events only inside one persistent launch; the
+  // homogeneous engine polls them in its one-sequence ops only
+  if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA &&
+      !(o->exec_mode == MK_EXEC_FLAT && o->max_batch < MK_MFMA_MIN_BATCH))
+    return MK_ERR_UNSUPPORTED;
   // the stream engine runs one sequence per step; its sync wave holds a
   // normalised vector of at most 4096 floats in registers
   if (o->exec_mode == MK_EXEC_STREAM && (o->max_batch != 1 || s->hidden > 4096)) return MK_ERR_UNSUPPORTED;
@@ -189,6 +192,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
     return at;
   };
   y.prog = take(sizeof(MkProgram));
+  y.prog_odd = take(sizeof(MkProgram));
   y.instr = take(sizeof(MkInstr) * std::max<size_t>(p->instr.size(), 1));
   y.cu_begin = take(4 * (p->n_cu + 1));
   y.level_begin = take(4 * (p->n_levels + 1));

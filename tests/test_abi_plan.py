@@ -322,7 +322,18 @@ def test_stream_engine_limits():
     with pytest.raises(mk.MkError) as e:  # one sequence per step only
         mk.mk_plan(shape_struct(s), plan_opts(2, 1152, num_cus=256, exec_mode=mk.MK_EXEC_STREAM))
     assert e.value.code == mk.MK_ERR_UNSUPPORTED
-    with pytest.raises(mk.MkError) as e:  # data sentinels are the role engine's
+    with pytest.raises(mk.MkError) as e:  # data sentinels: role engine and one-sequence homogeneous engine
         mk.mk_plan(shape_struct(s), plan_opts(1, 1152, num_cus=256, exec_mode=mk.MK_EXEC_STREAM,
                                               sync_mode=mk.MK_SYNC_SENTINEL))
     assert e.value.code == mk.MK_ERR_UNSUPPORTED
+    with pytest.raises(mk.MkError) as e:  # the batched (MFMA) projections do not poll
+        mk.mk_plan(shape_struct(s), plan_opts(2, 1152, num_cus=256, exec_mode=mk.MK_EXEC_FLAT,
+                                              sync_mode=mk.MK_SYNC_SENTINEL))
+    assert e.value.code == mk.MK_ERR_UNSUPPORTED
+    plan = mk.mk_plan(shape_struct(s), plan_opts(1, 1152, num_cus=256, exec_mode=mk.MK_EXEC_FLAT,
+                                                 sync_mode=mk.MK_SYNC_SENTINEL))
+    try:
+        lay = mk.mk_plan_get_layout(plan)
+        assert lay[7] == lay[5] - lay[0] > 0  # a second activation copy, one per step parity
+    finally:
+        mk.mk_plan_destroy(plan)

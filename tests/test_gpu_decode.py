@@ -47,6 +47,7 @@ def test_device_is_mi355x():
 MODES = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
          "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
          "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
+         "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
          "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
          "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
 
@@ -63,7 +64,8 @@ def test_tiny_decode_matches_oracle(tiny_setup, mode):
 
 
 @pytest.mark.parametrize("group", [("mega-counter", "mega-flag", "mega-sentinel", "multi"),
-                                   ("flat-counter", "flat-flag"), ("stream-counter", "stream-flag")],
+                                   ("flat-counter", "flat-flag", "flat-sentinel"),
+                                   ("stream-counter", "stream-flag")],
                          ids=["roles", "flat", "stream"])
 def test_tiny_modes_bit_identical(tiny_setup, group):
     # the same ops under different synchronisation / launch schemes give the same bits
@@ -112,7 +114,8 @@ def llama1b():
 # sequence (128 passes), in every engine; the oracle trajectory is computed
 # once and shared by the modes whose tokens agree.
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("mode", ["stream-flag", "stream-counter", "flat-flag", "flat-counter", "mega-counter",
+@pytest.mark.parametrize("mode", ["stream-flag", "stream-counter", "flat-flag", "flat-counter", "flat-sentinel",
+                                  "mega-counter",
                                   "mega-flag", "mega-sentinel", "multi"])
 def test_llama1b_pos1024_full_sequence(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
@@ -128,7 +131,7 @@ def test_llama1b_pos1024_full_sequence(llama1b, mode):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("mode", ["stream-flag", "flat-flag", "mega-sentinel"])
+@pytest.mark.parametrize("mode", ["stream-flag", "flat-flag", "flat-sentinel", "mega-sentinel"])
 def test_llama1b_pos8192_full_sequence(llama1b, mode):
     # long context: split attention over the key range, 64 passes
     wl = si.WORKLOADS["llama1b_pos8192"]
@@ -208,7 +211,8 @@ def test_llama1b_batch16(llama1b, mode):
     print(f"kv exact fraction {check_kv(res, max_rel_err=1e-3):.5f}")
 
 
-@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter", "stream-flag"])
+@pytest.mark.parametrize("mode", ["mega-counter", "mega-sentinel", "multi", "flat-counter", "flat-sentinel",
+                                  "stream-flag"])
 def test_invalid_token_reports_input_error_and_poisons(tiny_setup, mode):
     w, gw, model = tiny_setup
     s = TINY.shape
