@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one 256 MiB device copy (the scale reference for HBM byte counters)")
+    ap.add_argument("--steps-per-launch", type=int, default=1,
+                    help="greedy passes per launch of the headline mode (> 1: multi-token persistent decode, "
+                         "homogeneous engine only)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -213,14 +216,27 @@ def main():
     logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
 
-    def timed(exec_mode, sync_mode, k, w_):
+    def timed(exec_mode, sync_mode, k, w_, chunk=1):
+        """k passes (after w_ warmup passes) as launches of `chunk` greedy
+        steps each (mk_decode_steps when chunk > 1)."""
         eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, kv_splits=args.kv_splits, sync_mode=sync_mode,
                             exec_mode=exec_mode, stream=stream)
+        lg_many = nx_many = None
+        if chunk > 1:
+            lg_many = torch.empty((chunk, B, s.vocab), dtype=torch.float32, device=dev)
+            nx_many = torch.empty((chunk, B), dtype=torch.int32, device=dev)
+
+        def run(n):
+            if chunk == 1:
+                for _ in range(n):
+                    eng.step(tokens, positions, kv, logits, nxt, advance=True)
+            else:
+                for i in range(0, n, chunk):
+                    eng.steps(tokens, positions, kv, lg_many, nx_many, min(chunk, n - i))
         try:
             tokens.copy_(torch.tensor(first, dtype=torch.int32))
             positions.copy_(torch.tensor(pos0, dtype=torch.int32))
-            for _ in range(w_):
-                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+            run(w_)
             rc, det = eng.device_error()
             if rc != 0:
                 raise RuntimeError(f"device error {rc} ({mk.mk_strerror(rc)}) detail {det}")
@@ -230,8 +246,7 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(k):
-                eng.step(tokens, positions, kv, logits, nxt, advance=True)
+            run(k)
             e1.record(stream)
             torch.cuda.synchronize()
             rc, det = eng.device_error()
@@ -261,8 +276,9 @@ def main():
              "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
              "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
              "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
-    ms, info = timed(*modes[args.mode], K, W)
-    log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms")
+    spl = max(1, args.steps_per_launch)
+    ms, info = timed(*modes[args.mode], K, W, spl)
+    log(f"[bench] {args.mode}: {K} passes in {ms:.3f} ms ({spl} per launch)")
     ms_per = ms / K
     passes_s = 1000.0 / ms_per * 1.0
     bpp = bytes_per_pass(s, [[p + t for p in pos0] for t in range(K)])
@@ -284,6 +300,17 @@ def main():
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[bench] {name}: {K} passes in {ms2:.3f} ms")
+        # multi-token persistent decode: all K passes in one launch
+        for name in ("flat-sentinel", "flat-flag"):
+            if B > 1 and name == "flat-sentinel":
+                continue
+            if name == args.mode and spl == K:
+                continue
+            ms2, _ = timed(*modes[name], K, W, K)
+            extras.setdefault("one_launch", {})[name] = {
+                "passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
+                "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "passes_per_launch": K}
+            log(f"[bench] {name}: {K} passes in one launch in {ms2:.3f} ms")
         if "multi" in extras and args.mode.startswith("mega"):
             extras["bubble_us_per_pass"] = round((extras["multi"]["ms_per_pass"] - ms_per) * 1000.0, 2)
             extras["launches_per_pass_multi"] = info.n_levels
@@ -370,7 +397,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "start_position": pos0[0], "passes": K,
                    "layers": s.n_layers, "hidden": s.hidden, "heads": f"{s.n_q_heads}/{s.n_kv_heads}",
                    "head_dim": s.head_dim, "ffn": s.ffn, "vocab": s.vocab, "tied": s.tied,
-                   "exec": args.mode},
+                   "exec": args.mode, "passes_per_launch": spl},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extras": extras,

@@ -234,6 +234,30 @@ int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
 int mk_decode_step(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
                    float *d_logits, int32_t *d_next_tokens, uint32_t flags, void *stream);
 
+/* Multi-token persistent decode: n_steps greedy steps in ONE launch of the
+ * homogeneous engine (MK_EXEC_FLAT, any sync mode).  The executive-summary
+ * page names what a kernel boundary costs per token (launch latency and the
+ * memory bubble while the next kernel's first loads travel, "Le problème");
+ * here the argmax of step t feeds step t + 1's embedding on the device and
+ * step t + 1 starts as soon as that token is published, inside the same
+ * persistent launch (megakernel page, section 2.1).  Step t reads
+ * d_tokens/d_positions as step t - 1 left them (the device advances both,
+ * as MK_ADVANCE does), appends cache slot positions[b] and writes its
+ * logits at d_logits + t * batch * vocab and, when d_next_tokens is not
+ * NULL, its tokens at d_next_tokens + t * batch.  Buffers: d_logits fp32
+ * [n_steps][batch][vocab]; d_next_tokens int32 [n_steps][batch]; others as
+ * for mk_decode_step.  Results are bit-identical to n_steps calls of
+ * mk_decode_step with MK_ADVANCE.  The context's epoch advances by n_steps.
+ * Host-side errors: those of mk_decode_step, MK_ERR_UNSUPPORTED (exec mode
+ * not MK_EXEC_FLAT), MK_ERR_INVALID_ARG (n_steps outside 1..MK_MAX_STEPS),
+ * MK_ERR_ALIGN (d_kv_cache not 128-byte aligned: an appended row must not
+ * share a cache line with rows an earlier step of the launch has read).
+ * Device-side errors as for mk_decode_step (a position reaching max_ctx
+ * stops the launch with MK_ERR_INPUT). */
+#define MK_MAX_STEPS 65536
+int mk_decode_steps(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
+                    float *d_logits, int32_t *d_next_tokens, int32_t n_steps, void *stream);
+
 /* Synchronise `stream`, read the device error word: MK_OK, MK_ERR_TIMEOUT or
  * MK_ERR_INPUT.  *detail (optional) receives the instruction/ CU code.  A
  * non-OK result poisons ctx (mk_decode_step returns MK_ERR_STATE) until

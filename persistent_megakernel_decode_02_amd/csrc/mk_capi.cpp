@@ -414,6 +414,7 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   P.ctr = (uint32_t *)(w + y.ctr);
   P.flags = (uint32_t *)(w + y.flags);
   P.tickets = (uint32_t *)(w + y.tickets);
+  P.lm_done = (uint32_t *)(w + y.lm_done);
   P.err = (int32_t *)(w + y.err);
   build_rope(p, c->rope);
   int rc = MK_OK;
@@ -480,8 +481,9 @@ int mk_load_weights(mk_ctx *c, const mk_weights *wt, void *stream) {
   return rc;
 }
 
-int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv, float *d_logits,
-                   int32_t *d_next, uint32_t flags, void *stream) {
+// Shared checks and step record of mk_decode_step / mk_decode_steps.
+static int step_record(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv, float *d_logits,
+                       int32_t *d_next, uint32_t flags, MkStep &S) {
   if (!c || !d_tokens || !d_positions || !d_kv || !d_logits) return MK_ERR_INVALID_ARG;
   if (c->poisoned) return MK_ERR_STATE;
   if (!c->weights) return MK_ERR_INVALID_ARG;
@@ -489,9 +491,9 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
   if (c->scratch_gen && !mk_scratch_current(c->device, c->scratch_gen)) return MK_ERR_STATE;
   if (batch < 1 || batch > c->plan.B) return MK_ERR_CTX_OVERFLOW;
   if (flags & ~MK_ADVANCE) return MK_ERR_INVALID_ARG;
-  if (!aligned16(d_kv) || ((uintptr_t)d_logits & 3u) || ((uintptr_t)d_tokens & 3u) || ((uintptr_t)d_positions & 3u))
+  if (!aligned16(d_kv) || ((uintptr_t)d_logits & 3u) || ((uintptr_t)d_tokens & 3u) || ((uintptr_t)d_positions & 3u) ||
+      ((uintptr_t)d_next & 3u))
     return MK_ERR_ALIGN;
-  MkStep S;
   std::memset(&S, 0, sizeof S);
   S.tokens = d_tokens;
   S.positions = d_positions;
@@ -501,19 +503,36 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
   S.batch = batch;
   S.epoch = (uint32_t)c->epoch;
   S.flags = flags;
+  S.n_steps = 1;
+  return MK_OK;
+}
+
+// Homogeneous engine: the program record of the step with this epoch, and
+// the other parity's (sentinel mode keeps one record per activation copy).
+static void flat_records(const mk_ctx *c, uint64_t epoch, const MkProgram **first, const MkProgram **other) {
+  const MkProgram *even = (const MkProgram *)(c->ws + c->plan.lay.prog);
+  const MkProgram *odd = (const MkProgram *)(c->ws + c->plan.lay.prog_odd);
+  const bool sent = c->plan.opts.sync_mode == MK_SYNC_SENTINEL;
+  *first = sent && (epoch & 1) ? odd : even;
+  *other = sent && !(epoch & 1) ? odd : even;
+}
+
+int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv, float *d_logits,
+                   int32_t *d_next, uint32_t flags, void *stream) {
+  MkStep S;
+  const int rc = step_record(c, d_tokens, d_positions, batch, d_kv, d_logits, d_next, flags, S);
+  if (rc != MK_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const MkProgram *dp = (const MkProgram *)(c->ws + c->plan.lay.prog);
   const int mode = c->plan.opts.exec_mode;
   if (mode == MK_EXEC_MEGA) {
-    S.multi = 0;
     if (mk_launch_role_mega(dp, S, c->plan.n_cu, c->plan.lds_bytes, st)) return MK_ERR_HIP;
   } else if (mode == MK_EXEC_FLAT) {
-    S.multi = 0;
-    const bool sent = c->plan.opts.sync_mode == MK_SYNC_SENTINEL;
-    if (sent && (c->epoch & 1)) dp = (const MkProgram *)(c->ws + c->plan.lay.prog_odd);
-    if (mk_launch_mega(dp, S, c->plan.n_cu, mega_lds(&c->plan), sent, st)) return MK_ERR_HIP;
+    const MkProgram *other = nullptr;
+    flat_records(c, c->epoch, &dp, &other);
+    if (mk_launch_mega(dp, other, S, c->plan.n_cu, mega_lds(&c->plan), c->plan.opts.sync_mode == MK_SYNC_SENTINEL, st))
+      return MK_ERR_HIP;
   } else if (mode == MK_EXEC_STREAM) {
-    S.multi = 0;
     if (mk_launch_stream(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
   } else {
     S.multi = 1;
@@ -524,6 +543,26 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
     }
   }
   c->epoch++;
+  return MK_OK;
+}
+
+int mk_decode_steps(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv, float *d_logits,
+                    int32_t *d_next, int32_t n_steps, void *stream) {
+  MkStep S;
+  const int rc = step_record(c, d_tokens, d_positions, batch, d_kv, d_logits, d_next, MK_ADVANCE, S);
+  if (rc != MK_OK) return rc;
+  if (c->plan.opts.exec_mode != MK_EXEC_FLAT) return MK_ERR_UNSUPPORTED;
+  if (n_steps < 1 || n_steps > MK_MAX_STEPS) return MK_ERR_INVALID_ARG;
+  // cache rows start on 128-byte lines, so no line holds both a row that a
+  // step appends and one that an earlier step of the launch has read
+  if ((uintptr_t)d_kv & 127u) return MK_ERR_ALIGN;
+  S.n_steps = n_steps;
+  const MkProgram *dp = nullptr, *other = nullptr;
+  flat_records(c, c->epoch, &dp, &other);
+  if (mk_launch_mega(dp, other, S, c->plan.n_cu, mega_lds(&c->plan), c->plan.opts.sync_mode == MK_SYNC_SENTINEL,
+                     (hipStream_t)stream))
+    return MK_ERR_HIP;
+  c->epoch += (uint64_t)n_steps;
   return MK_OK;
 }
 

@@ -57,12 +57,14 @@ __device__ __forceinline__ void trace_record(uint64_t *trace, int i, uint64_t tw
   r[4] = r[5] = r[6] = r[7] = 0;
 }
 
-// Homogeneous engine: every workgroup walks its CU's instruction list.  SENT:
-// data-sentinel synchronisation (the ops poll their inputs; no events), a
-// build of its own so the event build keeps its register allocation.
-template <bool SENT>
-MKD void mega_body(const MkProgram &P, const MkStep &S, float *smem, int *s_flag) {
-  if (mk_aborted(P)) return;
+// Homogeneous engine, one step: every workgroup walks its CU's instruction
+// list.  SENT: data-sentinel synchronisation (the ops poll their inputs; no
+// events), a build of its own so the event build keeps its register
+// allocation.  STEPS: one of several steps of a launch.  False when the
+// step is being aborted.
+template <bool SENT, bool STEPS>
+MKD bool mega_step(const MkProgram &P, const MkStep &S, float *smem, int *s_flag) {
+  if (mk_aborted(P)) return false;
   const int cu = blockIdx.x;
   if constexpr (SENT) {
     // this CU's share of the other parity's activations (read by the next
@@ -71,6 +73,10 @@ MKD void mega_body(const MkProgram &P, const MkStep &S, float *smem, int *s_flag
     const size_t lo = (size_t)cu * per, hi = min(lo + per, n);
     uint32_t *o = reinterpret_cast<uint32_t *>(P.act_other);
     for (size_t i = lo + threadIdx.x; i < hi; i += MK_BLOCK) stcu(o + i, MK_SENTINEL);
+    // within a launch the next step's producers write this copy once this
+    // step's tokens are out: the resets must have landed before any of this
+    // CU's outputs can let the step complete
+    if constexpr (STEPS) wait_vm();
   }
   const int i0 = cld(&P.cu_begin[cu]), i1 = cld(&P.cu_begin[cu + 1]);  // scalar: the list walk stays uniform
   uint64_t *const trace = P.trace;
@@ -83,7 +89,7 @@ MKD void mega_body(const MkProgram &P, const MkStep &S, float *smem, int *s_flag
       if (nx.op == MKOP_GATEUP && nx.layer == in.layer) {  // O and gate/up as one unit
         uint64_t te_o = 0, ts_g = 0;
         const int st = run_o_gateup<SENT>(P, S, in, nx, smem, s_flag, trace != nullptr, ts, te_o, ts_g);
-        if (st == MK_ST_ABORT) return;
+        if (st == MK_ST_ABORT) return false;
         if (!SENT && st == MK_ST_SIGNAL && nx.sig_ev >= 0) mk_signal(P, S, nx.sig_ev, nx.sig_slot);
         __syncthreads();
         if (trace && threadIdx.x == 0) {
@@ -95,24 +101,78 @@ MKD void mega_body(const MkProgram &P, const MkStep &S, float *smem, int *s_flag
       }
     }
     const int st = run_instr<SENT>(P, S, in, smem, s_flag, trace != nullptr, ts);
-    if (st == MK_ST_ABORT) return;
+    if (st == MK_ST_ABORT) return false;
     if (!SENT && st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
     __syncthreads();
     if (trace && threadIdx.x == 0) trace_record(trace, i, tw, ts, __builtin_amdgcn_s_memrealtime(), cu, S.epoch);
   }
+  return true;
 }
 
-extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_flag;
-  mega_body<false>(*Pp, S, smem, &s_flag);
+// Wait until the step with this epoch may start: the previous step's last
+// LM-head arriver has published its tokens (lm_done >= epoch).  Bounded by
+// the watchdog; false (uniformly) on a timeout or abort.
+MKD bool wait_prev_step(const MkProgram &P, uint32_t epoch, int *s_flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint64_t t0 = 0;
+    uint32_t spins = 0;
+    while ((int32_t)(ldcu(P.lm_done) - epoch) < 0) {
+      if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
+      __builtin_amdgcn_s_sleep(1);
+      if ((++spins & 31u) == 0) {
+        if (mk_aborted(P)) { ok = 0; break; }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)P.watchdog_ticks) {
+          mk_raise(P, MK_E_TIMEOUT, 0x40000);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    *s_flag = ok;
+  }
+  __syncthreads();
+  const int ok = *s_flag;
+  __syncthreads();
+  return ok != 0;
 }
 
-extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_mega_sent_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_flag;
-  mega_body<true>(*Pp, S, smem, &s_flag);
+// One launch runs S.n_steps greedy steps (STEPS) or one.  Step t has epoch
+// S.epoch + t, writes its logits at logits + t * batch * V and its tokens at
+// next + t * batch, and feeds its token back on the device for step t + 1,
+// which starts once that token is published.  In sentinel mode consecutive
+// steps alternate between the two activation copies: Pa is the record of the
+// first step's parity, Pb the other's.
+template <bool SENT, bool STEPS>
+MKD void mega_body(const MkProgram *Pa, const MkProgram *Pb, const MkStep &S, float *smem, int *s_flag) {
+  if constexpr (!STEPS) {
+    mega_step<SENT, false>(*Pa, S, smem, s_flag);
+  } else {
+    const int n = S.n_steps;
+    for (int t = 0; t < n; ++t) {
+      const MkProgram &P = (SENT && (t & 1)) ? *Pb : *Pa;
+      MkStep St = S;
+      St.epoch = S.epoch + (uint32_t)t;
+      St.logits = S.logits + (size_t)t * S.batch * P.V;
+      St.next = S.next ? S.next + (size_t)t * S.batch : nullptr;
+      St.flags = S.flags | 1u;  // MK_ADVANCE
+      if (t > 0 && !wait_prev_step(P, St.epoch, s_flag)) return;
+      if (!mega_step<SENT, true>(P, St, smem, s_flag)) return;
+    }
+  }
 }
+
+#define MK_MEGA_KERNEL(name, sent, steps)                                                                     \
+  extern "C" __global__ void __launch_bounds__(MK_BLOCK)                                                      \
+      name(const MkProgram *__restrict__ Pa, const MkProgram *__restrict__ Pb, MkStep S) {                   \
+    extern __shared__ __attribute__((aligned(16))) float smem[];                                              \
+    __shared__ int s_flag;                                                                                    \
+    mega_body<sent, steps>(Pa, Pb, S, smem, &s_flag);                                                         \
+  }
+MK_MEGA_KERNEL(mk_mega_kernel, false, false)
+MK_MEGA_KERNEL(mk_mega_sent_kernel, true, false)
+MK_MEGA_KERNEL(mk_mega_steps_kernel, false, true)
+MK_MEGA_KERNEL(mk_mega_sent_steps_kernel, true, true)
 
 // Stream engine (one sequence per step): waves 0..MK_NSW-1 stream projection
 // weights through register rings, wave MK_NSW synchronises; the waves meet
@@ -198,16 +258,20 @@ extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// Dynamic-LDS limit of each kernel, as last set in this process.  Launches
-// compare against it and call hipFuncSetAttribute only when it differs (a
-// context binds it once; a later occupancy query may have changed it).
-static int g_lds_set[5] = {-1, -1, -1, -1, -1};
+// Persistent kernels and the dynamic-LDS limit of each, as last set in this
+// process.  Launches compare against it and call hipFuncSetAttribute only
+// when it differs (a context binds it once; a later occupancy query may have
+// changed it).
+static const void *const g_kernels[] = {(const void *)mk_mega_kernel,           (const void *)mk_role_mega_kernel,
+                                        (const void *)mk_role_level_kernel,     (const void *)mk_stream_kernel,
+                                        (const void *)mk_mega_sent_kernel,      (const void *)mk_mega_steps_kernel,
+                                        (const void *)mk_mega_sent_steps_kernel};
+static constexpr int MK_NKERNELS = (int)(sizeof g_kernels / sizeof g_kernels[0]);
+static int g_lds_set[MK_NKERNELS] = {-1, -1, -1, -1, -1, -1, -1};
 static int lds_slot(const void *fn) {
-  return fn == (const void *)mk_mega_kernel        ? 0
-         : fn == (const void *)mk_role_mega_kernel ? 1
-         : fn == (const void *)mk_stream_kernel    ? 3
-         : fn == (const void *)mk_mega_sent_kernel ? 4
-                                                   : 2;
+  for (int i = 0; i < MK_NKERNELS; ++i)
+    if (g_kernels[i] == fn) return i;
+  return 0;
 }
 static hipError_t set_lds(const void *fn, int lds) {
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -217,19 +281,24 @@ static hipError_t set_lds(const void *fn, int lds) {
 static inline bool ensure_lds(const void *fn, int lds) {
   return g_lds_set[lds_slot(fn)] == lds || set_lds(fn, lds) == hipSuccess;
 }
+static const void *mega_fn(bool sentinel, bool steps) {
+  return steps ? (sentinel ? (const void *)mk_mega_sent_steps_kernel : (const void *)mk_mega_steps_kernel)
+               : (sentinel ? (const void *)mk_mega_sent_kernel : (const void *)mk_mega_kernel);
+}
 
 // The dynamic-LDS limit of a kernel is set once, when a context is bound
 // (mk_prepare_launch), not on every step: the step path is only the launch.
 static const void *exec_kernel(int exec_mode, int sync_mode) {
-  if (exec_mode == MKEXEC_FLAT && sync_mode == MKSYNC_SENTINEL) return (const void *)mk_mega_sent_kernel;
-  return exec_mode == MKEXEC_FLAT     ? (const void *)mk_mega_kernel
-         : exec_mode == MKEXEC_MEGA   ? (const void *)mk_role_mega_kernel
+  if (exec_mode == MKEXEC_FLAT) return mega_fn(sync_mode == MKSYNC_SENTINEL, false);
+  return exec_mode == MKEXEC_MEGA     ? (const void *)mk_role_mega_kernel
          : exec_mode == MKEXEC_STREAM ? (const void *)mk_stream_kernel
                                       : (const void *)mk_role_level_kernel;
 }
 
 int mk_prepare_launch(int exec_mode, int sync_mode, int lds) {
-  return set_lds(exec_kernel(exec_mode, sync_mode), lds) == hipSuccess ? 0 : -1;
+  if (set_lds(exec_kernel(exec_mode, sync_mode), lds) != hipSuccess) return -1;
+  if (exec_mode == MKEXEC_FLAT && set_lds(mega_fn(sync_mode == MKSYNC_SENTINEL, true), lds) != hipSuccess) return -1;
+  return 0;
 }
 
 int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
@@ -247,11 +316,13 @@ int mk_occupancy(int exec_mode, int sync_mode, int lds, int *blocks_per_cu) {
   return 0;
 }
 
-int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, bool sentinel, hipStream_t s) {
-  const void *fn = sentinel ? (const void *)mk_mega_sent_kernel : (const void *)mk_mega_kernel;
+int mk_launch_mega(const MkProgram *d_prog, const MkProgram *d_prog_other, const MkStep &st, int n_cu, int lds,
+                   bool sentinel, hipStream_t s) {
+  const bool steps = st.n_steps > 1;
+  const void *fn = mega_fn(sentinel, steps);
   if (!ensure_lds(fn, lds)) return -1;
-  if (sentinel) hipLaunchKernelGGL(mk_mega_sent_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
-  else hipLaunchKernelGGL(mk_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  void *args[] = {(void *)&d_prog, (void *)&d_prog_other, (void *)&st};
+  if (hipLaunchKernel(fn, dim3(n_cu), dim3(MK_BLOCK), args, (size_t)lds, s) != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -15,7 +15,10 @@ bool mk_scratch_current(int dev, uint64_t gen);
 int mk_prepare_launch(int exec_mode, int sync_mode, int lds);  // once per context: dynamic LDS limit
 int mk_launch_stream(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
 int mk_occupancy(int exec_mode, int sync_mode, int lds, int *blocks_per_cu);  // persistent kernels of the exec modes
-int mk_launch_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, bool sentinel, hipStream_t s);
+// homogeneous engine: d_prog is the first step's record, d_prog_other the
+// other parity's (sentinel mode); st.n_steps > 1 selects the multi-step build
+int mk_launch_mega(const MkProgram *d_prog, const MkProgram *d_prog_other, const MkStep &st, int n_cu, int lds,
+                   bool sentinel, hipStream_t s);
 int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_occupancy_role(int lds, int *blocks_per_cu);

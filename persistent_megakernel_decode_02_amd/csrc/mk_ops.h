@@ -239,8 +239,10 @@ MKD bool block_failed(bool ok, bool bar) {
   return false;
 }
 
+// Tokens and positions are read and written device-coherently: within a
+// multi-step launch the previous step's last arriver (on any CU) wrote them.
 MKD bool token_ok(const MkProgram &P, const MkStep &S, int b, int *tok) {
-  int t = S.tokens[b];
+  int t = ldci(S.tokens + b);
   *tok = t;
   return t >= 0 && t < P.V;
 }
@@ -442,12 +444,17 @@ MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
     }
     if (lane == 0) {
       if (ix == 0x7fffffff) ix = 0;  // every logit NaN: fall back to token 0
-      if (S.next) S.next[b] = ix;
+      if (S.next) stci(S.next + b, ix);
       if (S.flags & 1u) {
-        S.tokens[b] = ix;
-        S.positions[b] = S.positions[b] + 1;
+        stci(S.tokens + b, ix);
+        stci(S.positions + b, ldci(S.positions + b) + 1);
       }
     }
+  }
+  if (last) {  // the step's tokens are out: publish its epoch
+    wait_vm();
+    __syncthreads();
+    if (tid == 0) stcu(P.lm_done, S.epoch + 1u);
   }
   return MK_ST_QUIET;
 }

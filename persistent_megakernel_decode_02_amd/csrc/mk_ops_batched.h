@@ -280,7 +280,7 @@ MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wa
   if (l == 0) {
     if (!tokens_ok_all(P, S)) return MK_ST_ABORT;
     const int b = mk_tid() >> 5;
-    const BEmbSrc src{b < nb ? P.embed + (size_t)S.tokens[b] * H : nullptr};
+    const BEmbSrc src{b < nb ? P.embed + (size_t)ldci(S.tokens + b) * H : nullptr};
     if (!bgemm(src, H, nt, W.attn_norm, P.eps, rowptr, fin, wait)) return MK_ST_ABORT;
   } else {
     if (!bgemm(bact(P.xout + (size_t)(l - 1) * P.B_max * H, nb, H), H, nt, W.attn_norm, P.eps, rowptr, fin, wait))
@@ -304,7 +304,7 @@ MKD int op_oproj_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait 
         const int b = b0 + j;
         if (b < nb) {
           const int row = r0 + v;
-          const float res = l == 0 ? bf2f(P.embed[(size_t)S.tokens[b] * H + row])
+          const float res = l == 0 ? bf2f(P.embed[(size_t)ldci(S.tokens + b) * H + row])
                                    : ldc(P.xout + ((size_t)(l - 1) * P.B_max + b) * H + row);
           stc(out + (size_t)b * H + row, res + a[j]);
         }
@@ -508,7 +508,7 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   // a sequence slot beyond this step's batch: no position, no queries, no
   // cache access; the unit only keeps the event and ticket protocol
   if (b >= S.batch) return NS == 1 ? MK_ST_SIGNAL : attn_ticket(P, S, in, s_flag) ? MK_ST_SIGNAL : MK_ST_QUIET;
-  const int p = S.positions[b];
+  const int p = ldci(S.positions + b);
   if (p < 0 || p >= P.max_ctx) {
     if (tid == 0) mk_raise(P, MK_E_INPUT, 1000 + b);
     return MK_ST_ABORT;
@@ -561,10 +561,12 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
   for (int i = tid; i < D; i += MK_BLOCK) vn[i] = f2bf(ldcp(P, qkv + (size_t)(nq + nkv + g) * D + i, sent, ok));
   if (block_failed<SENT>(ok, true)) return MK_ST_ABORT;
 
+  // the appended row is stored device-coherently (as bf16 pairs): a later
+  // step of the same launch may read it from another XCD
   if (t0 <= p && p < t1)
-    for (int i = tid; i < D; i += MK_BLOCK) {
-      Kc[(size_t)p * D + i] = kn[i];
-      Vc[(size_t)p * D + i] = vn[i];
+    for (int i = tid; i < HALF; i += MK_BLOCK) {
+      stcu(reinterpret_cast<uint32_t *>(Kc + (size_t)p * D) + i, (uint32_t)kn[2 * i] | ((uint32_t)kn[2 * i + 1] << 16));
+      stcu(reinterpret_cast<uint32_t *>(Vc + (size_t)p * D) + i, (uint32_t)vn[2 * i] | ((uint32_t)vn[2 * i + 1] << 16));
     }
 
   // queries as the B operand (column = head), high and low parts

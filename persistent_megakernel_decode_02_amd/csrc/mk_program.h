@@ -109,6 +109,9 @@ struct MkProgram {
   // one parity; `act_other` is the other parity's activation block, which a
   // step resets to the sentinel for the step after it
   float *act_other;
+  // epoch+1 of the last step whose greedy tokens are merged (multi-step
+  // launches: a step starts once the previous one has produced its token)
+  uint32_t *lm_done;
 
   // lists (device pointers into the workspace)
   const MkInstr *instr;        // CU-major
@@ -153,6 +156,7 @@ struct MkStep {
   uint32_t flags;  // MK_ADVANCE
   int32_t multi;   // 1: launched per level (no waits/signals)
   int32_t level;   // multi-launch: level this launch runs
+  int32_t n_steps; // homogeneous engine: greedy steps run by this launch (>= 1)
 };
 
 // Device code of the role engine reads the program and step records through

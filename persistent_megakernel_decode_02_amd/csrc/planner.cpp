@@ -216,6 +216,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.ctr = take(4 * std::max(p->n_events, 1));
   y.flags = take(4 * std::max(p->n_flags, 1));
   y.tickets = take(4 * std::max(p->n_tickets, 1));
+  y.lm_done = take(4);
   y.err = take(16);
   y.sync_end = o;
   y.total = o;

@@ -102,6 +102,22 @@ class Engine:
         if rc != mk.MK_OK:
             raise mk.MkError(rc, "mk_decode_step")
 
+    def steps(self, tokens: torch.Tensor, positions: torch.Tensor, kv: torch.Tensor, logits: torch.Tensor,
+              next_tokens: Optional[torch.Tensor], n_steps: int):
+        """Enqueue n_steps greedy steps as one persistent launch (no host sync);
+        logits [n_steps][batch][vocab], next_tokens [n_steps][batch]."""
+        assert tokens.dtype == torch.int32 and positions.dtype == torch.int32
+        assert kv.dtype == torch.bfloat16 and logits.dtype == torch.float32
+        assert kv.numel() * 2 == self.kv_bytes and kv.is_contiguous()
+        b = tokens.numel()
+        assert positions.numel() == b and logits.numel() >= n_steps * b * self.shape.vocab
+        assert next_tokens is None or next_tokens.numel() >= n_steps * b
+        rc = mk.mk_decode_steps(self.ctx, tokens.data_ptr(), positions.data_ptr(), b, kv.data_ptr(),
+                                logits.data_ptr(), next_tokens.data_ptr() if next_tokens is not None else None,
+                                n_steps, self.stream.cuda_stream)
+        if rc != mk.MK_OK:
+            raise mk.MkError(rc, "mk_decode_steps")
+
     def device_error(self):
         return mk.mk_get_device_error(self.ctx, self.stream.cuda_stream)
 

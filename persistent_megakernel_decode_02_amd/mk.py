@@ -31,6 +31,7 @@ MK_ERR_SCRATCH = -12
 MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
 MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM = 0, 1, 2, 3
 MK_ADVANCE = 1
+MK_MAX_STEPS = 65536
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6
 
 GRIDSYNC_VARIANTS = {0: "cooperative_grid_sync", 1: "counter_release_acquire", 2: "counter_write_through",
@@ -105,6 +106,8 @@ SIGNATURES = {
     "mk_load_weights": (C.c_int, [C.c_void_p, C.POINTER(mk_weights), C.c_void_p]),
     "mk_decode_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_uint32, C.c_void_p]),
+    "mk_decode_steps": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_int32, C.c_void_p]),
     "mk_get_device_error": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
     "mk_ctx_reset": (C.c_int, [C.c_void_p, C.c_void_p]),
     "mk_ctx_epoch": (C.c_int64, [C.c_void_p]),
@@ -228,6 +231,13 @@ def mk_decode_step(ctx, d_tokens: int, d_positions: int, batch: int, d_kv: int, 
     return load_library().mk_decode_step(ctx, C.c_void_p(d_tokens), C.c_void_p(d_positions), batch,
                                          C.c_void_p(d_kv), C.c_void_p(d_logits),
                                          C.c_void_p(d_next) if d_next else None, flags, C.c_void_p(stream))
+
+
+def mk_decode_steps(ctx, d_tokens: int, d_positions: int, batch: int, d_kv: int, d_logits: int,
+                    d_next: Optional[int], n_steps: int, stream: int) -> int:
+    return load_library().mk_decode_steps(ctx, C.c_void_p(d_tokens), C.c_void_p(d_positions), batch,
+                                          C.c_void_p(d_kv), C.c_void_p(d_logits),
+                                          C.c_void_p(d_next) if d_next else None, n_steps, C.c_void_p(stream))
 
 
 def mk_get_device_error(ctx, stream: int):

@@ -57,6 +57,7 @@ class RunResult:
     kv_ref: np.ndarray
     kv_written: np.ndarray          # bool mask of slots written by the steps
     logits_last: np.ndarray
+    logits_all: List[np.ndarray]    # fp32 logits of every step [step] -> [B][V]
     kv_before: np.ndarray
     kv_idx: tuple                   # flat indices (into the cache) of every appended value
     kv_unrounded: np.ndarray        # the oracle's unrounded value at each of them
@@ -245,7 +246,7 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
                 idx.append(flat.ravel())
                 unr.append(vals.ravel())
                 bnd.append(np.broadcast_to(bb[:, None, None], (L, nkv, d)).ravel())
-    return RunResult(g_tokens, max(errs), errs, near, kv_gpu, orun.kv_ref, written, g_logits[-1], kv0,
+    return RunResult(g_tokens, max(errs), errs, near, kv_gpu, orun.kv_ref, written, g_logits[-1], g_logits, kv0,
                      np.concatenate(idx), np.concatenate(unr), np.concatenate(bnd), rel)
 
 
@@ -287,3 +288,54 @@ def check_kv(res: RunResult, max_rel_err: float = 1e-4):
     before = res.kv_before.reshape(-1)[res.kv_idx]
     assert np.mean(g != before) > 0.99 and np.mean(r != before) > 0.99
     return exact
+
+
+@dataclasses.dataclass
+class MultiStepResult:
+    tokens: List[List[int]]       # [step][b]
+    logits: np.ndarray            # fp32 [step][B][V]
+    kv_gpu: np.ndarray            # cache bits after the run
+    launches: int
+
+
+def run_multistep(wl: si.Workload, n_steps: int, chunk: int, exec_mode=mk.MK_EXEC_FLAT,
+                  sync_mode=mk.MK_SYNC_FLAG, kv_splits: int = 0, weights=None, gpu_weights=None,
+                  master: int = 0) -> MultiStepResult:
+    """The same free-running greedy decode as run_decode (same seeded inputs,
+    prompt-free workloads), but `chunk` steps per launch through
+    mk_decode_steps: the device feeds each step's token to the next."""
+    assert not wl.prompt_len
+    s = wl.shape
+    B = wl.batch
+    gw = gpu_weights if gpu_weights is not None else engine.to_gpu(
+        weights if weights is not None else si.make_weights(s, master=master))
+    pos0 = wl.positions0(master)
+    prefill = pos0 if wl.start_pos != 0 else [0] * B
+    kv_cpu = si.make_kv_cache(s, B, wl.max_ctx, prefill, master=master)
+    first = si.workload_tokens(wl, master)
+    if len(first) < B:
+        first = (first * B)[:B]
+    eng = engine.Engine(s, gw, max_batch=B, max_ctx=wl.max_ctx, kv_splits=kv_splits, sync_mode=sync_mode,
+                        exec_mode=exec_mode)
+    try:
+        kv = kv_cpu.to("cuda:0")
+        toks = torch.tensor(first[:B], dtype=torch.int32, device="cuda:0")
+        pos = torch.tensor(pos0, dtype=torch.int32, device="cuda:0")
+        logits = torch.empty((n_steps, B, s.vocab), dtype=torch.float32, device="cuda:0")
+        nxt = torch.empty((n_steps, B), dtype=torch.int32, device="cuda:0")
+        done, launches = 0, 0
+        while done < n_steps:
+            n = min(chunk, n_steps - done)
+            eng.steps(toks, pos, kv, logits[done:], nxt[done:], n)
+            launches += 1
+            done += n
+        rc, detail = eng.device_error()
+        assert rc == 0, f"device error {rc} ({mk.mk_strerror(rc)}), detail {detail}"
+        assert [int(v) for v in pos.cpu().numpy()] == [p + n_steps for p in pos0]
+        torch.cuda.synchronize()
+        res = MultiStepResult([[int(v) for v in row] for row in nxt.cpu().numpy()], logits.cpu().numpy(),
+                              kv.view(torch.int16).cpu().numpy().view(np.uint16), launches)
+        assert [int(v) for v in toks.cpu().numpy()] == res.tokens[-1]
+        return res
+    finally:
+        eng.close()
