@@ -144,6 +144,15 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
             "context_lengths": [min(pos0), max(pos0)]}
 
 
+def kernel_name(mode: str, per_launch: int) -> str:
+    """The kernel that runs a mode's passes (the one profiled for it)."""
+    if mode in ("flat-counter", "flat-flag", "flat-sentinel"):
+        sent = "_sent" if mode == "flat-sentinel" else ""
+        return f"mk_mega{sent}_steps_kernel" if per_launch > 1 else f"mk_mega{sent}_kernel"
+    return {"multi": "mk_role_level_kernel", "flat-levels": "mk_flat_level_kernel",
+            "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(mode, "mk_role_mega_kernel")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -151,8 +160,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
-                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag", "flat-sentinel",
-                             "stream-counter", "stream-flag"],
+                    choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
+                             "flat-sentinel", "flat-levels", "stream-counter", "stream-flag"],
                     help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
                          "homogeneous engine with flag events)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
@@ -216,9 +225,10 @@ def main():
     logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
 
-    def timed(exec_mode, sync_mode, k, w_, chunk=1):
+    def timed(exec_mode, sync_mode, k, w_, chunk=1, graph=False):
         """k passes (after w_ warmup passes) as launches of `chunk` greedy
-        steps each (mk_decode_steps when chunk > 1)."""
+        steps each (mk_decode_steps when chunk > 1), or as replays of one
+        captured step (graph: MK_EXEC_FLAT_MULTI)."""
         eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, kv_splits=args.kv_splits, sync_mode=sync_mode,
                             exec_mode=exec_mode, stream=stream)
         lg_many = nx_many = None
@@ -226,8 +236,13 @@ def main():
             lg_many = torch.empty((chunk, B, s.vocab), dtype=torch.float32, device=dev)
             nx_many = torch.empty((chunk, B), dtype=torch.int32, device=dev)
 
+        g = eng.graph(tokens, positions, kv, logits, nxt, advance=True) if graph else None
+
         def run(n):
-            if chunk == 1:
+            if g is not None:
+                for _ in range(n):
+                    g.launch()
+            elif chunk == 1:
                 for _ in range(n):
                     eng.step(tokens, positions, kv, logits, nxt, advance=True)
             else:
@@ -267,6 +282,8 @@ def main():
                 np.savez(args.trace, desc=arr, t=tr[: eng.n_instr * 8].cpu().numpy().reshape(-1, 8))
             return ms, eng.info
         finally:
+            if g is not None:
+                g.close()
             eng.close()
 
     modes = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk.MK_EXEC_MEGA, mk.MK_SYNC_FLAG),
@@ -274,6 +291,7 @@ def main():
              "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
              "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
              "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
+             "flat-levels": (mk.MK_EXEC_FLAT_MULTI, mk.MK_SYNC_COUNTER),
              "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
              "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
     spl = max(1, args.steps_per_launch)
@@ -285,10 +303,8 @@ def main():
     achieved = bpp / (ms_per * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.mode),
-            "kernel": {"multi": "mk_role_level_kernel", "flat-counter": "mk_mega_kernel", "flat-flag": "mk_mega_kernel",
-                       "flat-sentinel": "mk_mega_kernel", "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(
-                args.mode, "mk_role_mega_kernel"),
-            "bytes_per_launch": bpp if args.mode != "multi" else None}
+            "kernel": kernel_name(args.mode, spl),
+            "bytes_per_launch": bpp * spl if args.mode not in ("multi", "flat-levels") else None}
 
     extras = {"plan": {"cus": info.num_cus, "instructions": info.n_instructions, "levels": info.n_levels,
                        "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
@@ -311,6 +327,19 @@ def main():
                 "passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),
                 "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "passes_per_launch": K}
             log(f"[bench] {name}: {K} passes in one launch in {ms2:.3f} ms")
+        # the homogeneous engine's multi-launch baseline captured as a hipGraph:
+        # the same launches without the host's per-launch cost
+        if "flat-levels" in extras:
+            ms2, _ = timed(*modes["flat-levels"], K, W, graph=True)
+            extras["flat-levels-graph"] = {"passes_per_s": round(1000.0 * K / ms2, 2),
+                                           "ms_per_pass": round(ms2 / K, 5),
+                                           "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] flat-levels-graph: {K} passes in {ms2:.3f} ms")
+            if args.mode.startswith("flat"):
+                extras["bubble_us_per_pass"] = round((extras["flat-levels-graph"]["ms_per_pass"] - ms_per) * 1000.0, 2)
+                extras["host_launch_us_per_pass"] = round(
+                    (extras["flat-levels"]["ms_per_pass"] - extras["flat-levels-graph"]["ms_per_pass"]) * 1000.0, 2)
+                extras["launches_per_pass_levels"] = info.n_levels + 1
         if "multi" in extras and args.mode.startswith("mega"):
             extras["bubble_us_per_pass"] = round((extras["multi"]["ms_per_pass"] - ms_per) * 1000.0, 2)
             extras["launches_per_pass_multi"] = info.n_levels

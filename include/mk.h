@@ -69,17 +69,22 @@ enum { MK_SYNC_COUNTER = 0, /* one monotonic counter per event, atomic add */
        MK_SYNC_FLAG = 1,    /* one epoch flag per producer, plain stores */
        MK_SYNC_SENTINEL = 2 /* the data is the signal: activation words start as a
                                NaN sentinel pattern each step and consumers poll
-                               the data itself (MK_EXEC_MEGA only) */ };
+                               the data itself (MK_EXEC_MEGA; MK_EXEC_FLAT with
+                               max_batch 1) */ };
 enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step, loader /
                                sync-storer / compute wavefronts, LDS page ring */
        MK_EXEC_MULTI = 1,   /* the same role-specialised ops, one launch per
                                dependency level (kernel boundaries) */
        MK_EXEC_FLAT = 2,    /* one persistent launch with homogeneous waves: all
                                waves load, wait and compute each instruction */
-       MK_EXEC_STREAM = 3   /* one persistent launch, one sequence per step:
+       MK_EXEC_STREAM = 3,  /* one persistent launch, one sequence per step:
                                streamer waves keep projection weights in flight
                                across instructions, one wave synchronises
-                               (MK_SYNC_COUNTER or MK_SYNC_FLAG, max_batch 1) */ };
+                               (MK_SYNC_COUNTER or MK_SYNC_FLAG, max_batch 1) */
+       MK_EXEC_FLAT_MULTI = 4 /* MK_EXEC_FLAT's plan and ops, one launch per
+                               dependency level with no waits: the multi-kernel
+                               baseline of the homogeneous engine (also
+                               capturable as a hipGraph, mk_graph_create) */ };
 
 typedef struct {
   int32_t max_batch;   /* sequences per step: 1..16 (MK_EXEC_FLAT), 1 (MK_EXEC_STREAM),
@@ -219,8 +224,9 @@ int mk_load_weights(mk_ctx *ctx, const mk_weights *w, void *stream);
  * into d_tokens and increments d_positions on the device, so steps can be
  * enqueued back to back without the host.  Enqueued on `stream`; device-side
  * input errors (token or position out of range) and watchdog expiries are
- * reported by mk_get_device_error.  MK_EXEC_MEGA and MK_EXEC_FLAT: exactly
- * one kernel launch; MK_EXEC_MULTI: one launch per dependency level.
+ * reported by mk_get_device_error.  MK_EXEC_MEGA, MK_EXEC_FLAT and
+ * MK_EXEC_STREAM: exactly one kernel launch; MK_EXEC_MULTI and
+ * MK_EXEC_FLAT_MULTI: one launch per dependency level.
  * Layouts: d_tokens, d_positions int32[batch] (sequence b uses sequence
  * slot b of the cache); d_kv_cache as mk_plan_sizes describes; d_logits
  * fp32 [batch][vocab]; d_next_tokens int32[batch].  Sequence slots
@@ -257,6 +263,28 @@ int mk_decode_step(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t
 #define MK_MAX_STEPS 65536
 int mk_decode_steps(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
                     float *d_logits, int32_t *d_next_tokens, int32_t n_steps, void *stream);
+
+/* The per-level build (MK_EXEC_FLAT_MULTI) of one decode step captured into
+ * a hipGraph: the baseline that separates the host's launch cost from the
+ * kernel-boundary bubble.  The megakernel page (section 2.2) sets the
+ * persistent kernel apart from a captured graph, which still ends and starts
+ * a kernel at every node; the executive-summary page ("Le problème") names
+ * the costs a boundary keeps even when the graph removes the host's launch
+ * latency (the drain of the finishing kernel, the next kernel's cold start).
+ * mk_graph_create captures one step on these buffers and flags (MK_ADVANCE
+ * or 0) as n_levels kernel nodes plus one node that advances the step's
+ * epoch on the device; mk_graph_launch replays it on `stream` (one step,
+ * results identical to mk_decode_step with the same arguments); steps
+ * enqueued by other calls in between are accounted for before the replay.
+ * The graph owns a small device record of the step (allocated at creation);
+ * destroy graphs before their context.  Errors: those of mk_decode_step's
+ * host checks, MK_ERR_UNSUPPORTED (exec mode not MK_EXEC_FLAT_MULTI),
+ * MK_ERR_HIP (allocation, capture or instantiation failed). */
+typedef struct mk_graph_s mk_graph; /* opaque, host memory, owned by the library */
+int mk_graph_create(mk_ctx *ctx, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv_cache,
+                    float *d_logits, int32_t *d_next_tokens, uint32_t flags, void *stream, mk_graph **out);
+int mk_graph_launch(mk_graph *graph, void *stream);
+void mk_graph_destroy(mk_graph *graph);
 
 /* Synchronise `stream`, read the device error word: MK_OK, MK_ERR_TIMEOUT or
  * MK_ERR_INPUT.  *detail (optional) receives the instruction/ CU code.  A

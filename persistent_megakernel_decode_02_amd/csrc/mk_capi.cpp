@@ -36,7 +36,8 @@ static inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; 
 static inline int mega_lds(const mk_plan_t *p) { return std::max(p->lds_bytes, 80 * 1024 + 256); }
 // dynamic LDS a plan's kernel is launched with
 static inline int launch_lds(const mk_plan_t *p) {
-  return p->opts.exec_mode == MK_EXEC_FLAT || p->opts.exec_mode == MK_EXEC_STREAM ? mega_lds(p) : p->lds_bytes;
+  const int m = p->opts.exec_mode;
+  return m == MK_EXEC_FLAT || m == MK_EXEC_FLAT_MULTI || m == MK_EXEC_STREAM ? mega_lds(p) : p->lds_bytes;
 }
 
 extern "C" {
@@ -341,7 +342,7 @@ int mk_ctx_create_scratch(const mk_plan_t *plan, void *stream, mk_ctx **out) {
 
 static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_bytes, int dev, hipStream_t st,
                          uint64_t scratch_gen, mk_ctx **out) {
-  if (plan->opts.exec_mode != MK_EXEC_MULTI) {
+  if (plan->opts.exec_mode != MK_EXEC_MULTI && plan->opts.exec_mode != MK_EXEC_FLAT_MULTI) {
     int n_dev_cu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&n_dev_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_ERR_HIP;
     const int occ = mk_occupancy(plan->opts.exec_mode, plan->opts.sync_mode, launch_lds(plan), &per_cu);
@@ -534,6 +535,13 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
       return MK_ERR_HIP;
   } else if (mode == MK_EXEC_STREAM) {
     if (mk_launch_stream(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
+  } else if (mode == MK_EXEC_FLAT_MULTI) {
+    S.multi = 1;
+    for (int lv = 0; lv < c->plan.n_levels; ++lv) {
+      S.level = lv;
+      const int nb = c->plan.level_begin[lv + 1] - c->plan.level_begin[lv];
+      if (mk_launch_flat_level(dp, nullptr, S, nb, mega_lds(&c->plan), st)) return MK_ERR_HIP;
+    }
   } else {
     S.multi = 1;
     for (int lv = 0; lv < c->plan.n_levels; ++lv) {
@@ -565,6 +573,84 @@ int mk_decode_steps(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t 
   c->epoch += (uint64_t)n_steps;
   return MK_OK;
 }
+
+// A step of the per-level build captured into a hipGraph.  The captured
+// launches read the step record from device memory (d_step): a replay cannot
+// change kernel arguments, and the epoch moves on the device (the graph's
+// last node increments it).
+struct mk_graph_s {
+  mk_ctx *ctx = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  MkStep *d_step = nullptr;
+  uint64_t dev_epoch = 0;  // the epoch d_step holds once the last replay has run
+  ~mk_graph_s() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (d_step) (void)hipFree(d_step);
+  }
+};
+
+int mk_graph_create(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t batch, void *d_kv, float *d_logits,
+                    int32_t *d_next, uint32_t flags, void *stream, mk_graph **out) {
+  if (!out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  MkStep S;
+  int rc = step_record(c, d_tokens, d_positions, batch, d_kv, d_logits, d_next, flags, S);
+  if (rc != MK_OK) return rc;
+  if (c->plan.opts.exec_mode != MK_EXEC_FLAT_MULTI) return MK_ERR_UNSUPPORTED;
+  mk_graph *g = new (std::nothrow) mk_graph_s();
+  if (!g) return MK_ERR_INVALID_ARG;
+  g->ctx = c;
+  hipStream_t st = (hipStream_t)stream, cs = nullptr;
+  S.multi = 1;
+  rc = hipMalloc((void **)&g->d_step, sizeof(MkStep)) == hipSuccess ? MK_OK : MK_ERR_HIP;
+  if (rc == MK_OK && (hipMemcpyAsync(g->d_step, &S, sizeof S, hipMemcpyHostToDevice, st) != hipSuccess ||
+                      hipStreamSynchronize(st) != hipSuccess))
+    rc = MK_ERR_HIP;
+  g->dev_epoch = c->epoch;
+  if (rc == MK_OK && hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) rc = MK_ERR_HIP;
+  if (rc == MK_OK && hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) rc = MK_ERR_HIP;
+  if (rc == MK_OK) {
+    const MkProgram *dp = (const MkProgram *)(c->ws + c->plan.lay.prog);
+    for (int lv = 0; lv < c->plan.n_levels && rc == MK_OK; ++lv) {
+      S.level = lv;
+      const int nb = c->plan.level_begin[lv + 1] - c->plan.level_begin[lv];
+      if (mk_launch_flat_level(dp, g->d_step, S, nb, mega_lds(&c->plan), cs)) rc = MK_ERR_HIP;
+    }
+    if (rc == MK_OK && mk_launch_step_end(g->d_step, cs)) rc = MK_ERR_HIP;
+    hipGraph_t graph = nullptr;
+    if (hipStreamEndCapture(cs, &graph) != hipSuccess) rc = MK_ERR_HIP;
+    g->graph = graph;
+  }
+  if (rc == MK_OK && hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0) != hipSuccess) rc = MK_ERR_HIP;
+  if (cs) (void)hipStreamDestroy(cs);
+  if (rc != MK_OK) {
+    delete g;
+    return rc;
+  }
+  *out = g;
+  return MK_OK;
+}
+
+int mk_graph_launch(mk_graph *g, void *stream) {
+  if (!g) return MK_ERR_INVALID_ARG;
+  mk_ctx *c = g->ctx;
+  if (c->poisoned) return MK_ERR_STATE;
+  if (c->scratch_gen && !mk_scratch_current(c->device, c->scratch_gen)) return MK_ERR_STATE;
+  hipStream_t st = (hipStream_t)stream;
+  // other steps ran on the context since this graph's last replay: bring the
+  // device record's epoch up to date first (a fill kernel, outside the graph)
+  if (g->dev_epoch != (uint64_t)c->epoch &&
+      mk_launch_fill(&g->d_step->epoch, (uint32_t)c->epoch, 1, st))
+    return MK_ERR_HIP;
+  if (hipGraphLaunch(g->exec, st) != hipSuccess) return MK_ERR_HIP;
+  c->epoch++;
+  g->dev_epoch = c->epoch;
+  return MK_OK;
+}
+
+void mk_graph_destroy(mk_graph *g) { delete g; }
 
 int mk_get_device_error(mk_ctx *c, void *stream, int32_t *detail) {
   if (!c) return MK_ERR_INVALID_ARG;

@@ -174,6 +174,29 @@ MK_MEGA_KERNEL(mk_mega_sent_kernel, true, false)
 MK_MEGA_KERNEL(mk_mega_steps_kernel, false, true)
 MK_MEGA_KERNEL(mk_mega_sent_steps_kernel, true, true)
 
+// The homogeneous engine's ops, one launch per dependency level: block i
+// runs instruction i of level S.level, with no waits and no signals (the
+// kernel boundaries order the levels).  Sd, when set, is the step record in
+// device memory (graph replays, where the record cannot change per launch).
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_flat_level_kernel(const MkProgram *__restrict__ Pp,
+                                                                           const MkStep *__restrict__ Sd, MkStep S0) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag;
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const MkStep S = Sd ? cld(Sd) : S0;
+  const int idx = cld(&P.level_list[cld(&P.level_begin[S0.level]) + blockIdx.x]);
+  const MkInstr in = cld(&P.instr[idx]);
+  uint64_t ts = 0;
+  run_instr<false, true>(P, S, in, smem, &s_flag, false, ts);
+}
+
+// end of a captured step: the device copy of the step record moves to the
+// next epoch (one thread, a plain vector store)
+extern "C" __global__ void mk_step_end_kernel(MkStep *Sd) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) Sd->epoch = Sd->epoch + 1u;
+}
+
 // Stream engine (one sequence per step): waves 0..MK_NSW-1 stream projection
 // weights through register rings, wave MK_NSW synchronises; the waves meet
 // only at attention instructions, which all of them run together.
@@ -265,9 +288,9 @@ extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
 static const void *const g_kernels[] = {(const void *)mk_mega_kernel,           (const void *)mk_role_mega_kernel,
                                         (const void *)mk_role_level_kernel,     (const void *)mk_stream_kernel,
                                         (const void *)mk_mega_sent_kernel,      (const void *)mk_mega_steps_kernel,
-                                        (const void *)mk_mega_sent_steps_kernel};
+                                        (const void *)mk_mega_sent_steps_kernel, (const void *)mk_flat_level_kernel};
 static constexpr int MK_NKERNELS = (int)(sizeof g_kernels / sizeof g_kernels[0]);
-static int g_lds_set[MK_NKERNELS] = {-1, -1, -1, -1, -1, -1, -1};
+static int g_lds_set[MK_NKERNELS] = {-1, -1, -1, -1, -1, -1, -1, -1};
 static int lds_slot(const void *fn) {
   for (int i = 0; i < MK_NKERNELS; ++i)
     if (g_kernels[i] == fn) return i;
@@ -290,6 +313,7 @@ static const void *mega_fn(bool sentinel, bool steps) {
 // (mk_prepare_launch), not on every step: the step path is only the launch.
 static const void *exec_kernel(int exec_mode, int sync_mode) {
   if (exec_mode == MKEXEC_FLAT) return mega_fn(sync_mode == MKSYNC_SENTINEL, false);
+  if (exec_mode == MKEXEC_FLAT_MULTI) return (const void *)mk_flat_level_kernel;
   return exec_mode == MKEXEC_MEGA     ? (const void *)mk_role_mega_kernel
          : exec_mode == MKEXEC_STREAM ? (const void *)mk_stream_kernel
                                       : (const void *)mk_role_level_kernel;
@@ -329,6 +353,19 @@ int mk_launch_mega(const MkProgram *d_prog, const MkProgram *d_prog_other, const
 int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
   if (!ensure_lds((const void *)mk_role_mega_kernel, lds)) return -1;
   hipLaunchKernelGGL(mk_role_mega_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_flat_level(const MkProgram *d_prog, const MkStep *d_step, const MkStep &st, int n_blocks, int lds,
+                         hipStream_t s) {
+  if (n_blocks <= 0) return 0;
+  if (!ensure_lds((const void *)mk_flat_level_kernel, lds)) return -1;
+  hipLaunchKernelGGL(mk_flat_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, d_step, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_step_end(MkStep *d_step, hipStream_t s) {
+  hipLaunchKernelGGL(mk_step_end_kernel, dim3(1), dim3(64), 0, s, d_step);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

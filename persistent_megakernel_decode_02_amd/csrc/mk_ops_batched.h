@@ -727,11 +727,13 @@ MKD int op_attn_mfma(const MkProgram &P, const MkStep &S, const MkInstr &in, int
 // receives the time the wait ended when `timed`.  SENT: data-sentinel
 // synchronisation (one sequence per step; the ops poll their inputs and no
 // event is waited for).
-template <bool SENT>
+// NOWAIT: launched per dependency level (the kernel boundary orders the
+// levels; nothing is waited for).
+template <bool SENT, bool NOWAIT = false>
 MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, bool timed,
                   uint64_t &ts) {
   auto wait = [&]() -> bool {
-    const bool ok = SENT || in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, s_flag);
+    const bool ok = SENT || NOWAIT || in.wait_ev < 0 || mk_wait(P, S, in.wait_ev, s_flag);
     if (timed) ts = __builtin_amdgcn_s_memrealtime();
     return ok;
   };

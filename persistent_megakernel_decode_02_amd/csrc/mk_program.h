@@ -47,7 +47,7 @@
 #define MK_FA_LDS (MK_FA_WP + MK_NWAVES * MK_MAX_GROUP * 130 * 4)
 
 enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
-enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2, MKEXEC_STREAM = 3 };
+enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2, MKEXEC_STREAM = 3, MKEXEC_FLAT_MULTI = 4 };
 
 enum MkOp : int32_t {
   MKOP_QKV = 1,

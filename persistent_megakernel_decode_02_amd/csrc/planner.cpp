@@ -56,7 +56,7 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
   if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
-  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_STREAM) return MK_ERR_INVALID_ARG;
+  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_FLAT_MULTI) return MK_ERR_INVALID_ARG;
   // data sentinels replace the events only inside one persistent launch; the
   // homogeneous engine polls them in its one-sequence ops only
   if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA &&
@@ -266,7 +266,8 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // gate/up stream the other CUs started during attention, and would hold
   // up the O and gate/up events
   int og_cus = n_cu;
-  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_STREAM) && B == 1 &&
+  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI || opts->exec_mode == MK_EXEC_STREAM) &&
+      B == 1 &&
       (int64_t)B * nkv * S < n_cu / 2)
     og_cus = n_cu - B * nkv * S;
   const int rg = (int)((ceil_div(I, og_cus) + 3) / 4 * 4), ro = (int)ceil_div(H, og_cus);
@@ -464,7 +465,7 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
       delete p;
       return MK_ERR_UNSUPPORTED;
     }
-  } else if (opts->exec_mode == MK_EXEC_FLAT) {
+  } else if (opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI) {
     p->lds_bytes = lds_requirement(p);
     // the one-sequence ops stage a normalised vector of at most 16 floats per thread
     if (p->lds_bytes > MK_LDS_TOTAL || shape->hidden > 16 * MK_BLOCK) {

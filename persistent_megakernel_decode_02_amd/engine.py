@@ -118,6 +118,28 @@ class Engine:
         if rc != mk.MK_OK:
             raise mk.MkError(rc, "mk_decode_steps")
 
+    def graph(self, tokens: torch.Tensor, positions: torch.Tensor, kv: torch.Tensor, logits: torch.Tensor,
+              next_tokens: Optional[torch.Tensor] = None, advance: bool = False):
+        """Capture one step on these buffers as a hipGraph (MK_EXEC_FLAT_MULTI);
+        returns an object with launch() and close()."""
+        b = tokens.numel()
+        g = mk.mk_graph_create(self.ctx, tokens.data_ptr(), positions.data_ptr(), b, kv.data_ptr(),
+                               logits.data_ptr(), next_tokens.data_ptr() if next_tokens is not None else None,
+                               mk.MK_ADVANCE if advance else 0, self.stream.cuda_stream)
+        eng = self
+
+        class _Graph:
+            def launch(self):
+                rc = mk.mk_graph_launch(g, eng.stream.cuda_stream)
+                if rc != mk.MK_OK:
+                    raise mk.MkError(rc, "mk_graph_launch")
+
+            def close(self):
+                torch.cuda.synchronize(eng.device)
+                mk.mk_graph_destroy(g)
+
+        return _Graph()
+
     def device_error(self):
         return mk.mk_get_device_error(self.ctx, self.stream.cuda_stream)
 

@@ -29,7 +29,7 @@ MK_ERR_UNSUPPORTED = -11
 MK_ERR_SCRATCH = -12
 
 MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
-MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM = 0, 1, 2, 3
+MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM, MK_EXEC_FLAT_MULTI = 0, 1, 2, 3, 4
 MK_ADVANCE = 1
 MK_MAX_STEPS = 65536
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6
@@ -108,6 +108,10 @@ SIGNATURES = {
                                  C.c_void_p, C.c_uint32, C.c_void_p]),
     "mk_decode_steps": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_int32, C.c_void_p]),
+    "mk_graph_create": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_uint32, C.c_void_p, C.POINTER(C.c_void_p)]),
+    "mk_graph_launch": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "mk_graph_destroy": (None, [C.c_void_p]),
     "mk_get_device_error": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
     "mk_ctx_reset": (C.c_int, [C.c_void_p, C.c_void_p]),
     "mk_ctx_epoch": (C.c_int64, [C.c_void_p]),
@@ -238,6 +242,24 @@ def mk_decode_steps(ctx, d_tokens: int, d_positions: int, batch: int, d_kv: int,
     return load_library().mk_decode_steps(ctx, C.c_void_p(d_tokens), C.c_void_p(d_positions), batch,
                                           C.c_void_p(d_kv), C.c_void_p(d_logits),
                                           C.c_void_p(d_next) if d_next else None, n_steps, C.c_void_p(stream))
+
+
+def mk_graph_create(ctx, d_tokens: int, d_positions: int, batch: int, d_kv: int, d_logits: int,
+                    d_next: Optional[int], flags: int, stream: int):
+    out = C.c_void_p()
+    _check(load_library().mk_graph_create(ctx, C.c_void_p(d_tokens), C.c_void_p(d_positions), batch,
+                                          C.c_void_p(d_kv), C.c_void_p(d_logits),
+                                          C.c_void_p(d_next) if d_next else None, flags, C.c_void_p(stream),
+                                          C.byref(out)), "mk_graph_create")
+    return out
+
+
+def mk_graph_launch(graph, stream: int) -> int:
+    return load_library().mk_graph_launch(graph, C.c_void_p(stream))
+
+
+def mk_graph_destroy(graph):
+    load_library().mk_graph_destroy(graph)
 
 
 def mk_get_device_error(ctx, stream: int):

@@ -111,12 +111,15 @@ def _fill_unwritten(kv: torch.Tensor, prefill: List[int], bits: int):
 def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mode=mk.MK_SYNC_COUNTER,
                kv_splits: int = 0, weights=None, gpu_weights=None, model: Optional[orc.Model] = None,
                advance: bool = True, master: int = 0, batch: Optional[int] = None,
-               max_batch: Optional[int] = None, kv_fill: Optional[int] = None) -> RunResult:
+               max_batch: Optional[int] = None, kv_fill: Optional[int] = None, use_graph: bool = False,
+               eager_steps=()) -> RunResult:
     """Decode n_steps passes of `wl` on the GPU, then check every step against
     the oracle.  batch / max_batch: sequences per step and the plan's bound
     (defaults: the workload's batch for both); sequence slots past `batch`
     keep their prefill and must stay untouched.  kv_fill: bf16 bits stored in
-    every not-yet-written cache slot of both sides."""
+    every not-yet-written cache slot of both sides.  use_graph: the step is
+    captured once as a hipGraph (MK_EXEC_FLAT_MULTI) and replayed, except the
+    steps listed in eager_steps, which are enqueued by mk_decode_step."""
     s = wl.shape
     B = batch or wl.batch
     Bmax = max_batch or B
@@ -149,6 +152,7 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
         pos = torch.tensor(pos0, dtype=torch.int32, device="cuda:0")
         logits = torch.empty((B, s.vocab), dtype=torch.float32, device="cuda:0")
         nxt = torch.empty(B, dtype=torch.int32, device="cuda:0")
+        graph = eng.graph(toks, pos, kv, logits, nxt, advance=advance) if use_graph else None
         feeds, poss, g_tokens, g_logits, g_kv = [], [], [], [], []
         cur_tok = list(toks.cpu().numpy())
         cur_pos = list(pos0)
@@ -158,7 +162,10 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
                 feed = [prompt[t]]
                 toks.copy_(torch.tensor(feed, dtype=torch.int32))
             epoch = mk.mk_ctx_epoch(eng.ctx)
-            eng.step(toks, pos, kv, logits, nxt, advance=advance)
+            if graph is not None and t not in eager_steps:
+                graph.launch()
+            else:
+                eng.step(toks, pos, kv, logits, nxt, advance=advance)
             rc, detail = eng.device_error()
             assert rc == 0, f"device error {rc} ({mk.mk_strerror(rc)}), detail {detail}, step {t}"
             g_next = [int(v) for v in nxt.cpu().numpy()]
@@ -180,6 +187,8 @@ def run_decode(wl: si.Workload, n_steps: int, exec_mode=mk.MK_EXEC_MEGA, sync_mo
             cur_pos = [p + 1 for p in cur_pos]
         torch.cuda.synchronize()
         kv_gpu = kv.view(torch.int16).cpu().numpy().view(np.uint16)
+        if graph is not None:
+            graph.close()
     finally:
         eng.close()
 

@@ -48,6 +48,7 @@ MODES = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk
          "mega-sentinel": (mk.MK_EXEC_MEGA, mk.MK_SYNC_SENTINEL), "multi": (mk.MK_EXEC_MULTI, mk.MK_SYNC_COUNTER),
          "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
          "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
+         "flat-levels": (mk.MK_EXEC_FLAT_MULTI, mk.MK_SYNC_COUNTER),
          "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
          "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
 
@@ -115,7 +116,7 @@ def llama1b():
 # once and shared by the modes whose tokens agree.
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("mode", ["stream-flag", "stream-counter", "flat-flag", "flat-counter", "flat-sentinel",
-                                  "mega-counter",
+                                  "flat-levels", "mega-counter",
                                   "mega-flag", "mega-sentinel", "multi"])
 def test_llama1b_pos1024_full_sequence(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
