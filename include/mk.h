@@ -156,6 +156,34 @@ int mk_plan_export(const mk_plan_t *plan, mk_instr_desc *out, size_t cap, size_t
  * every wait is eventually satisfied and every read follows its producers.
  * MK_OK or MK_ERR_PLAN. */
 int mk_plan_simulate(const mk_plan_t *plan, int32_t n_trials, uint64_t seed);
+
+/* Event normalisation of a task graph, the scheme the megakernel page's Q&A
+ * attributes to MPK ("En quoi le mécanisme de MPK diffère-t-il de simples
+ * compteurs ?"): every task waits for at most one event and triggers at most
+ * one; tasks with the same predecessors share one event and events that
+ * share a predecessor are fused; events and tasks are then numbered
+ * breadth-first, so the tasks one event releases are contiguous in `order`.
+ * mk_plan_create derives its plans' events this way from the slices each
+ * instruction reads and writes (the splits of an attention unit are one task).
+ * Input: n_tasks; raw predecessors of task t are pred_list[pred_begin[t] ..
+ * pred_begin[t+1]) (CSR, duplicates and transitively implied edges allowed:
+ * the latter are removed); rank (optional, int64[n_tasks]) breaks ties in the
+ * breadth-first order (smaller first; NULL: task index); flags bit 0 skips
+ * the transitive reduction (tests).  Output arrays of n_tasks entries:
+ * wait_event / trigger_event (-1: none), trigger_slot (the task's index among
+ * its event's triggers), event_count[e] (triggers of event e; entries below
+ * *n_events are written), order (tasks in breadth-first order).  Errors:
+ * MK_ERR_INVALID_ARG (NULL array, bad offsets or task id), MK_ERR_PLAN (a
+ * cycle among the edges, or a fused event that one of its own waiters would
+ * have to precede).  Host only; no allocation is kept. */
+#define MK_NORM_NO_REDUCTION 1u
+int mk_events_normalize(int32_t n_tasks, const int32_t *pred_begin, const int32_t *pred_list, const int64_t *rank,
+                        uint32_t flags, int32_t *wait_event, int32_t *trigger_event, int32_t *trigger_slot,
+                        int32_t *event_count, int32_t *order, int32_t *n_events);
+/* The plan's breadth-first instruction order (indices as mk_plan_export
+ * numbers them): the order a global work queue hands instructions out in.
+ * Writes min(cap, count) entries; *n_out receives the count. */
+int mk_plan_get_queue(const mk_plan_t *plan, int32_t *out, size_t cap, size_t *n_out);
 void mk_plan_destroy(mk_plan_t *plan);
 
 /* Bind a plan to caller-owned device workspace (d_workspace, at least the

@@ -139,6 +139,13 @@ int mk_plan_export(const mk_plan_t *p, mk_instr_desc *out, size_t cap, size_t *n
   return MK_OK;
 }
 
+int mk_plan_get_queue(const mk_plan_t *p, int32_t *out, size_t cap, size_t *n_out) {
+  if (!p) return MK_ERR_INVALID_ARG;
+  if (n_out) *n_out = p->queue.size();
+  for (size_t i = 0; out && i < cap && i < p->queue.size(); ++i) out[i] = p->queue[i];
+  return MK_OK;
+}
+
 void mk_plan_destroy(mk_plan_t *p) { delete p; }
 
 // Host-side test hook: replace the instruction list of a plan with `n`
@@ -185,6 +192,7 @@ int mk_plan_set_instructions(mk_plan_t *p, const mk_instr_desc *d, size_t n) {
   }
   p->instr.swap(ins);
   p->instr_cu.swap(cus);
+  p->queue.clear();  // indices of the previous instruction array
   mk_plan_finalize_lists(p);
   mk_plan_compute_layout(p);
   p->validated = mk_plan_check(p, false, 0, 0) == MK_OK;

@@ -15,23 +15,13 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <map>
 #include <random>
 
 namespace {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
-struct Events {
-  int L, nkv;
-  int per() const { return nkv + 4; }
-  int qkv(int l, int g) const { return l * per() + g; }
-  int attn(int l) const { return l * per() + nkv; }
-  int o(int l) const { return l * per() + nkv + 1; }
-  int gu(int l) const { return l * per() + nkv + 2; }
-  int down(int l) const { return l * per() + nkv + 3; }
-  int count() const { return L * per(); }
-};
 
 enum { LV_QKV = 0, LV_ATTN = 1, LV_O = 2, LV_GU = 3, LV_DOWN = 4, LV_PER_LAYER = 5 };
 
@@ -252,8 +242,6 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   }
   p->S = S;
 
-  Events ev{L, nkv};
-  p->n_events = ev.count();
   p->n_levels = LV_PER_LAYER * L + 1;
 
   // rows per instruction
@@ -277,8 +265,6 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   p->n_tickets = (S > 1 ? L * B * nkv : 0) + 1;
   const int lm_ticket = p->n_tickets - 1;
 
-  // event trigger counts and flag slots
-  p->ev_count.assign(p->n_events, 0);
   auto blank = [](int op, int layer, int level) {
     MkInstr in;
     std::memset(&in, 0, sizeof in);
@@ -320,22 +306,10 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     const int base = l * LV_PER_LAYER;
     // QKV row slices (each inside one head, hence one kv group)
     {
-      std::vector<int> slot(nkv, 0);
       for (int r0 = 0; r0 < R; r0 += rq) {
         MkInstr in = blank(MKOP_QKV, l, base + LV_QKV);
         in.r0 = r0;
         in.r1 = std::min(R, r0 + rq);
-        int g;
-        if (r0 < nq * d)
-          g = (r0 / d) / p->G;
-        else if (r0 < (nq + nkv) * d)
-          g = (r0 - nq * d) / d;
-        else
-          g = (r0 - (nq + nkv) * d) / d;
-        in.wait_ev = l > 0 ? ev.down(l - 1) : -1;
-        in.sig_ev = ev.qkv(l, g);
-        in.sig_slot = slot[g]++;
-        p->ev_count[in.sig_ev]++;
         lvl.push_back({in, 2.0 * (in.r1 - in.r0) * H});
         wbytes += 2.0 * (in.r1 - in.r0) * H;
       }
@@ -351,13 +325,9 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
             in.r1 = g;
             in.split = sp;
             in.nsplit = S;
-            in.wait_ev = ev.qkv(l, g);
-            in.sig_ev = ev.attn(l);
-            in.sig_slot = b * nkv + g;
             in.ticket = S > 1 ? (l * B + b) * nkv + g : -1;
             lvl.push_back({in, 4.0 * d * (double)ceil_div(p->max_ctx, S)});
           }
-      p->ev_count[ev.attn(l)] = B * nkv;
       const size_t first = p->instr_cu.size();
       assign(lvl);
       std::fill(busy.begin(), busy.end(), 0);
@@ -365,15 +335,10 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     }
     // O projection + residual
     {
-      int k = 0;
-      for (int r0 = 0; r0 < H; r0 += ro, ++k) {
+      for (int r0 = 0; r0 < H; r0 += ro) {
         MkInstr in = blank(MKOP_OPROJ, l, base + LV_O);
         in.r0 = r0;
         in.r1 = std::min(H, r0 + ro);
-        in.wait_ev = ev.attn(l);
-        in.sig_ev = ev.o(l);
-        in.sig_slot = k;
-        p->ev_count[in.sig_ev]++;
         lvl.push_back({in, 2.0 * (in.r1 - in.r0) * nq * d});
         wbytes += 2.0 * (in.r1 - in.r0) * nq * d;
       }
@@ -381,15 +346,10 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     }
     // gate/up + SiLU (RMSNorm prologue)
     {
-      int k = 0;
-      for (int r0 = 0; r0 < I; r0 += rg, ++k) {
+      for (int r0 = 0; r0 < I; r0 += rg) {
         MkInstr in = blank(MKOP_GATEUP, l, base + LV_GU);
         in.r0 = r0;
         in.r1 = std::min(I, r0 + rg);
-        in.wait_ev = ev.o(l);
-        in.sig_ev = ev.gu(l);
-        in.sig_slot = k;
-        p->ev_count[in.sig_ev]++;
         lvl.push_back({in, 4.0 * (in.r1 - in.r0) * H});
         wbytes += 4.0 * (in.r1 - in.r0) * H;
       }
@@ -397,15 +357,10 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     }
     // down projection + residual
     {
-      int k = 0;
-      for (int r0 = 0; r0 < H; r0 += rd, ++k) {
+      for (int r0 = 0; r0 < H; r0 += rd) {
         MkInstr in = blank(MKOP_DOWN, l, base + LV_DOWN);
         in.r0 = r0;
         in.r1 = std::min(H, r0 + rd);
-        in.wait_ev = ev.gu(l);
-        in.sig_ev = ev.down(l);
-        in.sig_slot = k;
-        p->ev_count[in.sig_ev]++;
         lvl.push_back({in, 2.0 * (in.r1 - in.r0) * I});
         wbytes += 2.0 * (in.r1 - in.r0) * I;
       }
@@ -420,7 +375,6 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
       MkInstr in = blank(MKOP_LMHEAD, L, LV_PER_LAYER * L);
       in.r0 = r0;
       in.r1 = std::min(V, r0 + rl);
-      in.wait_ev = ev.down(L - 1);
       in.ticket = lm_ticket;
       in.part = k;
       lvl.push_back({in, 2.0 * (in.r1 - in.r0) * H});
@@ -430,15 +384,6 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     wbytes += 2.0 * H;  // final norm gain
   }
   p->weight_bytes = wbytes;
-
-  // flag slots
-  p->ev_flag_base.assign(p->n_events, 0);
-  int acc = 0;
-  for (int e = 0; e < p->n_events; ++e) {
-    p->ev_flag_base[e] = acc;
-    acc += p->ev_count[e];
-  }
-  p->n_flags = acc;
 
   // per-CU lists in level order (stable)
   {
@@ -459,6 +404,12 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     p->instr_cu.swap(cu2);
   }
   mk_plan_finalize_lists(p);
+  // the events the instructions wait for and trigger, derived from their data
+  rc = mk_plan_normalize_events(p);
+  if (rc) {
+    delete p;
+    return rc;
+  }
   if (opts->exec_mode == MK_EXEC_STREAM) {
     stream_lds_layout(p);
     if (p->lds_bytes > MK_LDS_TOTAL) {
@@ -578,10 +529,27 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
   Checker ck(p);
   const int n = (int)p->instr.size();
   const int L = ck.L;
-  Events ev{L, ck.nkv};
   if ((int)p->instr_cu.size() != n) return MK_ERR_PLAN;
   if ((int)p->cu_begin.size() != p->n_cu + 1 || p->cu_begin[p->n_cu] != n) return MK_ERR_PLAN;
-  if (p->n_events != ev.count()) return MK_ERR_PLAN;
+  if ((int)p->ev_count.size() != p->n_events || (int)p->ev_flag_base.size() != p->n_events) return MK_ERR_PLAN;
+  // the queue order (when present): a permutation in which every
+  // instruction follows all triggers of the event it waits for
+  if (!p->queue.empty()) {
+    if ((int)p->queue.size() != n) return MK_ERR_PLAN;
+    std::vector<int> pos(n, -1), last_trig(std::max(p->n_events, 1), -1);
+    for (int k = 0; k < n; ++k) {
+      const int i = p->queue[k];
+      if (i < 0 || i >= n || pos[i] >= 0) return MK_ERR_PLAN;
+      pos[i] = k;
+    }
+    for (int i = 0; i < n; ++i)
+      if (p->instr[i].sig_ev >= 0 && p->instr[i].sig_ev < p->n_events)
+        last_trig[p->instr[i].sig_ev] = std::max(last_trig[p->instr[i].sig_ev], pos[i]);
+    for (int i = 0; i < n; ++i) {
+      const int e = p->instr[i].wait_ev;
+      if (e >= 0 && e < p->n_events && last_trig[e] >= pos[i]) return MK_ERR_PLAN;
+    }
+  }
 
   // 1. structure: fields in range, lists level-sorted
   for (int i = 0; i < n; ++i) {
@@ -822,6 +790,292 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
         park_or_ready(c);
       }
       if (executed != n) return MK_ERR_PLAN;  // some CU never got past a wait: deadlock
+    }
+  }
+  return MK_OK;
+}
+
+// ------------------------------------------------------- event normalisation
+//
+// The megakernel page's Q&A on MPK describes how a task graph's events are
+// normalised: each task waits for at most one event and triggers at most
+// one, events are fused by their predecessor and successor sets, and the
+// graph is linearised breadth-first so that the tasks one event releases
+// have contiguous indices.  mk_events_normalize does this for any DAG given
+// as raw predecessor lists:
+//   1. topological order (Kahn); a cycle among the raw edges is an error;
+//   2. transitive reduction: an edge q -> t is dropped when q is already an
+//      ancestor of another predecessor of t (ancestor bitsets filled in
+//      topological order; the union over a predecessor list is cached, since
+//      whole levels of tasks share one);
+//   3. fusion by predecessor set: tasks with the same reduced predecessors
+//      wait for one event;
+//   4. fusion by successor set: two events that share a predecessor are
+//      merged (union-find), so every task triggers at most one; a merged
+//      event one of whose waiters precedes one of its producers would never
+//      fire, and is reported;
+//   5. breadth-first linearisation from the source tasks (ties by rank): an
+//      event fires once its last predecessor has been visited and appends
+//      its waiters together; events are numbered in firing order, trigger
+//      slots in visiting order.
+
+namespace {
+struct UnionFind {
+  std::vector<int> p;
+  explicit UnionFind(int n) : p(n) {
+    for (int i = 0; i < n; ++i) p[i] = i;
+  }
+  int find(int x) {
+    while (p[x] != x) x = p[x] = p[p[x]];
+    return x;
+  }
+  void join(int a, int b) {
+    a = find(a);
+    b = find(b);
+    if (a != b) p[std::max(a, b)] = std::min(a, b);
+  }
+};
+}  // namespace
+
+extern "C" int mk_events_normalize(int32_t nt, const int32_t *pred_begin, const int32_t *pred_list, const int64_t *rank,
+                                   uint32_t flags, int32_t *wait_event, int32_t *trigger_event, int32_t *trigger_slot,
+                                   int32_t *event_count, int32_t *order_out, int32_t *n_events_out) {
+  if (nt < 0 || (nt > 0 && (!pred_begin || !wait_event || !trigger_event || !trigger_slot || !event_count ||
+                            !order_out)) || !n_events_out)
+    return MK_ERR_INVALID_ARG;
+  if (nt == 0) {
+    *n_events_out = 0;
+    return MK_OK;
+  }
+  if (pred_begin[0] != 0) return MK_ERR_INVALID_ARG;
+  // raw predecessor lists, sorted and without duplicates
+  std::vector<std::vector<int>> raw(nt);
+  for (int t = 0; t < nt; ++t) {
+    if (pred_begin[t + 1] < pred_begin[t]) return MK_ERR_INVALID_ARG;
+    for (int k = pred_begin[t]; k < pred_begin[t + 1]; ++k) {
+      const int q = pred_list[k];
+      if (q < 0 || q >= nt) return MK_ERR_INVALID_ARG;
+      if (q == t) return MK_ERR_PLAN;
+      raw[t].push_back(q);
+    }
+    std::sort(raw[t].begin(), raw[t].end());
+    raw[t].erase(std::unique(raw[t].begin(), raw[t].end()), raw[t].end());
+  }
+  // 1. topological order
+  std::vector<std::vector<int>> succ(nt);
+  std::vector<int> indeg(nt, 0), topo;
+  for (int t = 0; t < nt; ++t) {
+    for (int q : raw[t]) succ[q].push_back(t);
+    indeg[t] = (int)raw[t].size();
+  }
+  topo.reserve(nt);
+  for (int t = 0; t < nt; ++t)
+    if (!indeg[t]) topo.push_back(t);
+  for (size_t k = 0; k < topo.size(); ++k)
+    for (int s : succ[topo[k]])
+      if (--indeg[s] == 0) topo.push_back(s);
+  if ((int)topo.size() != nt) return MK_ERR_PLAN;
+
+  // 2. ancestors and transitive reduction
+  const size_t words = ((size_t)nt + 63) / 64;
+  std::vector<uint64_t> anc((size_t)nt * words, 0);
+  std::map<std::vector<int>, std::vector<uint64_t>> through_of;  // predecessor list -> union of their ancestors
+  std::vector<std::vector<int>> preds(nt);
+  const bool reduce = !(flags & 1u);
+  for (int t : topo) {
+    if (raw[t].empty()) continue;
+    auto it = through_of.find(raw[t]);
+    if (it == through_of.end()) {
+      std::vector<uint64_t> u(words, 0);
+      for (int q : raw[t]) {
+        const uint64_t *a = &anc[(size_t)q * words];
+        for (size_t w = 0; w < words; ++w) u[w] |= a[w];
+      }
+      it = through_of.emplace(raw[t], std::move(u)).first;
+    }
+    const std::vector<uint64_t> &through = it->second;
+    uint64_t *a = &anc[(size_t)t * words];
+    for (size_t w = 0; w < words; ++w) a[w] = through[w];
+    for (int q : raw[t]) {
+      a[q / 64] |= 1ull << (q % 64);
+      if (!reduce || !((through[q / 64] >> (q % 64)) & 1)) preds[t].push_back(q);
+    }
+  }
+  auto is_anc = [&](int x, int of) { return (anc[(size_t)of * words + x / 64] >> (x % 64)) & 1; };
+
+  // 3. fusion by predecessor set
+  std::map<std::vector<int>, int> ev_of_set;
+  std::vector<std::vector<int>> ev_preds, ev_waiters;
+  std::vector<int> wait_of(nt, -1);
+  for (int t = 0; t < nt; ++t) {
+    if (preds[t].empty()) continue;
+    auto it = ev_of_set.find(preds[t]);
+    int e;
+    if (it == ev_of_set.end()) {
+      e = (int)ev_preds.size();
+      ev_of_set[preds[t]] = e;
+      ev_preds.push_back(preds[t]);
+      ev_waiters.emplace_back();
+    } else {
+      e = it->second;
+    }
+    wait_of[t] = e;
+    ev_waiters[e].push_back(t);
+  }
+  // 4. fusion by successor set
+  const int ne0 = (int)ev_preds.size();
+  UnionFind uf(std::max(ne0, 1));
+  std::vector<int> trig_first(nt, -1);
+  for (int e = 0; e < ne0; ++e)
+    for (int q : ev_preds[e]) {
+      if (trig_first[q] < 0) trig_first[q] = e;
+      else uf.join(trig_first[q], e);
+    }
+  std::vector<int> root_id(std::max(ne0, 1), -1);
+  std::vector<std::vector<int>> mpreds, mwaiters;
+  for (int e = 0; e < ne0; ++e) {
+    const int r = uf.find(e);
+    if (root_id[r] < 0) {
+      root_id[r] = (int)mpreds.size();
+      mpreds.emplace_back();
+      mwaiters.emplace_back();
+    }
+    const int m = root_id[r];
+    mpreds[m].insert(mpreds[m].end(), ev_preds[e].begin(), ev_preds[e].end());
+    mwaiters[m].insert(mwaiters[m].end(), ev_waiters[e].begin(), ev_waiters[e].end());
+  }
+  const int ne = (int)mpreds.size();
+  std::vector<int> trig_of(nt, -1);
+  for (int m = 0; m < ne; ++m) {
+    auto &pr = mpreds[m];
+    std::sort(pr.begin(), pr.end());
+    pr.erase(std::unique(pr.begin(), pr.end()), pr.end());
+    for (int q : pr) trig_of[q] = m;
+    for (int w : mwaiters[m])
+      for (int q : pr)
+        if (q == w || is_anc(w, q)) return MK_ERR_PLAN;
+  }
+  for (int t = 0; t < nt; ++t)
+    if (wait_of[t] >= 0) wait_of[t] = root_id[uf.find(wait_of[t])];
+
+  // 5. breadth-first linearisation
+  std::vector<int> remaining(ne);
+  for (int m = 0; m < ne; ++m) remaining[m] = (int)mpreds[m].size();
+  auto before = [&](int x, int y) {
+    const int64_t rx = rank ? rank[x] : x, ry = rank ? rank[y] : y;
+    return rx != ry ? rx < ry : x < y;
+  };
+  std::vector<int> order;
+  order.reserve(nt);
+  for (int t = 0; t < nt; ++t)
+    if (wait_of[t] < 0) order.push_back(t);
+  std::sort(order.begin(), order.end(), before);
+  std::vector<int> ev_num(ne, -1), slot(nt, 0), ev_n(ne, 0);
+  int fired = 0;
+  for (size_t k = 0; k < order.size(); ++k) {
+    const int t = order[k];
+    const int m = trig_of[t];
+    if (m < 0) continue;
+    slot[t] = ev_n[m]++;
+    if (--remaining[m] == 0) {
+      ev_num[m] = fired++;
+      std::vector<int> ws = mwaiters[m];
+      std::sort(ws.begin(), ws.end(), before);
+      order.insert(order.end(), ws.begin(), ws.end());
+    }
+  }
+  if ((int)order.size() != nt || fired != ne) return MK_ERR_PLAN;
+  for (int t = 0; t < nt; ++t) {
+    wait_event[t] = wait_of[t] >= 0 ? ev_num[wait_of[t]] : -1;
+    trigger_event[t] = trig_of[t] >= 0 ? ev_num[trig_of[t]] : -1;
+    trigger_slot[t] = slot[t];
+    order_out[t] = order[t];
+  }
+  for (int m = 0; m < ne; ++m) event_count[ev_num[m]] = (int)mpreds[m].size();
+  *n_events_out = ne;
+  return MK_OK;
+}
+
+// The plan's tasks are its instructions, except that the splits of one
+// attention unit are one task (only the unit's last arriver triggers); the
+// raw edges run from the writers of every slice an instruction reads.
+int mk_plan_normalize_events(mk_plan_t *p) {
+  if (!p) return MK_ERR_INVALID_ARG;
+  Checker ck(p);
+  const int n = (int)p->instr.size();
+  std::vector<int> task_of(n, -1), first_instr;
+  std::map<std::tuple<int, int, int>, int> attn_task;
+  for (int i = 0; i < n; ++i) {
+    const MkInstr &in = p->instr[i];
+    if (in.op == MKOP_ATTN) {
+      auto key = std::make_tuple(in.layer, in.r0, in.r1);
+      auto it = attn_task.find(key);
+      if (it != attn_task.end()) {
+        task_of[i] = it->second;
+        continue;
+      }
+      attn_task[key] = (int)first_instr.size();
+    }
+    task_of[i] = (int)first_instr.size();
+    first_instr.push_back(i);
+  }
+  const int nt = (int)first_instr.size();
+  std::vector<std::vector<Writer>> writers(BK_N * ck.L);
+  std::vector<Access> rd, wr;
+  for (int t = 0; t < nt; ++t) {
+    ck.accesses(p->instr[first_instr[t]], rd, wr);
+    for (auto &a : wr) writers[a.buf].push_back({a.lo, a.hi, t});
+  }
+  for (auto &w : writers)
+    std::sort(w.begin(), w.end(), [](const Writer &a, const Writer &b) { return a.lo != b.lo ? a.lo < b.lo : a.instr < b.instr; });
+  std::vector<int32_t> begin(nt + 1, 0), list;
+  std::vector<int64_t> rank(nt);
+  std::vector<int> seen(nt, -1);  // a task writes one slice per sequence: list it once per reader
+  for (int t = 0; t < nt; ++t) {
+    ck.accesses(p->instr[first_instr[t]], rd, wr);
+    for (auto &r : rd) {
+      const auto &ws = writers[r.buf];  // disjoint slices sorted by lo
+      auto it = std::lower_bound(ws.begin(), ws.end(), r.lo, [](const Writer &w, int64_t v) { return w.lo < v; });
+      if (it != ws.begin() && std::prev(it)->hi > r.lo) --it;
+      int64_t covered = r.lo;
+      for (; it != ws.end() && it->lo < r.hi; ++it) {
+        if (it->hi <= r.lo) continue;
+        if (seen[it->instr] != t) {
+          seen[it->instr] = t;
+          list.push_back(it->instr);
+        }
+        if (it->lo <= covered) covered = std::max(covered, it->hi);
+      }
+      if (covered < r.hi) return MK_ERR_PLAN;  // part of the slice has no writer
+    }
+    begin[t + 1] = (int32_t)list.size();
+    rank[t] = (int64_t)p->instr[first_instr[t]].level * n + first_instr[t];  // level, then list order
+  }
+  std::vector<int32_t> wait(nt), trig(nt), slot(nt), count(nt), order(nt);
+  int32_t ne = 0;
+  const int rc = mk_events_normalize(nt, begin.data(), list.data(), rank.data(), 0, wait.data(), trig.data(),
+                                     slot.data(), count.data(), order.data(), &ne);
+  if (rc != MK_OK) return rc;
+  p->n_events = ne;
+  p->ev_count.assign(count.begin(), count.begin() + ne);
+  p->ev_flag_base.assign(ne, 0);
+  int acc = 0;
+  for (int e = 0; e < ne; ++e) {
+    p->ev_flag_base[e] = acc;
+    acc += p->ev_count[e];
+  }
+  p->n_flags = acc;
+  std::vector<std::vector<int>> members(nt);
+  for (int i = 0; i < n; ++i) members[task_of[i]].push_back(i);
+  p->queue.clear();
+  for (int k = 0; k < nt; ++k) {
+    const int t = order[k];
+    for (int i : members[t]) {
+      MkInstr &in = p->instr[i];
+      in.wait_ev = wait[t];
+      in.sig_ev = trig[t];
+      in.sig_slot = trig[t] >= 0 ? slot[t] : 0;
+      p->queue.push_back(i);
     }
   }
   return MK_OK;

@@ -29,6 +29,10 @@ struct mk_plan_s {
   std::vector<MkInstr> instr;  // CU-major
   std::vector<int32_t> instr_cu;
   std::vector<int32_t> cu_begin, level_begin, level_list, ev_count, ev_flag_base;
+  // BFS linearisation of the instructions (indices into instr): the order a
+  // global work queue hands them out in; the instructions one event releases
+  // are contiguous, and every instruction comes after all its producers
+  std::vector<int32_t> queue;
   MkLayout lay{};
   bool validated = false;
   double weight_bytes = 0;
@@ -36,5 +40,12 @@ struct mk_plan_s {
 
 int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan_t **out);
 int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed);
+// Derive the plan's events from the instructions' data accesses (MPK-style
+// normalisation): at most one wait and one trigger event per instruction,
+// events fused by predecessor set and by successor set, numbered and
+// linearised breadth-first (fills ev_count, ev_flag_base, n_flags, the
+// instructions' wait/trigger fields and `queue`).  MK_ERR_PLAN when the
+// fusion would create a cycle or an instruction reads a slice nobody writes.
+int mk_plan_normalize_events(mk_plan_t *p);
 void mk_plan_finalize_lists(mk_plan_t *p);  // recompute cu_begin / level lists from instr + instr_cu
 void mk_plan_compute_layout(mk_plan_t *p);

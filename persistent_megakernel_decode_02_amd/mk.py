@@ -100,6 +100,10 @@ SIGNATURES = {
     "mk_plan_export": (C.c_int, [C.c_void_p, C.POINTER(mk_instr_desc), C.c_size_t, C.POINTER(C.c_size_t)]),
     "mk_plan_simulate": (C.c_int, [C.c_void_p, C.c_int32, C.c_uint64]),
     "mk_plan_destroy": (None, [C.c_void_p]),
+    "mk_plan_get_queue": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_size_t, C.POINTER(C.c_size_t)]),
+    "mk_events_normalize": (C.c_int, [C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int64),
+                                      C.c_uint32, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                      C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "mk_plan_set_instructions": (C.c_int, [C.c_void_p, C.POINTER(mk_instr_desc), C.c_size_t]),
     "mk_ctx_create": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(C.c_void_p)]),
     "mk_ctx_create_scratch": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p)]),
@@ -184,6 +188,39 @@ def mk_plan_get_info(plan) -> mk_plan_info:
     info = mk_plan_info()
     _check(load_library().mk_plan_get_info(plan, C.byref(info)), "mk_plan_get_info")
     return info
+
+
+def mk_plan_get_queue(plan) -> List[int]:
+    lib = load_library()
+    n = C.c_size_t()
+    _check(lib.mk_plan_get_queue(plan, None, 0, C.byref(n)), "mk_plan_get_queue")
+    arr = (C.c_int32 * max(n.value, 1))()
+    _check(lib.mk_plan_get_queue(plan, arr, n.value, C.byref(n)), "mk_plan_get_queue")
+    return list(arr[:n.value])
+
+
+MK_NORM_NO_REDUCTION = 1
+
+
+def mk_events_normalize(preds: List[List[int]], rank: Optional[List[int]] = None, flags: int = 0):
+    """Normalise a task graph given as predecessor lists.  Returns (rc, dict
+    with wait, trigger, slot, count, order, n_events)."""
+    nt = len(preds)
+    begin = (C.c_int32 * (nt + 1))()
+    flat = [q for ps in preds for q in ps]
+    lst = (C.c_int32 * max(len(flat), 1))(*flat)
+    acc = 0
+    for t, ps in enumerate(preds):
+        begin[t] = acc
+        acc += len(ps)
+    begin[nt] = acc
+    rk = (C.c_int64 * nt)(*rank) if rank is not None else None
+    outs = [(C.c_int32 * max(nt, 1))() for _ in range(5)]
+    ne = C.c_int32()
+    rc = load_library().mk_events_normalize(nt, begin, lst, rk, flags, *outs, C.byref(ne))
+    wait, trig, slot, count, order = (list(o[:nt]) for o in outs)
+    return rc, {"wait": wait, "trigger": trig, "slot": slot, "count": count[:ne.value], "order": order,
+                "n_events": ne.value}
 
 
 def mk_plan_export(plan) -> List[mk_instr_desc]:
