@@ -149,7 +149,7 @@ def kernel_name(mode: str, per_launch: int) -> str:
     if mode in ("flat-counter", "flat-flag", "flat-sentinel"):
         sent = "_sent" if mode == "flat-sentinel" else ""
         return f"mk_mega{sent}_steps_kernel" if per_launch > 1 else f"mk_mega{sent}_kernel"
-    return {"multi": "mk_role_level_kernel", "flat-levels": "mk_flat_level_kernel",
+    return {"multi": "mk_role_level_kernel", "flat-levels": "mk_flat_level_kernel", "queue-flag": "mk_queue_kernel",
             "stream-counter": "mk_stream_kernel", "stream-flag": "mk_stream_kernel"}.get(mode, "mk_role_mega_kernel")
 
 
@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--workload", default="llama1b_pos1024")
     ap.add_argument("--mode", default=None,
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
-                             "flat-sentinel", "flat-levels", "stream-counter", "stream-flag"],
+                             "flat-sentinel", "flat-levels", "queue-flag", "stream-counter", "stream-flag"],
                     help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
                          "homogeneous engine with flag events)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
@@ -292,6 +292,7 @@ def main():
              "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
              "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
              "flat-levels": (mk.MK_EXEC_FLAT_MULTI, mk.MK_SYNC_COUNTER),
+             "queue-flag": (mk.MK_EXEC_QUEUE, mk.MK_SYNC_FLAG),
              "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
              "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
     spl = max(1, args.steps_per_launch)
@@ -310,7 +311,7 @@ def main():
                        "kv_splits": info.kv_splits, "lds_bytes": info.lds_bytes,
                        "block_threads": info.block_threads}}
     if not args.no_extras:
-        for name in [m for m in modes if m != args.mode and (B <= 4 or m.startswith("flat"))
+        for name in [m for m in modes if m != args.mode and (B <= 4 or m.startswith(("flat", "queue")))
                      and (B == 1 or not m.startswith("stream"))]:
             ms2, _ = timed(*modes[name], K, W)
             extras[name] = {"passes_per_s": round(1000.0 * K / ms2, 2), "ms_per_pass": round(ms2 / K, 5),

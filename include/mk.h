@@ -81,10 +81,16 @@ enum { MK_EXEC_MEGA = 0,    /* one persistent launch per decode step, loader /
                                streamer waves keep projection weights in flight
                                across instructions, one wave synchronises
                                (MK_SYNC_COUNTER or MK_SYNC_FLAG, max_batch 1) */
-       MK_EXEC_FLAT_MULTI = 4 /* MK_EXEC_FLAT's plan and ops, one launch per
+       MK_EXEC_FLAT_MULTI = 4, /* MK_EXEC_FLAT's plan and ops, one launch per
                                dependency level with no waits: the multi-kernel
                                baseline of the homogeneous engine (also
-                               capturable as a hipGraph, mk_graph_create) */ };
+                               capturable as a hipGraph, mk_graph_create) */
+       MK_EXEC_QUEUE = 5    /* one persistent launch, homogeneous ops, no per-CU
+                               lists: every workgroup takes the next instruction
+                               of the plan's breadth-first queue from a global
+                               atomic ticket (dynamic scheduling, megakernel page
+                               sections 2.4 and 2.6 item 5; MK_SYNC_COUNTER or
+                               MK_SYNC_FLAG) */ };
 
 typedef struct {
   int32_t max_batch;   /* sequences per step: 1..16 (MK_EXEC_FLAT), 1 (MK_EXEC_STREAM),

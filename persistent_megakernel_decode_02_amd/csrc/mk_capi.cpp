@@ -37,7 +37,8 @@ static inline int mega_lds(const mk_plan_t *p) { return std::max(p->lds_bytes, 8
 // dynamic LDS a plan's kernel is launched with
 static inline int launch_lds(const mk_plan_t *p) {
   const int m = p->opts.exec_mode;
-  return m == MK_EXEC_FLAT || m == MK_EXEC_FLAT_MULTI || m == MK_EXEC_STREAM ? mega_lds(p) : p->lds_bytes;
+  return m == MK_EXEC_FLAT || m == MK_EXEC_FLAT_MULTI || m == MK_EXEC_STREAM || m == MK_EXEC_QUEUE ? mega_lds(p)
+                                                                                                    : p->lds_bytes;
 }
 
 extern "C" {
@@ -407,6 +408,8 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   P.cu_begin = (const int32_t *)(w + y.cu_begin);
   P.level_begin = (const int32_t *)(w + y.level_begin);
   P.level_list = (const int32_t *)(w + y.level_list);
+  P.queue = (const int32_t *)(w + y.queue);
+  P.queue_ctr = (uint32_t *)(w + y.queue_ctr);
   P.ev_count = (const int32_t *)(w + y.ev_count);
   P.ev_flag_base = (const int32_t *)(w + y.ev_flag_base);
   P.rope = (const float *)(w + y.rope);
@@ -435,6 +438,7 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   up(y.cu_begin, p.cu_begin.data(), 4 * p.cu_begin.size());
   up(y.level_begin, p.level_begin.data(), 4 * p.level_begin.size());
   up(y.level_list, p.level_list.data(), 4 * p.level_list.size());
+  up(y.queue, p.queue.data(), 4 * p.queue.size());
   up(y.ev_count, p.ev_count.data(), 4 * p.ev_count.size());
   up(y.ev_flag_base, p.ev_flag_base.data(), 4 * p.ev_flag_base.size());
   up(y.rope, c->rope.data(), 4 * c->rope.size());
@@ -543,6 +547,9 @@ int mk_decode_step(mk_ctx *c, int32_t *d_tokens, int32_t *d_positions, int32_t b
       return MK_ERR_HIP;
   } else if (mode == MK_EXEC_STREAM) {
     if (mk_launch_stream(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
+  } else if (mode == MK_EXEC_QUEUE) {
+    if (c->plan.queue.size() != c->plan.instr.size()) return MK_ERR_PLAN;  // a plan whose list was replaced
+    if (mk_launch_queue(dp, S, c->plan.n_cu, mega_lds(&c->plan), st)) return MK_ERR_HIP;
   } else if (mode == MK_EXEC_FLAT_MULTI) {
     S.multi = 1;
     for (int lv = 0; lv < c->plan.n_levels; ++lv) {

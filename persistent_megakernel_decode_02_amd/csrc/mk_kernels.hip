@@ -197,6 +197,51 @@ extern "C" __global__ void mk_step_end_kernel(MkStep *Sd) {
   if (threadIdx.x == 0 && blockIdx.x == 0) Sd->epoch = Sd->epoch + 1u;
 }
 
+// Work-queue engine: the homogeneous ops, but no per-CU lists.  Every
+// workgroup takes the next ticket of a global counter (an atomic add) and
+// runs the instruction at that position of the breadth-first queue, waiting
+// for its event as usual.  The queue puts every instruction after the
+// triggers of the event it waits for, and each workgroup finishes the
+// instruction it holds before taking another, so the lowest unfinished
+// ticket can always run: the grid drains.  The next ticket is requested
+// while the current instruction runs.  Each workgroup takes exactly one
+// ticket past the end, so a step consumes n_instr + n_cu tickets and step e
+// starts at e (n_instr + n_cu) (modulo 2^32).
+MKD uint32_t queue_take(const MkProgram &P, int *s_flag) {
+  if (threadIdx.x == 0) *s_flag = (int)addcu(P.queue_ctr, 1u);
+  __syncthreads();
+  const uint32_t t = (uint32_t)__builtin_amdgcn_readfirstlane(*s_flag);  // uniform: scalar queue loads
+  __syncthreads();
+  return t;
+}
+
+extern "C" __global__ void __launch_bounds__(MK_BLOCK) mk_queue_kernel(const MkProgram *__restrict__ Pp, MkStep S) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_flag, s_next;
+  const MkProgram &P = *Pp;
+  if (mk_aborted(P)) return;
+  const uint32_t n = (uint32_t)P.n_instr, base = S.epoch * (n + (uint32_t)P.n_cu);
+  uint64_t *const trace = P.trace;
+  uint32_t t = queue_take(P, &s_flag) - base;
+  while (t < n) {
+    uint32_t next = 0;  // requested now, consumed (and waited for) once the instruction is done
+    if (threadIdx.x == 0) next = addcu(P.queue_ctr, 1u);
+    const int i = cld(&P.queue[t]);
+    const MkInstr in = cld(&P.instr[i]);
+    const uint64_t tw = trace ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint64_t ts = 0;
+    const int st = run_instr<false>(P, S, in, smem, &s_flag, trace != nullptr, ts);
+    if (st == MK_ST_ABORT) return;
+    if (st == MK_ST_SIGNAL && in.sig_ev >= 0) mk_signal(P, S, in.sig_ev, in.sig_slot);
+    __syncthreads();
+    if (trace && threadIdx.x == 0) trace_record(trace, i, tw, ts, __builtin_amdgcn_s_memrealtime(), blockIdx.x, S.epoch);
+    if (threadIdx.x == 0) s_next = (int)next;
+    __syncthreads();
+    t = (uint32_t)__builtin_amdgcn_readfirstlane(s_next) - base;
+    __syncthreads();
+  }
+}
+
 // Stream engine (one sequence per step): waves 0..MK_NSW-1 stream projection
 // weights through register rings, wave MK_NSW synchronises; the waves meet
 // only at attention instructions, which all of them run together.
@@ -288,9 +333,10 @@ extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
 static const void *const g_kernels[] = {(const void *)mk_mega_kernel,           (const void *)mk_role_mega_kernel,
                                         (const void *)mk_role_level_kernel,     (const void *)mk_stream_kernel,
                                         (const void *)mk_mega_sent_kernel,      (const void *)mk_mega_steps_kernel,
-                                        (const void *)mk_mega_sent_steps_kernel, (const void *)mk_flat_level_kernel};
+                                        (const void *)mk_mega_sent_steps_kernel, (const void *)mk_flat_level_kernel,
+                                        (const void *)mk_queue_kernel};
 static constexpr int MK_NKERNELS = (int)(sizeof g_kernels / sizeof g_kernels[0]);
-static int g_lds_set[MK_NKERNELS] = {-1, -1, -1, -1, -1, -1, -1, -1};
+static int g_lds_set[MK_NKERNELS] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
 static int lds_slot(const void *fn) {
   for (int i = 0; i < MK_NKERNELS; ++i)
     if (g_kernels[i] == fn) return i;
@@ -314,6 +360,7 @@ static const void *mega_fn(bool sentinel, bool steps) {
 static const void *exec_kernel(int exec_mode, int sync_mode) {
   if (exec_mode == MKEXEC_FLAT) return mega_fn(sync_mode == MKSYNC_SENTINEL, false);
   if (exec_mode == MKEXEC_FLAT_MULTI) return (const void *)mk_flat_level_kernel;
+  if (exec_mode == MKEXEC_QUEUE) return (const void *)mk_queue_kernel;
   return exec_mode == MKEXEC_MEGA     ? (const void *)mk_role_mega_kernel
          : exec_mode == MKEXEC_STREAM ? (const void *)mk_stream_kernel
                                       : (const void *)mk_role_level_kernel;
@@ -361,6 +408,12 @@ int mk_launch_flat_level(const MkProgram *d_prog, const MkStep *d_step, const Mk
   if (n_blocks <= 0) return 0;
   if (!ensure_lds((const void *)mk_flat_level_kernel, lds)) return -1;
   hipLaunchKernelGGL(mk_flat_level_kernel, dim3(n_blocks), dim3(MK_BLOCK), lds, s, d_prog, d_step, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int mk_launch_queue(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s) {
+  if (!ensure_lds((const void *)mk_queue_kernel, lds)) return -1;
+  hipLaunchKernelGGL(mk_queue_kernel, dim3(n_cu), dim3(MK_BLOCK), lds, s, d_prog, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -24,7 +24,9 @@ int mk_launch_role_mega(const MkProgram *d_prog, const MkStep &st, int n_cu, int
 // d_step: device step record or null (then st is used)
 int mk_launch_flat_level(const MkProgram *d_prog, const MkStep *d_step, const MkStep &st, int n_blocks, int lds,
                          hipStream_t s);
-int mk_launch_step_end(MkStep *d_step, hipStream_t s);  // d_step->epoch += 1 on the device
+int mk_launch_step_end(MkStep *d_step, hipStream_t s);
+// work-queue engine: n_cu persistent workgroups take instructions from the global queue
+int mk_launch_queue(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds, hipStream_t s);  // d_step->epoch += 1 on the device
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_occupancy_role(int lds, int *blocks_per_cu);
 int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s);

@@ -47,7 +47,14 @@
 #define MK_FA_LDS (MK_FA_WP + MK_NWAVES * MK_MAX_GROUP * 130 * 4)
 
 enum MkSync : int32_t { MKSYNC_COUNTER = 0, MKSYNC_FLAG = 1, MKSYNC_SENTINEL = 2 };
-enum MkExec : int32_t { MKEXEC_MEGA = 0, MKEXEC_MULTI = 1, MKEXEC_FLAT = 2, MKEXEC_STREAM = 3, MKEXEC_FLAT_MULTI = 4 };
+enum MkExec : int32_t {
+  MKEXEC_MEGA = 0,
+  MKEXEC_MULTI = 1,
+  MKEXEC_FLAT = 2,
+  MKEXEC_STREAM = 3,
+  MKEXEC_FLAT_MULTI = 4,
+  MKEXEC_QUEUE = 5
+};
 
 enum MkOp : int32_t {
   MKOP_QKV = 1,
@@ -118,6 +125,8 @@ struct MkProgram {
   const int32_t *cu_begin;     // [n_cu + 1]
   const int32_t *level_begin;  // [n_levels + 1] into level_list (multi-launch)
   const int32_t *level_list;   // instruction indices grouped by level
+  const int32_t *queue;        // [n_instr] breadth-first instruction order (work-queue engine)
+  uint32_t *queue_ctr;         // tickets handed out so far (n_instr + n_cu per step)
   const int32_t *ev_count;     // [n_events] triggers per step
   const int32_t *ev_flag_base; // [n_events] first flag slot
 

@@ -46,7 +46,7 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
   if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
-  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_FLAT_MULTI) return MK_ERR_INVALID_ARG;
+  if (o->exec_mode < MK_EXEC_MEGA || o->exec_mode > MK_EXEC_QUEUE) return MK_ERR_INVALID_ARG;
   // data sentinels replace the events only inside one persistent launch; the
   // homogeneous engine polls them in its one-sequence ops only
   if (o->sync_mode == MK_SYNC_SENTINEL && o->exec_mode != MK_EXEC_MEGA &&
@@ -187,6 +187,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.cu_begin = take(4 * (p->n_cu + 1));
   y.level_begin = take(4 * (p->n_levels + 1));
   y.level_list = take(4 * std::max<size_t>(p->instr.size(), 1));
+  y.queue = take(4 * std::max<size_t>(p->instr.size(), 1));
   y.ev_count = take(4 * std::max(p->n_events, 1));
   y.ev_flag_base = take(4 * std::max(p->n_events, 1));
   y.rope = take(4 * (size_t)p->max_ctx * d);
@@ -207,6 +208,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.flags = take(4 * std::max(p->n_flags, 1));
   y.tickets = take(4 * std::max(p->n_tickets, 1));
   y.lm_done = take(4);
+  y.queue_ctr = take(4);
   y.err = take(16);
   y.sync_end = o;
   y.total = o;
@@ -254,7 +256,8 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // gate/up stream the other CUs started during attention, and would hold
   // up the O and gate/up events
   int og_cus = n_cu;
-  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI || opts->exec_mode == MK_EXEC_STREAM) &&
+  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI || opts->exec_mode == MK_EXEC_STREAM ||
+       opts->exec_mode == MK_EXEC_QUEUE) &&
       B == 1 &&
       (int64_t)B * nkv * S < n_cu / 2)
     og_cus = n_cu - B * nkv * S;
@@ -416,7 +419,8 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
       delete p;
       return MK_ERR_UNSUPPORTED;
     }
-  } else if (opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI) {
+  } else if (opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI ||
+             opts->exec_mode == MK_EXEC_QUEUE) {
     p->lds_bytes = lds_requirement(p);
     // the one-sequence ops stage a normalised vector of at most 16 floats per thread
     if (p->lds_bytes > MK_LDS_TOTAL || shape->hidden > 16 * MK_BLOCK) {

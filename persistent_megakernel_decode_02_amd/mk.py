@@ -29,7 +29,7 @@ MK_ERR_UNSUPPORTED = -11
 MK_ERR_SCRATCH = -12
 
 MK_SYNC_COUNTER, MK_SYNC_FLAG, MK_SYNC_SENTINEL = 0, 1, 2
-MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM, MK_EXEC_FLAT_MULTI = 0, 1, 2, 3, 4
+MK_EXEC_MEGA, MK_EXEC_MULTI, MK_EXEC_FLAT, MK_EXEC_STREAM, MK_EXEC_FLAT_MULTI, MK_EXEC_QUEUE = 0, 1, 2, 3, 4, 5
 MK_ADVANCE = 1
 MK_MAX_STEPS = 65536
 MK_OP_QKV, MK_OP_ATTN, MK_OP_OPROJ, MK_OP_GATEUP, MK_OP_DOWN, MK_OP_LMHEAD = 1, 2, 3, 4, 5, 6

@@ -49,6 +49,7 @@ MODES = {"mega-counter": (mk.MK_EXEC_MEGA, mk.MK_SYNC_COUNTER), "mega-flag": (mk
          "flat-counter": (mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER), "flat-flag": (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
          "flat-sentinel": (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL),
          "flat-levels": (mk.MK_EXEC_FLAT_MULTI, mk.MK_SYNC_COUNTER),
+         "queue-counter": (mk.MK_EXEC_QUEUE, mk.MK_SYNC_COUNTER), "queue-flag": (mk.MK_EXEC_QUEUE, mk.MK_SYNC_FLAG),
          "stream-counter": (mk.MK_EXEC_STREAM, mk.MK_SYNC_COUNTER),
          "stream-flag": (mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG)}
 
@@ -66,8 +67,8 @@ def test_tiny_decode_matches_oracle(tiny_setup, mode):
 
 @pytest.mark.parametrize("group", [("mega-counter", "mega-flag", "mega-sentinel", "multi"),
                                    ("flat-counter", "flat-flag", "flat-sentinel"),
-                                   ("stream-counter", "stream-flag")],
-                         ids=["roles", "flat", "stream"])
+                                   ("stream-counter", "stream-flag"), ("flat-levels", "queue-counter", "queue-flag")],
+                         ids=["roles", "flat", "stream", "queue"])
 def test_tiny_modes_bit_identical(tiny_setup, group):
     # the same ops under different synchronisation / launch schemes give the same bits
     runs = [_run_tiny(tiny_setup, exec_mode=MODES[m][0], sync_mode=MODES[m][1]) for m in group]
@@ -116,7 +117,7 @@ def llama1b():
 # once and shared by the modes whose tokens agree.
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("mode", ["stream-flag", "stream-counter", "flat-flag", "flat-counter", "flat-sentinel",
-                                  "flat-levels", "mega-counter",
+                                  "flat-levels", "queue-flag", "mega-counter",
                                   "mega-flag", "mega-sentinel", "multi"])
 def test_llama1b_pos1024_full_sequence(llama1b, mode):
     wl = si.WORKLOADS["llama1b_pos1024"]
@@ -152,7 +153,7 @@ TINY_BATCHED = {b: si.Workload(f"tiny_b{b}", TINY.shape, batch=b, steps=6, start
 
 
 @pytest.mark.parametrize("batch", [2, 5, 16])
-@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag"])
+@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag", "queue-flag"])
 def test_tiny_batched_decode_matches_oracle(tiny_setup, batch, mode):
     wl = TINY_BATCHED[batch]
     w, gw, model = tiny_setup
