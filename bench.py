@@ -98,9 +98,9 @@ def stored_traffic(workload: str, mode: str):
     return round(float(kv["hbm_bytes_per_launch"]))
 
 
-def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
-    """Time k batched decode passes of workload `wl` (homogeneous engine,
-    flag synchronisation) after w_ untimed ones; returns a summary dict."""
+def run_workload(si, engine, mk, wl, gw, dev, stream, k, w_, log, exec_mode, sync_mode, label):
+    """Time k decode passes of workload `wl` (after w_ untimed ones) on the
+    given engine; returns a summary dict."""
     import torch
     s, B = wl.shape, wl.batch
     pos0 = wl.positions0(0)
@@ -108,13 +108,15 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
     t0 = time.time()
     kv = si.make_kv_cache(s, B, max_ctx, pos0, master=0).to(dev)
     first = si.workload_tokens(wl, 0)[:B]
-    log(f"[bench] batched inputs ready in {time.time() - t0:.1f}s ({wl.name})")
+    if len(first) < B:
+        first = (first * B)[:B]
+    log(f"[bench] {wl.name} inputs ready in {time.time() - t0:.1f}s")
     tokens = torch.tensor(first, dtype=torch.int32, device=dev)
     positions = torch.tensor(pos0, dtype=torch.int32, device=dev)
     logits = torch.empty((B, s.vocab), dtype=torch.float32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, exec_mode=mk.MK_EXEC_FLAT,
-                        sync_mode=mk.MK_SYNC_FLAG, stream=stream)
+    eng = engine.Engine(s, gw, max_batch=B, max_ctx=max_ctx, exec_mode=exec_mode, sync_mode=sync_mode,
+                        stream=stream)
     try:
         for _ in range(w_):
             eng.step(tokens, positions, kv, logits, nxt, advance=True)
@@ -135,13 +137,33 @@ def run_batched(si, engine, mk, wl, gw, dev, stream, k, w_, log):
         info = eng.info
     finally:
         eng.close()
+    del kv
     bpp = bytes_per_pass(s, [[p + t for p in pos0] for t in range(k)])
-    log(f"[bench] batched {wl.name}: {k} passes in {ms * k:.3f} ms")
-    return {"workload": wl.name, "batch": B, "exec": "flat-flag", "passes": k,
+    log(f"[bench] {wl.name} ({label}): {k} passes in {ms * k:.3f} ms")
+    return {"workload": wl.name, "batch": B, "exec": label, "passes": k,
             "passes_per_s": round(1000.0 / ms, 2), "tokens_per_s": round(1000.0 * B / ms, 1),
             "ms_per_pass": round(ms, 5), "bytes_per_pass": bpp,
             "hbm_frac": round(bpp / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "kv_splits": info.kv_splits,
             "context_lengths": [min(pos0), max(pos0)]}
+
+
+def gpu_weights(si, s, dev, seed):
+    """Random-init bf16 weights of shape `s` drawn on the device (N(0, 0.02),
+    norm gains 1): the timing-only configurations whose weights are too
+    large to draw on the host in the time a benchmark run allows."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def normal(shape):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+
+    shapes = si.layer_tensor_shapes(s)
+    out = {"embed": normal((s.vocab, s.hidden)), "lm_head": None if s.tied else normal((s.vocab, s.hidden)),
+           "final_norm": torch.ones(s.hidden, dtype=torch.bfloat16, device=dev)}
+    out["layers"] = [{name: (torch.ones(shapes[name], dtype=torch.bfloat16, device=dev) if name.endswith("norm")
+                             else normal(shapes[name])) for name in si.LAYER_TENSORS} for _ in range(s.n_layers)]
+    return out
 
 
 def kernel_name(mode: str, per_launch: int) -> str:
@@ -162,8 +184,8 @@ def main():
     ap.add_argument("--mode", default=None,
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
                              "flat-sentinel", "flat-levels", "queue-flag", "stream-counter", "stream-flag"],
-                    help="execution / synchronisation scheme of the headline number (default: flat-flag, the "
-                         "homogeneous engine with flag events)")
+                    help="execution / synchronisation scheme of the headline number (default: flat-sentinel, "
+                         "the homogeneous engine polling data sentinels, at batch 1; flat-flag otherwise)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--trace-passes", type=int, default=4, help="traced passes run back to back (the last is kept)")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
@@ -173,6 +195,7 @@ def main():
                     help="greedy passes per launch of the headline mode (> 1: multi-token persistent decode, "
                          "homogeneous engine only)")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-8b", action="store_true", help="skip the Llama-8B line of the extras")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -196,7 +219,7 @@ def main():
     s = wl.shape
     B = wl.batch
     if args.mode is None:
-        args.mode = "flat-flag"
+        args.mode = "flat-sentinel" if B == 1 else "flat-flag"
     K, W = args.steps, args.warmup
     # passes restart from the first position after the warmup (and before a
     # trace), so the workload's own context bound holds whenever it covers them
@@ -348,7 +371,24 @@ def main():
         # lengths 512..4096, projections as MFMA contractions (FLAT engine)
         bw = si.WORKLOADS["llama1b_b16"]
         if bw.shape == s and B != bw.batch:
-            extras["batched"] = run_batched(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log)
+            extras["batched"] = run_workload(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log,
+                                             mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG, "flat-flag")
+            extras["batched_queue"] = run_workload(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log,
+                                                   mk.MK_EXEC_QUEUE, mk.MK_SYNC_FLAG, "queue-flag")
+        # the other one-sequence configurations in the headline mode: the same
+        # weights at context 8192, and the Llama-8B shape (weights drawn on the GPU)
+        if B == 1 and args.workload == "llama1b_pos1024":
+            hm = modes[args.mode]
+            w3 = si.WORKLOADS["llama1b_pos8192"]
+            extras["c3"] = run_workload(si, engine, mk, w3, gw, dev, stream, 32, 4, log, *hm, args.mode)
+            if not args.no_8b:
+                w5 = si.WORKLOADS["llama8b_pos2048"]
+                t8 = time.time()
+                gw8 = gpu_weights(si, w5.shape, dev, 8)
+                log(f"[bench] {w5.name} weights drawn on the GPU in {time.time() - t8:.1f}s")
+                extras["c5"] = run_workload(si, engine, mk, w5, gw8, dev, stream, 16, 2, log, *hm, args.mode)
+                del gw8
+                torch.cuda.empty_cache()
         # grid-barrier microbenchmark
         dinfo = mk.mk_device_query(0)
         n = dinfo.num_cus

@@ -23,8 +23,9 @@ def llama8b():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("mode", [(mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG), (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG)],
-                         ids=["stream-flag", "flat-flag"])
+@pytest.mark.parametrize("mode", [(mk.MK_EXEC_STREAM, mk.MK_SYNC_FLAG), (mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG),
+                                  (mk.MK_EXEC_FLAT, mk.MK_SYNC_SENTINEL)],
+                         ids=["stream-flag", "flat-flag", "flat-sentinel"])
 def test_llama8b_pos2048_decode(llama8b, mode):
     w, gw, model = llama8b
     res = run_decode(WL, 4, weights=w, gpu_weights=gw, model=model, exec_mode=mode[0], sync_mode=mode[1])
