@@ -230,6 +230,16 @@ MKD float resid_in(const MkProgram &P, const MkStep &S, int l, int b, int i, int
   return ldcp(P, P.xout + ((size_t)(l - 1) * P.B_max + b) * P.H + i, sent, ok);
 }
 
+// Output rows are gathered in LDS (`ob`) by the row groups' finishers and
+// stored by the whole block once the instruction's last weight batch has been
+// consumed: a wave's vector-memory counter retires loads and stores in issue
+// order, so a device-scope store issued between two load batches would hold
+// the second batch back until the store is acknowledged.
+MKD void flush_rows(float *dst, const float *ob, int n) {
+  lds_barrier();
+  for (int i = mk_tid(); i < n; i += MK_BLOCK) stc(dst + i, ob[i]);
+}
+
 // After staging: true (block-uniform) when some thread's poll failed (data
 // sentinels); with events, only the barrier the caller asks for (bar).
 template <bool SENT>
@@ -259,7 +269,7 @@ template <bool SENT = false, class Wait>
 MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait) {
   const int H = P.H, l = in.layer;
   const int R = (P.nq + 2 * P.nkv) * P.d;
-  float *xs = smem, *red = smem + H;
+  float *xs = smem, *red = smem + H, *ob = smem + H + 96;
   const MkLayerW W = cld(&P.layers[l]);
   const int qd = P.nq * P.d, kd = P.nkv * P.d, r0 = in.r0, n = in.r1 - in.r0;
   auto rowptr = [&](int r) -> const uint16_t * {
@@ -287,9 +297,10 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
       if ((mk_tid() & 63) == 0)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (g0 + j < n) stc(out + g0 + j, acc[j]);
+          if (g0 + j < n) ob[g0 + j] = acc[j];
     });
     if (!ok) return MK_ST_ABORT;
+    flush_rows(out, ob, n);
     __syncthreads();
   }
   return MK_ST_SIGNAL;
@@ -304,6 +315,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
   float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
   const MkLayerW W = cld(&P.layers[l]);
   const int r0 = in.r0, n = in.r1 - in.r0;
+  float *ob = res + ((n + 3) & ~3);
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {
@@ -327,9 +339,10 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
                                       if ((mk_tid() & 63) == 0)
 #pragma unroll
                                         for (int j = 0; j < 4; ++j)
-                                          if (g0 + j < n) stc(out + r0 + g0 + j, res[g0 + j] + acc[j]);
+                                          if (g0 + j < n) ob[g0 + j] = res[g0 + j] + acc[j];
                                     });
     if (!ok) return MK_ST_ABORT;
+    flush_rows(out + r0, ob, n);
     __syncthreads();
   }
   return MK_ST_SIGNAL;
@@ -341,7 +354,7 @@ MKD int op_oproj(const MkProgram &P, const MkStep &S, const MkInstr &in, float *
 template <bool SENT = false, class Wait, class Before>
 MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, Wait &wait, Before &before) {
   const int H = P.H, l = in.layer;
-  float *xs = smem, *red = smem + H;
+  float *xs = smem, *red = smem + H, *ob = smem + H + 96;
   const MkLayerW W = cld(&P.layers[l]);
   const int r0 = in.r0, n = 2 * (in.r1 - in.r0);
   for (int b = 0; b < S.batch; ++b) {
@@ -365,10 +378,11 @@ MKD int op_gateup(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
             for (int j = 0; j < 4; j += 2)
               if (g0 + j < n) {
                 const float a = acc[j], u = acc[j + 1];
-                stc(out + r0 + ((g0 + j) >> 1), (a / (1.0f + expf(-a))) * u);
+                ob[(g0 + j) >> 1] = (a / (1.0f + expf(-a))) * u;
               }
         });
     if (!ok) return MK_ST_ABORT;
+    flush_rows(out + r0, ob, n >> 1);
     __syncthreads();
   }
   return MK_ST_SIGNAL;
@@ -381,6 +395,7 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
   float *xs = smem, *res = smem + K + 96;  // res: residual inputs of the rows [r0, r1)
   const MkLayerW W = cld(&P.layers[l]);
   const int r0 = in.r0, n = in.r1 - in.r0;
+  float *ob = res + ((n + 3) & ~3);
   for (int b = 0; b < S.batch; ++b) {
     const float *h = P.hbuf + ((size_t)l * P.B_max + b) * K;
     const float *xm = P.xmid + ((size_t)l * P.B_max + b) * H;
@@ -397,9 +412,10 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
                                       if ((mk_tid() & 63) == 0)
 #pragma unroll
                                         for (int j = 0; j < 4; ++j)
-                                          if (g0 + j < n) stc(out + r0 + g0 + j, res[g0 + j] + acc[j]);
+                                          if (g0 + j < n) ob[g0 + j] = res[g0 + j] + acc[j];
                                     });
     if (!ok) return MK_ST_ABORT;
+    flush_rows(out + r0, ob, n);
     __syncthreads();
   }
   return MK_ST_SIGNAL;
@@ -463,7 +479,7 @@ template <bool SENT = false, class Wait>
 MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float *smem, int *s_flag, Wait &wait) {
   const int H = P.H, L = P.L, V = P.V;
   const int tid = mk_tid(), lane = tid & 63, wave = tid >> 6;
-  float *xs = smem, *red = smem + H;
+  float *xs = smem, *red = smem + H, *ob = smem + H + 96;  // ob: this instruction's logits
   float *wv = red + MK_NWAVES;            // [MK_NWAVES] best value per wave
   int *wi = reinterpret_cast<int *>(wv + MK_NWAVES);  // [MK_NWAVES] best index per wave
   const uint16_t *Wlm = P.tied ? P.embed : P.lm_head;
@@ -487,7 +503,7 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
       for (int j = 0; j < 4; ++j)
         if (g0 + j < n) {
           const int row = r0 + g0 + j;
-          if (lane == 0) lg[row] = acc[j];
+          if (lane == 0) ob[g0 + j] = acc[j];
           if (better(acc[j], row, bv, bi)) {
             bv = acc[j];
             bi = row;
@@ -499,6 +515,8 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
       wv[wave] = bv;
       wi[wave] = bi;
     }
+    lds_barrier();
+    for (int i = tid; i < n; i += MK_BLOCK) gst(lg + r0 + i, ob[i]);
     __syncthreads();
     if (tid == 0) {
       float v = wv[0];
