@@ -58,6 +58,8 @@ MKD int32_t ldci(const int32_t *p) { return __hip_atomic_load((MK_G(int32_t) *)p
 MKD void stci(int32_t *p, int32_t v) { __hip_atomic_store((MK_G(int32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MKD uint32_t ldcu(const uint32_t *p) { return __hip_atomic_load((MK_G(uint32_t) *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MKD void stcu(uint32_t *p, uint32_t v) { __hip_atomic_store((MK_G(uint32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD uint64_t ldc64(const uint64_t *p) { return __hip_atomic_load((MK_G(uint64_t) *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MKD void stc64(uint64_t *p, uint64_t v) { __hip_atomic_store((MK_G(uint64_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MKD uint32_t addcu(uint32_t *p, uint32_t v) { return __hip_atomic_fetch_add((MK_G(uint32_t) *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 // plain global store / load (no coherence requirement)
 template <class T> MKD void gst(T *p, T v) { *(MK_G(T) *)p = v; }

@@ -423,27 +423,44 @@ MKD int op_down(const MkProgram &P, const MkStep &S, const MkInstr &in, float *s
 
 // ------------------------------------------ LM head + greedy argmax
 
-// Every LM-head instruction has stored its (max, index) partial per sequence:
-// take a ticket; the last arriver merges all partials into the greedy token
-// (and, with MK_ADVANCE, feeds it back as the next input).
-MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
+// Greedy-token merge.  Every LM-head instruction publishes, per sequence, its
+// best (value, row) tagged with the step in one 64-bit device-scope store:
+// value bits << 32 | row << 15 | (epoch + 1) mod 2^15 (row 0x1ffff: every
+// logit was NaN).  The one instruction the planner marks (split = 1, the last
+// of the breadth-first queue, so in the work-queue engine no instruction is
+// held behind it) polls every part until all carry this step's tag, merges
+// them (largest value, lowest row among equal values) and publishes the
+// token; the others just store.  No ticket: all parts arriving on one counter
+// serialised at the memory side.
+MKD uint64_t lm_pack(float v, int ix, uint32_t epoch) {
+  const uint32_t row = ix < 0 || ix > MK_MAX_VOCAB ? 0x1ffffu : (uint32_t)ix;
+  return (uint64_t)__float_as_uint(v) << 32 | (uint64_t)row << 15 | ((epoch + 1u) & 0x7fffu);
+}
+
+MKD int lm_merge(const MkProgram &P, const MkStep &S, const MkInstr &in) {
+  if (in.split != 1) return MK_ST_QUIET;
   const int tid = mk_tid(), lane = tid & 63;
-  wait_vm();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = addcu(P.tickets + in.ticket, 1u);
-    *s_flag = (old + 1u == (S.epoch + 1u) * (uint32_t)P.n_lm_parts) ? 1 : 0;
-  }
-  __syncthreads();
-  const int last = *s_flag;
-  __syncthreads();
-  // last arriver: one wave per sequence merges every instruction's (max, index) pair
-  for (int b = tid >> 6; last && b < S.batch; b += MK_NWAVES) {
+  const uint32_t tag = (S.epoch + 1u) & 0x7fffu;
+  bool ok = true;
+  // one wave per sequence merges every part's record
+  for (int b = tid >> 6; b < S.batch; b += MK_NWAVES) {
     float v = -INFINITY;
     int ix = 0x7fffffff;
     for (int k = lane; k < P.n_lm_parts; k += 64) {
-      const float pv = ldc(P.lm_val + (size_t)k * P.B_max + b);
-      const int pi = ldci(P.lm_idx + (size_t)k * P.B_max + b);
+      const uint64_t *src = P.lm_pk + (size_t)k * P.B_max + b;
+      uint64_t e = ldc64(src);
+      uint32_t spins = 0;
+      uint64_t t0 = 0;
+      while (ok && (uint32_t)(e & 0x7fffu) != tag) {
+        if (poll_fail(P, spins, t0, 0x30002)) {
+          ok = false;
+          break;
+        }
+        e = ldc64(src);
+      }
+      const uint32_t row = (uint32_t)(e >> 15) & 0x1ffffu;
+      const float pv = __uint_as_float((uint32_t)(e >> 32));
+      const int pi = row == 0x1ffffu ? 0x7fffffff : (int)row;
       if (better(pv, pi, v, ix)) {
         v = pv;
         ix = pi;
@@ -458,7 +475,7 @@ MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
         ix = oi;
       }
     }
-    if (lane == 0) {
+    if (lane == 0 && ok) {
       if (ix == 0x7fffffff) ix = 0;  // every logit NaN: fall back to token 0
       if (S.next) stci(S.next + b, ix);
       if (S.flags & 1u) {
@@ -467,11 +484,11 @@ MKD int lm_finish(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
       }
     }
   }
-  if (last) {  // the step's tokens are out: publish its epoch
-    wait_vm();
-    __syncthreads();
-    if (tid == 0) stcu(P.lm_done, S.epoch + 1u);
-  }
+  if (__syncthreads_or(!ok)) return MK_ST_ABORT;
+  // the step's tokens are out: publish its epoch
+  wait_vm();
+  __syncthreads();
+  if (tid == 0) stcu(P.lm_done, S.epoch + 1u);
   return MK_ST_QUIET;
 }
 
@@ -526,10 +543,9 @@ MKD int op_lmhead(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
           v = wv[w];
           ix = wi[w];
         }
-      stc(P.lm_val + (size_t)in.part * P.B_max + b, v);
-      stci(P.lm_idx + (size_t)in.part * P.B_max + b, ix);
+      stc64(P.lm_pk + (size_t)in.part * P.B_max + b, lm_pack(v, ix, S.epoch));
     }
     __syncthreads();
   }
-  return lm_finish(P, S, in, s_flag);
+  return lm_merge(P, S, in);
 }

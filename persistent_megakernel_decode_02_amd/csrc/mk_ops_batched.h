@@ -428,10 +428,10 @@ MKD int op_lmhead_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int 
         ix = wi;
       }
     }
-    stc(P.lm_val + (size_t)in.part * P.B_max + tid, v);
-    stci(P.lm_idx + (size_t)in.part * P.B_max + tid, ix);
+    stc64(P.lm_pk + (size_t)in.part * P.B_max + tid, lm_pack(v, ix, S.epoch));
   }
-  return lm_finish(P, S, in, s_flag);
+  __syncthreads();
+  return lm_merge(P, S, in);
 }
 
 // ------------------------------------------- attention on the matrix cores

@@ -30,6 +30,7 @@
 // stream engine: streamer waves per workgroup (the last wave synchronises)
 #define MK_STREAMERS (MK_NWAVES - 1)
 
+#define MK_MAX_VOCAB 131070                // token rows fit 17 bits (0x1ffff: no row)
 #define MK_MFMA_MIN_BATCH 2                   // sequences from which projections run on MFMA
 #define MK_BKC 2048                           // input columns staged in LDS per chunk
 #define MK_BROW (MK_BKC * 2 + 16)             // bytes per sequence row of one bf16 plane (+16: bank skew)
@@ -143,6 +144,7 @@ struct MkProgram {
   float *hbuf;   // [L][B][I]
   float *xout;   // [L][B][H]
   float *part;   // [L][B][nkv][S][G][d + 2]   (m, l, o[d]) per split and q head
+  uint64_t *lm_pk; // [n_lm_parts][B] tagged (value, row) of the homogeneous engine's LM-head parts
   float *lm_val; // [n_lm_parts][B]
   int32_t *lm_idx;
 

@@ -43,6 +43,7 @@ static int check_shape(const mk_model_shape *s, const mk_plan_opts *o) {
   if (s->hidden % 256 || s->ffn % 256 || (s->n_q_heads * s->head_dim) % 256) return MK_ERR_SHAPE;
   if (!(s->rms_eps > 0) || !(s->rope_theta > 1)) return MK_ERR_SHAPE;
   if (o->max_batch < 1 || o->max_batch > MK_MAX_BATCH) return MK_ERR_INVALID_ARG;
+  if (s->vocab > MK_MAX_VOCAB) return MK_ERR_SHAPE;  // a token index fits the tagged argmax record
   if (o->max_ctx < 1 || o->max_ctx > (1 << 20)) return MK_ERR_INVALID_ARG;
   if (o->kv_splits < 0 || o->kv_splits > o->max_ctx) return MK_ERR_INVALID_ARG;
   if (o->sync_mode < MK_SYNC_COUNTER || o->sync_mode > MK_SYNC_SENTINEL) return MK_ERR_INVALID_ARG;
@@ -211,6 +212,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.ctr = take(4 * std::max(p->n_events, 1));
   y.flags = take(4 * std::max(p->n_flags, 1));
   y.tickets = take(4 * std::max(p->n_tickets, 1));
+  y.lm_pk = take(8 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.lm_done = take(4);
   y.queue_ctr = take(4);
   y.err = take(16);
@@ -559,7 +561,8 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
     }
   }
 
-  // 1. structure: fields in range, lists level-sorted
+  // 1. structure: fields in range, lists level-sorted, one token merger
+  int n_merge = 0;
   for (int i = 0; i < n; ++i) {
     const MkInstr &in = p->instr[i];
     if (p->instr_cu[i] < 0 || p->instr_cu[i] >= p->n_cu) return MK_ERR_PLAN;
@@ -588,11 +591,14 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
       case MKOP_LMHEAD:
         if (in.r0 < 0 || in.r1 > ck.V || in.r0 >= in.r1 || in.ticket < 0) return MK_ERR_PLAN;
         if (in.part < 0 || in.part >= p->n_lm_parts) return MK_ERR_PLAN;
+        if (in.split != 0 && in.split != 1) return MK_ERR_PLAN;
+        n_merge += in.split;
         break;
       default:
         return MK_ERR_PLAN;
     }
   }
+  if (n_merge != 1) return MK_ERR_PLAN;
   for (int c = 0; c < p->n_cu; ++c)
     for (int i = p->cu_begin[c] + 1; i < p->cu_begin[c + 1]; ++i)
       if (p->instr[i].level < p->instr[i - 1].level) return MK_ERR_PLAN;
@@ -1086,5 +1092,11 @@ int mk_plan_normalize_events(mk_plan_t *p) {
       p->queue.push_back(i);
     }
   }
+  // the LM-head instruction that merges the greedy tokens: the last one
+  // handed out, so a work-queue workgroup that runs it holds nothing else
+  for (MkInstr &in : p->instr)
+    if (in.op == MKOP_LMHEAD) in.split = 0;
+  if (p->queue.empty() || p->instr[p->queue.back()].op != MKOP_LMHEAD) return MK_ERR_PLAN;
+  p->instr[p->queue.back()].split = 1;
   return MK_OK;
 }

@@ -13,7 +13,7 @@
 // engine's program record for odd steps in sentinel mode
 struct MkLayout {
   size_t prog, prog_odd, instr, cu_begin, level_begin, level_list, queue, ev_count, ev_flag_base, rope, layers, rowtab;
-  size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, lm_done, queue_ctr, err;
+  size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, lm_pk, lm_done, queue_ctr, err;
   size_t sync_begin, sync_end;  // [ctr .. err] zeroed on create/reset
   size_t total;
 };
