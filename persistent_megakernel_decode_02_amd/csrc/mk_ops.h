@@ -272,12 +272,12 @@ MKD int op_qkv(const MkProgram &P, const MkStep &S, const MkInstr &in, float *sm
   float *xs = smem, *red = smem + H, *ob = smem + H + 96;
   const MkLayerW W = cld(&P.layers[l]);
   const int qd = P.nq * P.d, kd = P.nkv * P.d, r0 = in.r0, n = in.r1 - in.r0;
-  auto rowptr = [&](int r) -> const uint16_t * {
-    const int row = r0 + r;
-    if (row < qd) return W.wq + (size_t)row * H;
-    if (row < qd + kd) return W.wk + (size_t)(row - qd) * H;
-    return W.wv + (size_t)(row - qd - kd) * H;
-  };
+  // the planner keeps a slice inside one head, so inside one of q, k, v: its
+  // first row decides the tensor
+  const uint16_t *base = r0 < qd ? W.wq + (size_t)r0 * H
+                         : r0 < qd + kd ? W.wk + (size_t)(r0 - qd) * H
+                                        : W.wv + (size_t)(r0 - qd - kd) * H;
+  auto rowptr = [&](int r) -> const uint16_t * { return base + (size_t)r * H; };
   for (int b = 0; b < S.batch; ++b) {
     int tok = 0;
     if (l == 0 && !token_ok(P, S, b, &tok)) {

@@ -263,12 +263,12 @@ MKD int op_qkv_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wa
   const int R = (P.nq + 2 * P.nkv) * P.d, qd = P.nq * P.d, kd = P.nkv * P.d;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
   const MkLayerW W = cld(&P.layers[l]);
-  auto rowptr = [&](int v) -> const uint16_t * {
-    const int row = r0 + min(v, nr - 1);
-    if (row < qd) return W.wq + (size_t)row * H;
-    if (row < qd + kd) return W.wk + (size_t)(row - qd) * H;
-    return W.wv + (size_t)(row - qd - kd) * H;
-  };
+  // the slice lies inside one of q, k, v (the planner keeps it inside one
+  // head): a per-lane choice of the tensor became a lookup table in scratch
+  const uint16_t *base = r0 < qd ? W.wq + (size_t)r0 * H
+                         : r0 < qd + kd ? W.wk + (size_t)(r0 - qd) * H
+                                        : W.wv + (size_t)(r0 - qd - kd) * H;
+  auto rowptr = [&](int v) -> const uint16_t * { return base + (size_t)min(v, nr - 1) * H; };
   float *out = P.qkv + (size_t)l * P.B_max * R + r0;
   auto fin = [&](int tile, mk_f32x4v a) {
     const int v = 16 * tile + (lane & 15), b0 = 4 * (lane >> 4);

@@ -573,9 +573,14 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
     if (in.ticket < -1 || in.ticket >= p->n_tickets) return MK_ERR_PLAN;
     const int l = in.layer;
     switch (in.op) {
-      case MKOP_QKV:
+      case MKOP_QKV: {
         if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.R || in.r0 >= in.r1) return MK_ERR_PLAN;
+        // a slice lies inside one of the q, k and v weight matrices
+        const int qd = ck.nq * ck.d, kd = ck.nkv * ck.d;
+        auto part_of = [&](int r) { return r < qd ? 0 : r < qd + kd ? 1 : 2; };
+        if (part_of(in.r0) != part_of(in.r1 - 1)) return MK_ERR_PLAN;
         break;
+      }
       case MKOP_ATTN:
         if (l < 0 || l >= L || in.r0 < 0 || in.r0 >= ck.B || in.r1 < 0 || in.r1 >= ck.nkv) return MK_ERR_PLAN;
         if (in.nsplit != p->S || in.split < 0 || in.split >= in.nsplit) return MK_ERR_PLAN;
