@@ -130,11 +130,6 @@ MKD T cld(const T *p) {
 // wait until this wave's outstanding memory operations (stores included) completed
 MKD void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-MKD float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 MKD float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -157,6 +152,11 @@ MKD float wave_total(float v) {
   v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Sum over the wave (all 64 lanes active), returned to every lane.  DPP
+// moves instead of cross-lane LDS permutes: the GEMV finishes each row group
+// with one of these per row, and six dependent LDS round trips per row group
+// sat on the dependency chain of every projection.
+MKD float wave_sum(float v) { return wave_total(v); }
 // DPP move where lanes without a source (masked rows) keep their own value
 template <int CTRL, int ROWMASK>
 MKD float dpp_keep(float v) {
