@@ -157,6 +157,27 @@ MKD float wave_total(float v) {
 // with one of these per row, and six dependent LDS round trips per row group
 // sat on the dependency chain of every projection.
 MKD float wave_sum(float v) { return wave_total(v); }
+// Combine each lane's value with the one 16 or 32 lanes away (lane ^ 16,
+// lane ^ 32) with the gfx950 lane swaps (v_permlane16_swap_b32: odd 16-lane
+// rows against even rows; v_permlane32_swap_b32: upper half against lower
+// half) instead of cross-lane LDS permutes.  The swap returns both partners
+// in every lane, in the same order for the two lanes of a pair.
+MKD float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+MKD float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+MKD float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+MKD float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // DPP move where lanes without a source (masked rows) keep their own value
 template <int CTRL, int ROWMASK>
 MKD float dpp_keep(float v) {

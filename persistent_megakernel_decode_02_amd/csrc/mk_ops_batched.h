@@ -616,8 +616,8 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
     // online softmax of head `col` (lanes col, col + 16, col + 32, col + 48 share it)
     float mb = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    mb = max_x16(mb);
+    mb = max_x32(mb);
     const float mn = fmaxf(m, mb);
     const float c = m == mn ? 1.f : exp2_fast(m - mn);
     float pr[8];
@@ -662,8 +662,8 @@ MKD int op_attn_d(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s
       if (u0 + MK_NWAVES * i < nu) process(ring[i], u0 + MK_NWAVES * i);
   }
   // wave partials per head: max, sum, unnormalised output (base-2 scores)
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = sum_x16(lsum);
+  lsum = sum_x32(lsum);
   lds_float *wpa = (lds_float *)(L + MK_FA_WP);
   lds_float *wp = wpa + wave * MK_MAX_GROUP * (D + 2);
   if (lane < G) {

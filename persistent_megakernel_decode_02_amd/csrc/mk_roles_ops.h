@@ -591,8 +591,8 @@ MKD bool attn_instr_d(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0,
     // online softmax for head `col` (its four lane rows share the max)
     float mb = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    mb = max_x16(mb);
+    mb = max_x32(mb);
     const float mn = fmaxf(m, mb);
     const float c = m == mn ? 1.f : exp2_fast(m - mn);
     float pr[8];
@@ -644,8 +644,8 @@ MKD bool attn_instr_d(const MkRole &R, const MkGeo &g, uint32_t seq0, int slot0,
     slot = ring_add(slot, MK_NCW * 2, R.np);
   }
   // this wave's partial per head: max, sum, unnormalised output (base-2 scores)
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_x16(l);
+  l = sum_x32(l);
   lds_float *wp = attn_wpart(R, cw);
   if (lane < G) {
     wp[lane * (D + 2)] = m;
