@@ -88,8 +88,10 @@ def test_plan_llama1b_one_gemv_slice_per_cu():
 def test_flat_plan_keeps_attention_cus_out_of_o_and_gateup():
     """Homogeneous engine, one sequence: every layer's O and gate/up slices go
     to CUs that run none of that layer's attention, while every row is still
-    covered exactly once and the plan validates and simulates; with 176
-    attention units (position 8192) the exclusion is off."""
+    covered exactly once and the plan validates and simulates.  At position
+    8192 the default splits stop at 3/8 of the CUs (12 splits, 96 units:
+    the exclusion holds); with 22 splits asked for (176 units, over half the
+    CUs) the exclusion is off."""
     shape, batch, max_ctx = SHAPES["llama1b_pos1024"]
     plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256,
                                                            exec_mode=mk.MK_EXEC_FLAT,
@@ -112,6 +114,16 @@ def test_flat_plan_keeps_attention_cus_out_of_o_and_gateup():
         mk.mk_plan_destroy(plan)
     shape, batch, max_ctx = SHAPES["llama1b_pos8192"]
     plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256,
+                                                           exec_mode=mk.MK_EXEC_FLAT))
+    try:
+        descs = mk.mk_plan_export(plan)
+        attn = {d.cu for d in descs if d.op == mk.MK_OP_ATTN and d.layer == 0}
+        assert max(d.n_splits for d in descs if d.op == mk.MK_OP_ATTN) == 12 and len(attn) == 96
+        o_cus = {d.cu for d in descs if d.op == mk.MK_OP_OPROJ and d.layer == 0}
+        assert len(o_cus) <= 256 - 96 and not attn & o_cus
+    finally:
+        mk.mk_plan_destroy(plan)
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, kv_splits=22, num_cus=256,
                                                            exec_mode=mk.MK_EXEC_FLAT))
     try:
         descs = mk.mk_plan_export(plan)
