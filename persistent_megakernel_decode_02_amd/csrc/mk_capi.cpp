@@ -489,6 +489,14 @@ int mk_load_weights(mk_ctx *c, const mk_weights *wt, void *stream) {
   c->prog.final_norm = (const uint16_t *)wt->final_norm;
   build_rowtab(c);
   hipStream_t st = (hipStream_t)stream;
+  // batched plans: the LM-head matrix as operand-order tiles in the workspace
+  c->prog.lm_tiled = nullptr;
+  const MkLayout &y = c->plan.lay;
+  if (y.lm_tiled_bytes) {
+    uint16_t *dst = (uint16_t *)(c->ws + y.lm_tiled);
+    if (mk_launch_tile_rows(c->prog.lm_head, s.vocab, s.hidden, dst, st)) return MK_ERR_HIP;
+    c->prog.lm_tiled = dst;
+  }
   int rc = upload_prog(c, st);
   if (rc == MK_OK && hipStreamSynchronize(st) != hipSuccess) rc = MK_ERR_HIP;
   if (rc == MK_OK) c->weights = true;

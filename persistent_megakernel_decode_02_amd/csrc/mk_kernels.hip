@@ -326,6 +326,23 @@ extern "C" __global__ void mk_fill_kernel(uint32_t *p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Repack a row-major bf16 matrix [rows][K] (K a multiple of 32) into 1 KiB
+// operand-order tiles: tile (T, j) holds rows 16 T .. + 15 and columns
+// 32 j .. + 31, its 16-byte piece L being row 16 T + L % 16, columns
+// 32 j + 8 (L / 16) .. + 7; rows past the end are zero.  One thread per
+// piece.
+extern "C" __global__ void mk_tile_rows_kernel(const uint16_t *src, int rows, int K, uint16_t *dst, size_t n_pieces) {
+  const int J = K >> 5;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pieces; i += (size_t)gridDim.x * blockDim.x) {
+    const int L = (int)(i & 63);
+    const size_t tj = i >> 6, T = tj / J, j = tj - T * J;
+    const size_t row = 16 * T + (L & 15), c = 32 * j + 8 * (L >> 4);
+    mk_u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < (size_t)rows) v = *(const mk_u32x4 *)(src + row * K + c);
+    *(mk_u32x4 *)(dst + 8 * i) = v;
+  }
+}
+
 // Persistent kernels and the dynamic-LDS limit of each, as last set in this
 // process.  Launches compare against it and call hipFuncSetAttribute only
 // when it differs (a context binds it once; a later occupancy query may have
@@ -436,6 +453,15 @@ int mk_occupancy_role(int lds, int *blocks_per_cu) {
     return -1;
   *blocks_per_cu = nb;
   return 0;
+}
+
+int mk_launch_tile_rows(const uint16_t *src, int rows, int K, uint16_t *dst, hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K & 31) != 0) return -1;
+  const size_t n_pieces = (size_t)(rows + 15) / 16 * (size_t)(K >> 5) * 64;
+  size_t blocks = (n_pieces + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(mk_tile_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, rows, K, dst, n_pieces);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s) {

@@ -30,6 +30,9 @@ int mk_launch_queue(const MkProgram *d_prog, const MkStep &st, int n_cu, int lds
 int mk_launch_role_level(const MkProgram *d_prog, const MkStep &st, int n_blocks, int lds, hipStream_t s);
 int mk_occupancy_role(int lds, int *blocks_per_cu);
 int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s);
+// repack a row-major bf16 matrix [rows][K] into operand-order 1 KiB tiles
+// (K a multiple of 32; dst holds ceil(rows / 16) * 16 * K elements)
+int mk_launch_tile_rows(const uint16_t *src, int rows, int K, uint16_t *dst, hipStream_t s);
 int mk_occupancy_mega(int lds, int *blocks_per_cu);
 
 // measurement kernels (mk_measure.hip)

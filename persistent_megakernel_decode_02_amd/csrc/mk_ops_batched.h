@@ -147,7 +147,13 @@ MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16
 // row 16 tile + lane % 16, sequences 4 (lane / 16) + j).  `wait` (the
 // instruction's dependency wait) runs once the first weights are in flight
 // when `first`; false from it aborts.
-template <int TPW, int PF, class Src, class RowPtr, class Fin, class Wait>
+//
+// TILED: the weights are stored as 1 KiB tiles in the operand order (tile
+// (T, j): rows 16 T .. + 15, columns 32 j .. + 31, lane L's 16 bytes = row
+// 16 T + L % 16, columns 32 j + 8 (L / 16) .. + 7), so every load
+// instruction reads 1 KiB contiguous instead of 16 rows x 64 bytes; rowptr
+// then gives the lane's address in step 0 of the tile.
+template <int TPW, int PF, bool TILED, class Src, class RowPtr, class Fin, class Wait>
 MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, const uint16_t *gain, float eps,
                    RowPtr rowptr, Fin fin, Wait wait) {
   lds_char *L = (lds_char *)mk_flat_lds;
@@ -160,6 +166,8 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
     const int c = min(j / per, nch - 1), s = j - c * per;
     return c * MK_BKC + 32 * (kp * (c == nch - 1 ? perl : per) + s) + 8 * q;
   };
+  // element offset of step j's 16 bytes from the lane's row / tile pointer
+  auto woff = [&](int j) -> size_t { return TILED ? (size_t)(col(j) >> 5) * 512 : (size_t)col(j); };
   const uint16_t *wrow[TPW];
   bool live[TPW];
 #pragma unroll
@@ -174,7 +182,7 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
     for (int p = 0; p < PF; ++p)
       if (p < J)
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + col(p)));
+        for (int t = 0; t < TPW; ++t) w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + woff(p)));
   if (first && !wait()) return false;
   const float rs = (gain && nch > 1) ? bnorm_rs(src, K, eps) : 1.f;
   mk_f32x4v acc[TPW];
@@ -203,7 +211,7 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
             if (jn < J)
 #pragma unroll
               for (int t = 0; t < TPW; ++t)
-                w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + col(jn)));
+                w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + woff(jn)));
           }
         }
       }
@@ -226,22 +234,23 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
 // Y[b][r] for the instruction's nt tiles of 16 rows (rowptr(v): weight row
 // of virtual row v in [0, 16 nt), already clamped to a valid row), inputs
 // from src (K columns, RMSNorm with `gain` when non-null).
-template <class Src, class RowPtr, class Fin, class Wait>
+template <bool TILED = false, class Src, class RowPtr, class Fin, class Wait>
 MKD bool bgemm(const Src &src, int K, int nt, const uint16_t *gain, float eps, RowPtr rowptr, Fin fin, Wait wait) {
   // up to 16 steps (64 registers) of weights in flight per wave
-  if (nt == 1) return bgemm_run<1, 8>(src, K, 0, nt, 8, true, gain, eps, rowptr, fin, wait);
-  if (nt == 2) return bgemm_run<1, 16>(src, K, 0, nt, 4, true, gain, eps, rowptr, fin, wait);
-  if (nt < MK_NWAVES) return bgemm_run<1, 16>(src, K, 0, nt, nt <= 4 ? 2 : 1, true, gain, eps, rowptr, fin, wait);
+  if (nt == 1) return bgemm_run<1, 8, TILED>(src, K, 0, nt, 8, true, gain, eps, rowptr, fin, wait);
+  if (nt == 2) return bgemm_run<1, 16, TILED>(src, K, 0, nt, 4, true, gain, eps, rowptr, fin, wait);
+  if (nt < MK_NWAVES)
+    return bgemm_run<1, 16, TILED>(src, K, 0, nt, nt <= 4 ? 2 : 1, true, gain, eps, rowptr, fin, wait);
   for (int g0 = 0; g0 < nt; g0 += 4 * MK_NWAVES) {
     const int ng = min(nt - g0, 4 * MK_NWAVES);
     const bool first = g0 == 0;
     bool ok;
     if (ng > 2 * MK_NWAVES)
-      ok = bgemm_run<4, 4>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<4, 4, TILED>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else if (ng > MK_NWAVES)
-      ok = bgemm_run<2, 8>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<2, 8, TILED>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     else
-      ok = bgemm_run<1, 8>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
+      ok = bgemm_run<1, 8, TILED>(src, K, g0, ng, 1, first, gain, eps, rowptr, fin, wait);
     if (!ok) return false;
   }
   return true;
@@ -392,9 +401,18 @@ MKD int op_lmhead_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int 
           }
         }
   };
-  if (!bgemm(bact(P.xout + (size_t)(P.L - 1) * P.B_max * H, nb, H), H, nt, P.final_norm, P.eps,
-             [&](int v) { return Wlm + (size_t)(r0 + min(v, nr - 1)) * H; }, fin, wait))
-    return MK_ST_ABORT;
+  const BActSrc xsrc = bact(P.xout + (size_t)(P.L - 1) * P.B_max * H, nb, H);
+  bool ok;
+  if (P.lm_tiled && (r0 & 15) == 0) {
+    // the tiled copy of the LM-head matrix (tiles of global rows 16 T ..)
+    const uint16_t *tb = P.lm_tiled + (size_t)(r0 >> 4) * (H >> 5) * 512 + 8 * lane;
+    ok = bgemm<true>(xsrc, H, nt, P.final_norm, P.eps,
+                     [&](int v) { return tb + (size_t)(v >> 4) * (H >> 5) * 512; }, fin, wait);
+  } else {
+    ok = bgemm(xsrc, H, nt, P.final_norm, P.eps, [&](int v) { return Wlm + (size_t)(r0 + min(v, nr - 1)) * H; }, fin,
+               wait);
+  }
+  if (!ok) return MK_ST_ABORT;
   // best per sequence: over the 16 rows of a lane group, then over waves
 #pragma unroll
   for (int j = 0; j < 4; ++j)

@@ -136,6 +136,9 @@ struct MkProgram {
   MkLayerW *layers;            // [L]
   const MkRowTab *rowtab;      // [n_instr] (stream engine)
   const uint16_t *embed, *lm_head, *final_norm;
+  // batched plans: the LM-head matrix repacked as 1 KiB operand-order tiles
+  // (16 rows x 32 columns, rows padded to a multiple of 16 with zeros), or null
+  const uint16_t *lm_tiled;
 
   // activations (fp32), one buffer per layer so no slot is rewritten in a step
   float *qkv;    // [L][B][(nq + 2 nkv) d]
