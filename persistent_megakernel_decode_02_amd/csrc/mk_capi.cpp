@@ -497,6 +497,15 @@ int mk_load_weights(mk_ctx *c, const mk_weights *wt, void *stream) {
     if (mk_launch_tile_rows(c->prog.lm_head, s.vocab, s.hidden, dst, st)) return MK_ERR_HIP;
     c->prog.lm_tiled = dst;
   }
+  c->prog.gu_tiled = nullptr;
+  if (y.gu_tiled_bytes) {
+    uint16_t *dst = (uint16_t *)(c->ws + y.gu_tiled);
+    for (int l = 0; l < L; ++l)
+      if (mk_launch_tile_pairs(c->layers[l].wg, c->layers[l].wu, s.ffn, s.hidden, dst + (size_t)l * 2 * s.ffn * s.hidden,
+                               st))
+        return MK_ERR_HIP;
+    c->prog.gu_tiled = dst;
+  }
   int rc = upload_prog(c, st);
   if (rc == MK_OK && hipStreamSynchronize(st) != hipSuccess) rc = MK_ERR_HIP;
   if (rc == MK_OK) c->weights = true;

@@ -455,6 +455,29 @@ int mk_occupancy_role(int lds, int *blocks_per_cu) {
   return 0;
 }
 
+// The same tiles for a pair of matrices [units][K] read together: tile T
+// holds units 8 T .. + 7, rows 0-7 from `a`, rows 8-15 from `b` (units a
+// multiple of 8).
+extern "C" __global__ void mk_tile_pairs_kernel(const uint16_t *a, const uint16_t *b, int K, uint16_t *dst,
+                                                size_t n_pieces) {
+  const int J = K >> 5;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pieces; i += (size_t)gridDim.x * blockDim.x) {
+    const int L = (int)(i & 63), r = L & 15;
+    const size_t tj = i >> 6, T = tj / J, j = tj - T * J;
+    const size_t unit = 8 * T + (r & 7), c = 32 * j + 8 * (L >> 4);
+    *(mk_u32x4 *)(dst + 8 * i) = *(const mk_u32x4 *)((r < 8 ? a : b) + unit * K + c);
+  }
+}
+
+int mk_launch_tile_pairs(const uint16_t *a, const uint16_t *b, int units, int K, uint16_t *dst, hipStream_t s) {
+  if (units <= 0 || (units & 7) != 0 || K <= 0 || (K & 31) != 0) return -1;
+  const size_t n_pieces = (size_t)(units / 8) * (size_t)(K >> 5) * 64;
+  size_t blocks = (n_pieces + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(mk_tile_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, b, K, dst, n_pieces);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int mk_launch_tile_rows(const uint16_t *src, int rows, int K, uint16_t *dst, hipStream_t s) {
   if (rows <= 0 || K <= 0 || (K & 31) != 0) return -1;
   const size_t n_pieces = (size_t)(rows + 15) / 16 * (size_t)(K >> 5) * 64;

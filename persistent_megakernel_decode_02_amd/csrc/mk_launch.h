@@ -33,6 +33,8 @@ int mk_launch_fill(void *p, uint32_t v, size_t n_words, hipStream_t s);
 // repack a row-major bf16 matrix [rows][K] into operand-order 1 KiB tiles
 // (K a multiple of 32; dst holds ceil(rows / 16) * 16 * K elements)
 int mk_launch_tile_rows(const uint16_t *src, int rows, int K, uint16_t *dst, hipStream_t s);
+// two matrices [units][K] into tiles of 8 units, rows 0-7 from a, 8-15 from b
+int mk_launch_tile_pairs(const uint16_t *a, const uint16_t *b, int units, int K, uint16_t *dst, hipStream_t s);
 int mk_occupancy_mega(int lds, int *blocks_per_cu);
 
 // measurement kernels (mk_measure.hip)

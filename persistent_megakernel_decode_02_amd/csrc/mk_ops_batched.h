@@ -347,8 +347,17 @@ MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait
       if (n < 8 && u < nh && b0 + j < nb) stc(out + (size_t)(b0 + j) * P.I + u, (g / (1.0f + expf(-g))) * up);
     }
   };
-  if (!bgemm(bact(P.xmid + (size_t)l * P.B_max * H, nb, H), H, nt, W.mlp_norm, P.eps, rowptr, fin, wait))
-    return MK_ST_ABORT;
+  const BActSrc xsrc = bact(P.xmid + (size_t)l * P.B_max * H, nb, H);
+  bool ok;
+  if (P.gu_tiled && (r0 & 7) == 0) {
+    // tile t of this slice is tile r0 / 8 + t of the layer's tiled gate/up copy
+    const uint16_t *tb = P.gu_tiled + (size_t)l * 2 * P.I * H + (size_t)(r0 >> 3) * (H >> 5) * 512 + 8 * lane;
+    ok = bgemm<true>(xsrc, H, nt, W.mlp_norm, P.eps, [&](int v) { return tb + (size_t)(v >> 4) * (H >> 5) * 512; }, fin,
+                     wait);
+  } else {
+    ok = bgemm(xsrc, H, nt, W.mlp_norm, P.eps, rowptr, fin, wait);
+  }
+  if (!ok) return MK_ST_ABORT;
   return MK_ST_SIGNAL;
 }
 

@@ -139,6 +139,9 @@ struct MkProgram {
   // batched plans: the LM-head matrix repacked as 1 KiB operand-order tiles
   // (16 rows x 32 columns, rows padded to a multiple of 16 with zeros), or null
   const uint16_t *lm_tiled;
+  // batched plans: each layer's gate and up matrices as 1 KiB tiles of 8
+  // hidden units (rows 0-7 gate, 8-15 up), layer l at l * 2 I H, or null
+  const uint16_t *gu_tiled;
 
   // activations (fp32), one buffer per layer so no slot is rewritten in a step
   float *qkv;    // [L][B][(nq + 2 nkv) d]

@@ -143,12 +143,13 @@ static void stream_lds_layout(mk_plan_t *p) {
   p->lds_bytes = (int)(o + 256);
 }
 
-// Batched plans of the homogeneous engine multiply the LM head on the
-// matrix cores from a copy of the matrix in operand-order tiles (built by
-// mk_load_weights); the hidden size must be a multiple of the tile width.
-bool mk_plan_tiles_lm(const mk_plan_t *p) {
+// Batched plans of the homogeneous engine multiply the LM head and gate/up
+// on the matrix cores from copies of their matrices in operand-order tiles
+// (built by mk_load_weights); the hidden size must be a multiple of the tile
+// width and the FFN size of the 8-unit gate/up tile.
+bool mk_plan_tiles(const mk_plan_t *p) {
   const int m = p->opts.exec_mode;
-  return p->B >= MK_MFMA_MIN_BATCH && p->shape.hidden % 32 == 0 &&
+  return p->B >= MK_MFMA_MIN_BATCH && p->shape.hidden % 32 == 0 && p->shape.ffn % 8 == 0 &&
          (m == MK_EXEC_FLAT || m == MK_EXEC_FLAT_MULTI || m == MK_EXEC_QUEUE);
 }
 
@@ -207,8 +208,10 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.rope = take(4 * (size_t)p->max_ctx * d);
   y.layers = take(sizeof(MkLayerW) * L);
   y.rowtab = take(sizeof(MkRowTab) * std::max<size_t>(p->instr.size(), 1));
-  y.lm_tiled_bytes = mk_plan_tiles_lm(p) ? (size_t)ceil_div(s.vocab, 16) * 16 * s.hidden * 2 : 0;
+  y.lm_tiled_bytes = mk_plan_tiles(p) ? (size_t)ceil_div(s.vocab, 16) * 16 * s.hidden * 2 : 0;
   y.lm_tiled = y.lm_tiled_bytes ? take(y.lm_tiled_bytes) : 0;
+  y.gu_tiled_bytes = mk_plan_tiles(p) ? L * 2 * I * H * 2 : 0;  // every layer's gate and up rows
+  y.gu_tiled = y.gu_tiled_bytes ? take(y.gu_tiled_bytes) : 0;
   y.qkv = take(4 * L * B * R);
   y.attn = take(4 * L * B * nq * d);
   y.xmid = take(4 * L * B * H);
@@ -284,11 +287,14 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
       B == 1 &&
       (int64_t)B * nkv * S < n_cu / 2)
     og_cus = n_cu - B * nkv * S;
-  const int rg = (int)((ceil_div(I, og_cus) + 3) / 4 * 4), ro = (int)ceil_div(H, og_cus);
+  // gate/up slices: multiples of 4 hidden units (8 when a batched plan
+  // reads the tiled copy, whose tiles hold 8 units' gate and up rows)
+  const int ru = mk_plan_tiles(p) ? 8 : 4;
+  const int rg = (int)((ceil_div(I, og_cus) + ru - 1) / ru * ru), ro = (int)ceil_div(H, og_cus);
   // LM-head slices; a batched plan of the homogeneous engine reads the
   // tiled copy of the matrix, so its slices start on 16-row tile boundaries
   int rl = (int)ceil_div(V, n_cu);
-  if (mk_plan_tiles_lm(p)) rl = (rl + 15) / 16 * 16;
+  if (mk_plan_tiles(p)) rl = (rl + 15) / 16 * 16;
   const int rd = (int)ceil_div(H, n_cu);
   p->n_lm_parts = (int)ceil_div(V, rl);
   p->n_tickets = (S > 1 ? L * B * nkv : 0) + 1;

@@ -15,6 +15,7 @@ struct MkLayout {
   size_t prog, prog_odd, instr, cu_begin, level_begin, level_list, queue, ev_count, ev_flag_base, rope, layers, rowtab;
   size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, lm_pk, lm_done, queue_ctr, err;
   size_t lm_tiled, lm_tiled_bytes;  // batched plans: tiled copy of the LM-head matrix (0 bytes: none)
+  size_t gu_tiled, gu_tiled_bytes;  // batched plans: tiled gate/up rows of every layer (0 bytes: none)
   size_t sync_begin, sync_end;  // [ctr .. err] zeroed on create/reset
   size_t total;
 };
@@ -41,7 +42,7 @@ struct mk_plan_s {
 
 int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_cu, mk_plan_t **out);
 int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed);
-bool mk_plan_tiles_lm(const mk_plan_t *p);
+bool mk_plan_tiles(const mk_plan_t *p);
 // Derive the plan's events from the instructions' data accesses (MPK-style
 // normalisation): at most one wait and one trigger event per instruction,
 // events fused by predecessor set and by successor set, numbered and
