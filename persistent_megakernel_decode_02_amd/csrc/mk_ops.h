@@ -11,7 +11,10 @@
 // -------------------------------------------------------------- GEMV core
 //
 // Dot products of `nrows` weight rows (bf16, K columns, rowptr(r) gives row
-// r) with one fp32 vector xs[K] held in LDS.
+// r) with one fp32 vector x[K] held in LDS in two halves (xs_put): elements
+// 8c .. 8c+3 at xs[4c ..], elements 8c+4 .. 8c+7 at xs[K/2 + 4c ..], so the
+// lanes of a wave read consecutive 16-byte pieces (one 16-byte piece per
+// lane at a 32-byte stride hit every LDS bank twice).
 //
 // Work split.  Rows form groups of NR; a wave owns whole groups.  With fewer
 // groups than waves the waves also split the columns of each group into kp
@@ -46,7 +49,7 @@ MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr
   const int c0 = kpart * pit * 64, c1 = min(nch, c0 + pit * 64);
   const int nb = (pit + U - 1) / U;  // batches per group
   const int T = kpart < kp ? (ng - gw + nw - 1) / nw * nb : 0;
-  const float4 *x4 = reinterpret_cast<const float4 *>(xs);
+  const float4 *x4 = reinterpret_cast<const float4 *>(xs), *x4b = x4 + (K >> 3);
   float acc[NR];
 #pragma unroll
   for (int j = 0; j < NR; ++j) acc[j] = 0.f;
@@ -72,7 +75,7 @@ MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(cb + 64 * u, nch - 1);  // out-of-range chunks carry zero weights
-      const float4 xa = x4[2 * c], xb = x4[2 * c + 1];
+      const float4 xa = x4[c], xb = x4b[c];
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         float a = acc[j];
@@ -128,6 +131,10 @@ MKD bool gemv_rows(int K, int nrows, const float *xs, float *part, RowPtr rowptr
 
 // ------------------------------------------------------- input staging
 //
+// xs_put: elements 4k .. 4k+3 of an n-element GEMV input into the two-half
+// layout gemv_rows reads.
+MKD float *xs_put(float *xs, int n, int k) { return xs + (k & 1) * (n >> 1) + 4 * (k >> 1); }
+//
 // Inputs are staged with 16-byte device-coherent loads, all issued back to
 // back: a chunk past the end reads zero through the descriptor's range, so
 // no load sits under a branch.  n is a multiple of 4.
@@ -149,7 +156,7 @@ MKD void stage_vec(const MkProgram &P, float *xs, const float *src, int n, bool 
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + tid + k * MK_BLOCK;
       if (sent) v[k] = poll16(P, r, c < nc ? c * 16 : MK_OOB, v[k], ok);
-      if (c < nc) *reinterpret_cast<mk_u32x4 *>(xs + 4 * c) = v[k];
+      if (c < nc) *reinterpret_cast<mk_u32x4 *>(xs_put(xs, n, c)) = v[k];
     }
   }
 }
@@ -216,7 +223,7 @@ MKD void stage_norm(const MkProgram &P, float *xs, const float *src, const uint1
   for (int k = 0; k < 4; ++k) {
     const int c = tid + k * MK_BLOCK;
     if (c < nc)
-      *reinterpret_cast<float4 *>(xs + 4 * c) =
+      *reinterpret_cast<float4 *>(xs_put(xs, n, c)) =
           make_float4((x[k].x * rn) * bf_lo(g.w[k][0]), (x[k].y * rn) * bf_hi(g.w[k][0]),
                       (x[k].z * rn) * bf_lo(g.w[k][1]), (x[k].w * rn) * bf_hi(g.w[k][1]));
   }
