@@ -390,6 +390,7 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   P.n_instr = (int32_t)p.instr.size();
   P.n_levels = p.n_levels;
   P.n_events = p.n_events;
+  P.ctr_stride = mk_ctr_stride(p.n_events);
   P.n_lm_parts = p.n_lm_parts;
   P.watchdog_ticks = 200000000u;  // 2 s
   P.lds_x = p.lds_x;

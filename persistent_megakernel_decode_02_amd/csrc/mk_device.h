@@ -362,11 +362,31 @@ MKD float ldcp(const PT &P, const float *p, bool sent, bool &ok) {
   return v;
 }
 
+// This wave's XCD (hardware register XCC_ID, bits 3:0), as a counter row.
+MKD uint32_t mk_xcc_row() {
+  const uint32_t x = __builtin_amdgcn_s_getreg((20) | (3 << 11)) & 15u;
+  return x < (uint32_t)MK_CTR_ROWS ? x : (uint32_t)MK_CTR_ROWS - 1u;
+}
+// Counter mode: count one trigger of event `ev` in this XCD's row.
+MKD void ctr_bump(const MkProgram &P, int ev) { addcu(P.ctr + mk_xcc_row() * (uint32_t)P.ctr_stride + ev, 1u); }
+// Counter mode: triggers of event `ev` so far, summed over the XCD rows (the
+// eight loads are independent, so they share one round trip).
+MKD uint32_t ctr_total(const MkProgram &P, int ev) {
+  uint32_t v[MK_CTR_ROWS];
+#pragma unroll
+  for (int r = 0; r < MK_CTR_ROWS; ++r) v[r] = ldcu(P.ctr + r * P.ctr_stride + ev);
+  uint32_t t = 0;
+#pragma unroll
+  for (int r = 0; r < MK_CTR_ROWS; ++r) t += v[r];
+  return t;
+}
+
 // Wait for event `ev` of this step (global loads issued before the wait stay
-// in flight: the workgroup barriers wait for LDS traffic only).  Counter mode: one lane polls the
-// monotonic counter until it reaches (epoch+1) * triggers.  Flag mode: one
-// wave polls all trigger flags of the event (each holds the epoch+1 of the
-// last step its producer finished).  Bounded by the watchdog; returns false
+// in flight: the workgroup barriers wait for LDS traffic only).  Counter
+// mode: one lane polls the monotonic counters (summed over the XCD rows)
+// until they reach (epoch+1) * triggers.  Flag mode: one wave polls all
+// trigger flags of the event (each holds the epoch+1 of the last step its
+// producer finished).  Bounded by the watchdog; returns false
 // (uniformly) when the step is being aborted.
 MKD bool mk_wait(const MkProgram &P, const MkStep &S, int ev, int *s_flag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -374,10 +394,10 @@ MKD bool mk_wait(const MkProgram &P, const MkStep &S, int ev, int *s_flag) {
     if (threadIdx.x == 0) {
       const uint32_t need = (S.epoch + 1u) * (uint32_t)P.ev_count[ev];
       int ok = 1;
-      if ((int32_t)(ldcu(P.ctr + ev) - need) < 0) {
+      if ((int32_t)(ctr_total(P, ev) - need) < 0) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         uint32_t spins = 0;
-        while ((int32_t)(ldcu(P.ctr + ev) - need) < 0) {
+        while ((int32_t)(ctr_total(P, ev) - need) < 0) {
           __builtin_amdgcn_s_sleep(1);
           if ((++spins & 31u) == 0) {
             if (mk_aborted(P)) { ok = 0; break; }
@@ -428,7 +448,7 @@ MKD void mk_signal(const MkProgram &P, const MkStep &S, int ev, int slot) {
   __syncthreads();
   if (threadIdx.x == 0) {
     if (P.sync_mode == 0)
-      addcu(P.ctr + ev, 1u);
+      ctr_bump(P, ev);
     else
       stcu(P.flags + P.ev_flag_base[ev] + slot, S.epoch + 1u);
   }

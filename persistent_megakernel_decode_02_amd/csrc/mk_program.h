@@ -8,6 +8,12 @@
 #pragma once
 #include <stdint.h>
 
+// Counter mode keeps one row of event counters per XCD: a producer bumps its
+// own XCD's row and a waiter sums the rows, so the atomic adds of one event
+// land on MK_CTR_ROWS addresses (4 KiB apart) instead of queueing on one.
+#define MK_CTR_ROWS 8
+static inline int mk_ctr_stride(int n_events) { return ((n_events > 1 ? n_events : 1) + 1023) & ~1023; }
+
 #define MK_MAX_BATCH 16
 #define MK_MAX_GROUP 4     // q heads per kv head
 #define MK_BLOCK 512       // threads per workgroup (8 wave64)
@@ -103,6 +109,7 @@ struct MkProgram {
   int32_t tied;
   int32_t sync_mode;                  // 0 counters, 1 flags, 2 data sentinels
   int32_t n_cu, n_instr, n_levels, n_events, n_lm_parts;
+  int32_t ctr_stride;                 // words between the per-XCD rows of ctr
   uint32_t watchdog_ticks;            // s_memrealtime ticks (100 MHz) before a wait gives up
   // role-engine LDS layout (byte offsets into dynamic LDS) and ring size
   int32_t lds_x, lds_resid, lds_out, lds_ring, n_pages, lds_total;
@@ -155,7 +162,7 @@ struct MkProgram {
   int32_t *lm_idx;
 
   // synchronisation
-  uint32_t *ctr;     // [n_events] monotonic counters
+  uint32_t *ctr;     // [MK_CTR_ROWS][ctr_stride] monotonic counters, one row per XCD
   uint32_t *flags;   // [sum ev_count] epoch flags
   uint32_t *tickets; // [n_tickets] monotonic last-arriver tickets
   int32_t *err;      // [4]: code, detail, abort flag, spare

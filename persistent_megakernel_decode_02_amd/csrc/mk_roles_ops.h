@@ -811,7 +811,7 @@ MKD bool wave_wait_event(const MkRole &R, int ev) {
     bool ready;
     if (P.sync_mode == 0) {
       const uint32_t need = (S.epoch + 1u) * (uint32_t)P.ev_count[ev];
-      ready = (int32_t)(__builtin_amdgcn_readfirstlane(ldcu(P.ctr + ev)) - need) >= 0;
+      ready = (int32_t)(__builtin_amdgcn_readfirstlane(ctr_total(P, ev)) - need) >= 0;
     } else {
       const uint32_t want = S.epoch + 1u;
       const int n = P.ev_count[ev];
@@ -831,7 +831,7 @@ MKD void wave_signal_event(const MkRole &R, int ev, int slot) {
   MkProgC &P = R.P;
   if ((threadIdx.x & 63) != 0) return;
   if (P.sync_mode == 0)
-    addcu(P.ctr + ev, 1u);
+    ctr_bump(P, ev);
   else
     stcu(P.flags + P.ev_flag_base[ev] + slot, R.S.epoch + 1u);
 }

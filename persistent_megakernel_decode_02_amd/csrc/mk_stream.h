@@ -262,7 +262,7 @@ MKD bool st_wait_event(const MkProgram &P, const MkStep &S, int ev) {
   if (P.sync_mode == MKSYNC_COUNTER) {
     const uint32_t need = (S.epoch + 1u) * (uint32_t)P.ev_count[ev];
     while (true) {
-      const uint32_t c = __builtin_amdgcn_readfirstlane(ldcu(P.ctr + ev));
+      const uint32_t c = __builtin_amdgcn_readfirstlane(ctr_total(P, ev));
       if ((int32_t)(c - need) >= 0) return true;
       if (spins == 0) t0 = __builtin_amdgcn_s_memrealtime();
       __builtin_amdgcn_s_sleep(1);
@@ -298,7 +298,7 @@ MKD void st_signal(const MkProgram &P, const MkStep &S, int ev, int slot) {
   wait_vm();  // this wave's output stores have completed
   if ((mk_tid() & 63) == 0) {
     if (P.sync_mode == MKSYNC_COUNTER)
-      addcu(P.ctr + ev, 1u);
+      ctr_bump(P, ev);
     else
       stcu(P.flags + P.ev_flag_base[ev] + slot, S.epoch + 1u);
   }

@@ -223,7 +223,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.lm_val = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.lm_idx = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.sync_begin = o;
-  y.ctr = take(4 * std::max(p->n_events, 1));
+  y.ctr = take(4 * (size_t)MK_CTR_ROWS * mk_ctr_stride(p->n_events));
   y.flags = take(4 * std::max(p->n_flags, 1));
   y.tickets = take(4 * std::max(p->n_tickets, 1));
   y.lm_pk = take(8 * (size_t)std::max(p->n_lm_parts, 1) * B);
