@@ -82,9 +82,10 @@ MKD float bnorm_rs(const Src &src, int K, float eps) {
 // Stage columns [c0, c0 + kc) of the 16 input rows into the bf16 high and
 // low planes.  With a gain the row is RMS-normalised, x * rs * gain[k]; rs is
 // computed here when the chunk is the whole row (kc == K), else taken from
-// rs_in.
+// rs_in.  pre: the gain of a one-chunk row is already in LDS at MK_BGAIN.
 template <class Src>
-MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16_t *gain, float eps, float rs_in) {
+MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16_t *gain, float eps, float rs_in,
+                bool pre) {
   const int b = mk_tid() >> 5, t32 = mk_tid() & 31;
   const int nj = kc >> 7;
   float4 v[MK_BKC / 128];
@@ -113,7 +114,7 @@ MKD void bstage(lds_char *L, const Src &src, int K, int c0, int kc, const uint16
       const int c4 = t32 + 32 * j;  // float4 column inside the chunk
       float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
       if (gain) {
-        const uint64_t g = gld((const uint64_t *)(gain + c0 + 4 * c4));
+        const uint64_t g = pre ? ((const lds_u64 *)(L + MK_BGAIN))[c4] : gld((const uint64_t *)(gain + c0 + 4 * c4));
         const uint32_t g0 = (uint32_t)g, g1 = (uint32_t)(g >> 32);
         x[0] = (x[0] * rs) * bf_lo(g0);
         x[1] = (x[1] * rs) * bf_hi(g0);
@@ -176,6 +177,13 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
     wrow[t] = rowptr(16 * (g0 + (live[t] ? wl + nw * t : 0)) + n);
   }
   const bool run = live[0];
+  // The RMSNorm gain of a one-chunk row goes out first, one 4-bf16 piece per
+  // thread, and into LDS once the wait is over: the gain is read once per
+  // layer, so it comes from HBM, where a load issued after the wait would
+  // queue behind every CU's weight stream.
+  const bool pre = gain && nch == 1;
+  uint64_t gpc = 0;
+  if (pre && mk_tid() < (K >> 2)) gpc = gld((const uint64_t *)gain + mk_tid());
   mk_u32x4 w[PF][TPW];
   if (run)
 #pragma unroll
@@ -184,6 +192,7 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
 #pragma unroll
         for (int t = 0; t < TPW; ++t) w[p][t] = __builtin_nontemporal_load((const MK_G(mk_u32x4) *)(wrow[t] + woff(p)));
   if (first && !wait()) return false;
+  if (pre) ((lds_u64 *)(L + MK_BGAIN))[mk_tid()] = gpc;  // read after the chunk loop's first barrier
   const float rs = (gain && nch > 1) ? bnorm_rs(src, K, eps) : 1.f;
   mk_f32x4v acc[TPW];
 #pragma unroll
@@ -191,7 +200,7 @@ MKD bool bgemm_run(const Src &src, int K, int g0, int ng, int ks, bool first, co
   for (int c = 0; c < nch; ++c) {
     const int last = c == nch - 1, kc = last ? kcl : MK_BKC, pc = last ? perl : per, j0 = c * per;
     lds_barrier();
-    bstage(L, src, K, c * MK_BKC, kc, gain, eps, rs);
+    bstage(L, src, K, c * MK_BKC, kc, gain, eps, rs, pre);
     lds_barrier();
     if (run) {
       const lds_char *xc = L + n * MK_BROW + 16 * q + 64 * kp * pc;

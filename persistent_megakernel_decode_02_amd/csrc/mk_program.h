@@ -44,6 +44,8 @@ static inline int mk_ctr_stride(int n_events) { return ((n_events > 1 ? n_events
 #define MK_BRED (2 * MK_BPLANE)               // per-wave fp32 partial tiles [MK_NWAVES][256]
 #define MK_BARG (MK_BRED + MK_NWAVES * 1024)  // per-wave argmax (value, index) per sequence
 #define MK_BLDS (MK_BARG + MK_NWAVES * MK_MAX_BATCH * 8)
+#define MK_BGAIN MK_BLDS                      // [MK_BKC / 4] RMSNorm gain of a one-chunk row, 4 bf16 each
+#define MK_BLDS_END (MK_BGAIN + MK_BKC * 2)
 
 // attention instruction of the homogeneous engine (byte offsets into dynamic LDS)
 #define MK_FA_Q 0                                                // [G][d] fp32 scaled, rotated queries

@@ -105,7 +105,7 @@ static int lds_requirement(const mk_plan_t *p) {
   for (const MkInstr &in : p->instr)
     if (in.op != MKOP_ATTN) rows = std::max<int64_t>(rows, in.r1 - in.r0);
   int64_t gemv = kmax * 4 + 256 + (int64_t)MK_NWAVES * 4 * 4 + (int64_t)s.hidden * 4 + (rows + 4) * 4;
-  if (B >= MK_MFMA_MIN_BATCH) gemv = std::max<int64_t>(gemv, MK_BLDS);
+  if (B >= MK_MFMA_MIN_BATCH) gemv = std::max<int64_t>(gemv, MK_BLDS_END);
   // attention: queries, this step's key/value, per-wave value blocks and partials
   return (int)std::max<int64_t>(gemv, MK_FA_LDS);
 }
