@@ -185,7 +185,7 @@ def main():
                     choices=["mega-counter", "mega-flag", "mega-sentinel", "multi", "flat-counter", "flat-flag",
                              "flat-sentinel", "flat-levels", "queue-flag", "stream-counter", "stream-flag"],
                     help="execution / synchronisation scheme of the headline number (default: flat-sentinel, "
-                         "the homogeneous engine polling data sentinels, at batch 1; flat-flag otherwise)")
+                         "the homogeneous engine polling data sentinels, at batch 1; flat-counter otherwise)")
     ap.add_argument("--trace", default=None, help="write a per-instruction trace of one pass (npz) here")
     ap.add_argument("--trace-passes", type=int, default=4, help="traced passes run back to back (the last is kept)")
     ap.add_argument("--kv-splits", type=int, default=0, help="attention key-range splits (0: planner default)")
@@ -219,7 +219,7 @@ def main():
     s = wl.shape
     B = wl.batch
     if args.mode is None:
-        args.mode = "flat-sentinel" if B == 1 else "flat-flag"
+        args.mode = "flat-sentinel" if B == 1 else "flat-counter"
     K, W = args.steps, args.warmup
     # passes restart from the first position after the warmup (and before a
     # trace), so the workload's own context bound holds whenever it covers them
@@ -341,7 +341,7 @@ def main():
                             "hbm_frac": round(bpp / (ms2 / K * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             log(f"[bench] {name}: {K} passes in {ms2:.3f} ms")
         # multi-token persistent decode: all K passes in one launch
-        for name in ("flat-sentinel", "flat-flag"):
+        for name in ("flat-sentinel", "flat-counter"):
             if B > 1 and name == "flat-sentinel":
                 continue
             if name == args.mode and spl == K:
@@ -372,7 +372,7 @@ def main():
         bw = si.WORKLOADS["llama1b_b16"]
         if bw.shape == s and B != bw.batch:
             extras["batched"] = run_workload(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log,
-                                             mk.MK_EXEC_FLAT, mk.MK_SYNC_FLAG, "flat-flag")
+                                             mk.MK_EXEC_FLAT, mk.MK_SYNC_COUNTER, "flat-counter")
             extras["batched_queue"] = run_workload(si, engine, mk, bw, gw, dev, stream, min(K, 32), 2, log,
                                                    mk.MK_EXEC_QUEUE, mk.MK_SYNC_FLAG, "queue-flag")
         # the other one-sequence configurations in the headline mode: the same
