@@ -422,6 +422,7 @@ static int ctx_create_on(const mk_plan_t *plan, void *d_workspace, size_t ws_byt
   P.hbuf = (float *)(w + y.hbuf);
   P.xout = (float *)(w + y.xout);
   P.part = (float *)(w + y.part);
+  P.dpart = (float *)(w + y.dpart);
   P.lm_pk = (uint64_t *)(w + y.lm_pk);
   P.lm_val = (float *)(w + y.lm_val);
   P.lm_idx = (int32_t *)(w + y.lm_idx);

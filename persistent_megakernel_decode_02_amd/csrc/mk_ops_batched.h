@@ -370,13 +370,35 @@ MKD int op_gateup_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait
   return MK_ST_SIGNAL;
 }
 
+// Every split of an attention unit (every part of a split down slice) takes
+// a ticket once its partial is stored; true (uniformly) on the last arriver
+// of this step.
+MKD bool attn_ticket(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
+  wait_vm();
+  __syncthreads();
+  if (mk_tid() == 0) {
+    const uint32_t old = addcu(P.tickets + in.ticket, 1u);
+    *s_flag = (old + 1u == (S.epoch + 1u) * (uint32_t)in.nsplit) ? 1 : 0;
+  }
+  __syncthreads();
+  const int last = *s_flag;
+  __syncthreads();
+  return last != 0;
+}
+
+// Down projection.  A slice split by input columns (in.nsplit parts of
+// K / nsplit columns, one staged chunk each) stores its partial tile in
+// dpart; the last part to finish (ticket) adds the parts in part order and
+// the residual, and stores the rows.
 template <class Wait>
-MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait wait) {
+MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag, Wait wait) {
   const int H = P.H, l = in.layer, K = P.I, nb = S.batch, lane = mk_tid() & 63;
   const int r0 = in.r0, nr = in.r1 - in.r0, nt = (nr + 15) >> 4;
+  const int NS = in.nsplit, Kp = K / NS, k0 = in.split * Kp;
   const MkLayerW W = cld(&P.layers[l]);
   const float *xm = P.xmid + (size_t)l * P.B_max * H;
   float *out = P.xout + (size_t)l * P.B_max * H;
+  float *dp = P.dpart + (size_t)l * NS * P.B_max * H;  // part s, sequence b, row r: dp[(s B_max + b) H + r]
   auto fin = [&](int tile, mk_f32x4v a) {
     const int v = 16 * tile + (lane & 15), b0 = 4 * (lane >> 4);
     if (v < nr)
@@ -384,12 +406,26 @@ MKD int op_down_b(const MkProgram &P, const MkStep &S, const MkInstr &in, Wait w
       for (int j = 0; j < 4; ++j)
         if (b0 + j < nb) {
           const size_t o = (size_t)(b0 + j) * H + r0 + v;
-          stc(out + o, ldc(xm + o) + a[j]);
+          if (NS == 1)
+            stc(out + o, ldc(xm + o) + a[j]);
+          else
+            stc(dp + (size_t)in.split * P.B_max * H + o, a[j]);
         }
   };
-  if (!bgemm(bact(P.hbuf + (size_t)l * P.B_max * K, nb, K), K, nt, nullptr, 0.f,
-             [&](int v) { return W.wd + (size_t)(r0 + min(v, nr - 1)) * K; }, fin, wait))
+  // the part's columns: rows of hbuf from column k0 on (row stride K), and
+  // the same columns of every weight row
+  if (!bgemm(bact(P.hbuf + (size_t)l * P.B_max * K + k0, nb, K), Kp, nt, nullptr, 0.f,
+             [&](int v) { return W.wd + (size_t)(r0 + min(v, nr - 1)) * K + k0; }, fin, wait))
     return MK_ST_ABORT;
+  if (NS == 1) return MK_ST_SIGNAL;
+  if (!attn_ticket(P, S, in, s_flag)) return MK_ST_QUIET;
+  for (int i = mk_tid(); i < nb * nr; i += MK_BLOCK) {
+    const int b = i / nr, v = i - b * nr;
+    const size_t o = (size_t)b * H + r0 + v;
+    float acc = ldc(dp + o);
+    for (int s2 = 1; s2 < NS; ++s2) acc += ldc(dp + (size_t)s2 * P.B_max * H + o);
+    stc(out + o, ldc(xm + o) + acc);
+  }
   return MK_ST_SIGNAL;
 }
 
@@ -517,21 +553,6 @@ MKD void fa_load(FaBlock<D> &f, const uint16_t *Kc, const uint16_t *Vc, int ta, 
     const int c = lane + 64 * r, row = c / FaBlock<D>::CPR, ch = c - row * FaBlock<D>::CPR;
     f.v[r] = gld((const mk_u32x4 *)(Vc + (size_t)min(ta + row, t1 - 1) * D + 8 * ch));
   }
-}
-
-// Every split of an attention unit takes a ticket once its partial is
-// stored; true (uniformly) on the last arriver of this step.
-MKD bool attn_ticket(const MkProgram &P, const MkStep &S, const MkInstr &in, int *s_flag) {
-  wait_vm();
-  __syncthreads();
-  if (mk_tid() == 0) {
-    const uint32_t old = addcu(P.tickets + in.ticket, 1u);
-    *s_flag = (old + 1u == (S.epoch + 1u) * (uint32_t)in.nsplit) ? 1 : 0;
-  }
-  __syncthreads();
-  const int last = *s_flag;
-  __syncthreads();
-  return last != 0;
 }
 
 template <int D, bool SENT, class Wait>
@@ -778,7 +799,7 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
       case MKOP_QKV: return op_qkv_b(P, S, in, wait);
       case MKOP_OPROJ: return op_oproj_b(P, S, in, wait);
       case MKOP_GATEUP: return op_gateup_b(P, S, in, wait);
-      case MKOP_DOWN: return op_down_b(P, S, in, wait);
+      case MKOP_DOWN: return op_down_b(P, S, in, s_flag, wait);
       case MKOP_LMHEAD: return op_lmhead_b(P, S, in, s_flag, wait);
       default: break;
     }

@@ -159,6 +159,7 @@ struct MkProgram {
   float *hbuf;   // [L][B][I]
   float *xout;   // [L][B][H]
   float *part;   // [L][B][nkv][S][G][d + 2]   (m, l, o[d]) per split and q head
+  float *dpart;  // batched down projection split by input columns: [L][Sd][B][H] partial sums per part
   uint64_t *lm_pk; // [n_lm_parts][B] tagged (value, row) of the homogeneous engine's LM-head parts
   float *lm_val; // [n_lm_parts][B]
   int32_t *lm_idx;

@@ -220,6 +220,7 @@ void mk_plan_compute_layout(mk_plan_t *p) {
   y.act_end = o;
   if (p->opts.sync_mode == MK_SYNC_SENTINEL) o += y.act_end - y.qkv;  // second parity
   y.part = take(4 * L * B * nkv * p->S * p->G * (d + 2));
+  y.dpart = take(p->Sd > 1 ? 4 * L * (size_t)p->Sd * B * H : 0);
   y.lm_val = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.lm_idx = take(4 * (size_t)std::max(p->n_lm_parts, 1) * B);
   y.sync_begin = o;
@@ -295,9 +296,24 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
   // tiled copy of the matrix, so its slices start on 16-row tile boundaries
   int rl = (int)ceil_div(V, n_cu);
   if (mk_plan_tiles(p)) rl = (rl + 15) / 16 * 16;
-  const int rd = (int)ceil_div(H, n_cu);
+  int rd = (int)ceil_div(H, n_cu);
+  // Batched plans of the homogeneous engine split each down-projection slice
+  // by its input columns into Sd parts of one staged chunk each (instead of
+  // one instruction staging all I columns chunk by chunk): every part stores
+  // a partial tile, and the last of them to finish adds the parts in order,
+  // plus the residual, and triggers (the attention splits' ticket protocol).
+  // Slices are whole 16-row tiles.
+  int Sd = 1;
+  if ((opts->exec_mode == MK_EXEC_FLAT || opts->exec_mode == MK_EXEC_FLAT_MULTI || opts->exec_mode == MK_EXEC_QUEUE) &&
+      B >= MK_MFMA_MIN_BATCH && I % MK_BKC == 0 && I >= 2 * MK_BKC && H % 16 == 0) {
+    Sd = I / MK_BKC;
+    rd = (int)(ceil_div(ceil_div((int64_t)H * Sd, n_cu), 16) * 16);
+  }
+  p->Sd = Sd;
+  const int n_dslices = (int)ceil_div(H, rd);
+  const int dticket0 = S > 1 ? L * B * nkv : 0;
   p->n_lm_parts = (int)ceil_div(V, rl);
-  p->n_tickets = (S > 1 ? L * B * nkv : 0) + 1;
+  p->n_tickets = dticket0 + (Sd > 1 ? L * n_dslices : 0) + 1;
   const int lm_ticket = p->n_tickets - 1;
 
   auto blank = [](int op, int layer, int level) {
@@ -392,13 +408,18 @@ int mk_plan_build(const mk_model_shape *shape, const mk_plan_opts *opts, int n_c
     }
     // down projection + residual
     {
-      for (int r0 = 0; r0 < H; r0 += rd) {
-        MkInstr in = blank(MKOP_DOWN, l, base + LV_DOWN);
-        in.r0 = r0;
-        in.r1 = std::min(H, r0 + rd);
-        lvl.push_back({in, 2.0 * (in.r1 - in.r0) * I});
-        wbytes += 2.0 * (in.r1 - in.r0) * I;
-      }
+      int k = 0;
+      for (int r0 = 0; r0 < H; r0 += rd, ++k)
+        for (int sp = 0; sp < Sd; ++sp) {
+          MkInstr in = blank(MKOP_DOWN, l, base + LV_DOWN);
+          in.r0 = r0;
+          in.r1 = std::min(H, r0 + rd);
+          in.split = sp;
+          in.nsplit = Sd;
+          in.ticket = Sd > 1 ? dticket0 + l * n_dslices + k : -1;
+          lvl.push_back({in, 2.0 * (in.r1 - in.r0) * I / Sd});
+          wbytes += 2.0 * (in.r1 - in.r0) * I / Sd;
+        }
       assign(lvl);
     }
     wbytes += 4.0 * H;  // two norm gains
@@ -613,8 +634,13 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
         if ((p->S > 1) != (in.ticket >= 0)) return MK_ERR_PLAN;
         break;
       case MKOP_OPROJ:
+        if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.H || in.r0 >= in.r1) return MK_ERR_PLAN;
+        break;
       case MKOP_DOWN:
         if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.H || in.r0 >= in.r1) return MK_ERR_PLAN;
+        if (in.nsplit != p->Sd || in.split < 0 || in.split >= in.nsplit) return MK_ERR_PLAN;
+        if ((p->Sd > 1) != (in.ticket >= 0)) return MK_ERR_PLAN;
+        if (p->Sd > 1 && (in.r0 % 16 || ck.I % (p->Sd * MK_BKC) != 0 || ck.I / p->Sd != MK_BKC)) return MK_ERR_PLAN;
         break;
       case MKOP_GATEUP:
         if (l < 0 || l >= L || in.r0 < 0 || in.r1 > ck.I || in.r0 >= in.r1) return MK_ERR_PLAN;
@@ -645,8 +671,8 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
     if (in.wait_ev >= 0) min_wait[in.wait_ev] = std::min(min_wait[in.wait_ev], in.level);
     if (in.sig_ev >= 0) {
       max_trig[in.sig_ev] = std::max(max_trig[in.sig_ev], in.level);
-      if (in.op == MKOP_ATTN) {
-        if (in.split == 0) attn_units[in.sig_ev]++;  // one trigger per (sequence, kv head)
+      if (in.op == MKOP_ATTN || (in.op == MKOP_DOWN && p->Sd > 1)) {
+        if (in.split == 0) attn_units[in.sig_ev]++;  // one trigger per attention unit / down slice
       } else {
         if (slot_used[in.sig_ev][in.sig_slot]) return MK_ERR_PLAN;
         slot_used[in.sig_ev][in.sig_slot] = 1;
@@ -673,6 +699,18 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
         if (v != full) return MK_ERR_PLAN;
   }
 
+  // every down slice has all Sd parts
+  if (p->Sd > 1) {
+    std::map<std::pair<int, int>, int> parts;
+    for (int i = 0; i < n; ++i) {
+      const MkInstr &in = p->instr[i];
+      if (in.op == MKOP_DOWN) parts[{in.layer, in.r0}] |= 1 << std::min(in.split, 30);
+    }
+    const int full = p->Sd >= 31 ? -1 : (1 << p->Sd) - 1;
+    for (auto &kv : parts)
+      if (kv.second != full) return MK_ERR_PLAN;
+  }
+
   // 3. writes: every output slice written exactly once per step
   std::vector<std::vector<Writer>> writers(BK_N * L);
   std::vector<Access> rd, wr;
@@ -696,7 +734,7 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
       }
       int64_t covered = 0;
       for (size_t j = 0; j < w.size(); ++j) {
-        if (k == BK_ATTN) {  // all splits of one unit share the unit's slice
+        if (k == BK_ATTN || (k == BK_XOUT && p->Sd > 1)) {  // all splits / parts of one unit share its slice
           if (w[j].lo < covered && !(j > 0 && w[j].lo == w[j - 1].lo && w[j].hi == w[j - 1].hi)) return MK_ERR_PLAN;
           covered = std::max(covered, w[j].hi);
           continue;
@@ -820,8 +858,8 @@ int mk_plan_check(const mk_plan_t *p, bool simulate, int trials, uint64_t seed) 
         ++executed;
         const MkInstr &in = p->instr[i];
         int fire = -1;
-        if (in.op == MKOP_ATTN && in.ticket >= 0) {
-          if (++tick[in.ticket] == p->S) fire = in.sig_ev;
+        if ((in.op == MKOP_ATTN || in.op == MKOP_DOWN) && in.ticket >= 0) {
+          if (++tick[in.ticket] == in.nsplit) fire = in.sig_ev;
         } else {
           fire = in.sig_ev;
         }
@@ -1042,18 +1080,19 @@ extern "C" int mk_events_normalize(int32_t nt, const int32_t *pred_begin, const 
 }
 
 // The plan's tasks are its instructions, except that the splits of one
-// attention unit are one task (only the unit's last arriver triggers); the
+// attention unit, and the parts of one down slice, are one task (only the
+// last arriver triggers); the
 // raw edges run from the writers of every slice an instruction reads.
 int mk_plan_normalize_events(mk_plan_t *p) {
   if (!p) return MK_ERR_INVALID_ARG;
   Checker ck(p);
   const int n = (int)p->instr.size();
   std::vector<int> task_of(n, -1), first_instr;
-  std::map<std::tuple<int, int, int>, int> attn_task;
+  std::map<std::tuple<int, int, int, int>, int> attn_task;
   for (int i = 0; i < n; ++i) {
     const MkInstr &in = p->instr[i];
-    if (in.op == MKOP_ATTN) {
-      auto key = std::make_tuple(in.layer, in.r0, in.r1);
+    if (in.op == MKOP_ATTN || (in.op == MKOP_DOWN && in.nsplit > 1)) {
+      auto key = std::make_tuple(in.op, in.layer, in.r0, in.r1);
       auto it = attn_task.find(key);
       if (it != attn_task.end()) {
         task_of[i] = it->second;

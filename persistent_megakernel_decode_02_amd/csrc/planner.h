@@ -13,7 +13,7 @@
 // engine's program record for odd steps in sentinel mode
 struct MkLayout {
   size_t prog, prog_odd, instr, cu_begin, level_begin, level_list, queue, ev_count, ev_flag_base, rope, layers, rowtab;
-  size_t qkv, attn, xmid, hbuf, xout, act_end, part, lm_val, lm_idx, ctr, flags, tickets, lm_pk, lm_done, queue_ctr, err;
+  size_t qkv, attn, xmid, hbuf, xout, act_end, part, dpart, lm_val, lm_idx, ctr, flags, tickets, lm_pk, lm_done, queue_ctr, err;
   size_t lm_tiled, lm_tiled_bytes;  // batched plans: tiled copy of the LM-head matrix (0 bytes: none)
   size_t gu_tiled, gu_tiled_bytes;  // batched plans: tiled gate/up rows of every layer (0 bytes: none)
   size_t sync_begin, sync_end;  // [ctr .. err] zeroed on create/reset
@@ -24,6 +24,7 @@ struct mk_plan_s {
   mk_model_shape shape;
   mk_plan_opts opts;
   int n_cu = 0, S = 1, B = 1, max_ctx = 0, G = 1;
+  int Sd = 1;  // input-column parts of each down-projection slice (batched plans)
   int n_levels = 0, n_events = 0, n_flags = 0, n_tickets = 0, n_lm_parts = 0;
   int lds_bytes = 0;
   int lds_x = 0, lds_resid = 0, lds_out = 0, lds_ring = 0, n_pages = 0, out_stride = 0;  // role engine

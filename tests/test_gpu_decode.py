@@ -165,27 +165,30 @@ def test_tiny_batched_decode_matches_oracle(tiny_setup, batch, mode):
     print(f"kv exact fraction {check_kv(res, max_rel_err=1e-3):.5f}")
 
 
-# FFN width 4608: the batched down projection stages its input in three
-# 2048-column chunks (the last one ragged, 512 columns), each chunk's loads
-# issued while the previous chunk is multiplied.
-WIDE = si.ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=4608, vocab=4096)
+# Wider FFNs at batch size >= 2.  Width 4608: the batched down projection
+# stages its input in three 2048-column chunks (the last one ragged, 512
+# columns).  Width 6144: each down slice is split by input columns into three
+# parts of one chunk, merged by the last part to finish (ticket).
+WIDE = {ffn: si.ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=ffn, vocab=4096)
+        for ffn in (4608, 6144)}
 
 
-@pytest.fixture(scope="module")
-def wide_setup():
-    w = si.make_weights(WIDE, master=3)
-    return w, engine.to_gpu(w), orc.Model(WIDE, w)
+@pytest.fixture(scope="module", params=[4608, 6144])
+def wide_setup(request):
+    s = WIDE[request.param]
+    w = si.make_weights(s, master=3)
+    return s, w, engine.to_gpu(w), orc.Model(s, w)
 
 
 @pytest.mark.parametrize("batch", [3, 16])
-@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag"])
+@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag", "queue-flag"])
 def test_tiny_wide_ffn_batched_decode_matches_oracle(wide_setup, batch, mode):
-    wl = si.Workload(f"wide_b{batch}", WIDE, batch=batch, steps=4, start_pos=-1, len_lo=1, len_hi=100,
+    s, w, gw, model = wide_setup
+    wl = si.Workload(f"wide{s.ffn}_b{batch}", s, batch=batch, steps=4, start_pos=-1, len_lo=1, len_hi=100,
                      max_ctx=TINY.max_ctx)
-    w, gw, model = wide_setup
     res = run_decode(wl, wl.steps, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
                      sync_mode=MODES[mode][1])
-    print(f"wide b={batch} {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}")
+    print(f"wide ffn={s.ffn} b={batch} {mode}: max rel logit err {res.max_rel_err:.3e}, near ties {res.near_ties}")
     assert res.max_rel_err <= 1e-3
     assert res.near_ties == 0
     check_kv(res, max_rel_err=1e-3)
