@@ -349,3 +349,55 @@ def test_stream_engine_limits():
         assert lay[7] == lay[5] - lay[0] > 0  # a second activation copy, one per step parity
     finally:
         mk.mk_plan_destroy(plan)
+
+
+def test_batched_down_projection_split_by_input_columns():
+    """Batched plans of the homogeneous engine cut each down-projection slice
+    (whole 16-row tiles) into I / 2048 parts of one staged input chunk; the
+    parts of a slice share its output rows and its event (the last part to
+    finish merges and triggers), every CU gets one part per layer at
+    Llama-1B batch 16, and one-sequence plans keep whole slices."""
+    shape, batch, max_ctx = SHAPES["llama1b_b16"]
+    plan = mk.mk_plan_create(shape_struct(shape), plan_opts(batch, max_ctx, num_cus=256, exec_mode=mk.MK_EXEC_FLAT))
+    try:
+        descs = mk.mk_plan_export(plan)
+        parts = {}
+        for d in descs:
+            if d.op == mk.MK_OP_DOWN:
+                assert d.n_splits == shape.ffn // 2048 == 4
+                assert d.r0 % 16 == 0 and d.r1 - d.r0 == 32
+                parts.setdefault((d.layer, d.r0), []).append(d)
+        assert len(parts) == shape.n_layers * shape.hidden // 32
+        for ps in parts.values():
+            assert sorted(p.split for p in ps) == [0, 1, 2, 3]
+            assert len({(p.r1, p.signal_event, p.wait_event) for p in ps}) == 1
+        for l in range(shape.n_layers):
+            cus = [d.cu for d in descs if d.op == mk.MK_OP_DOWN and d.layer == l]
+            assert len(cus) == 256 and len(set(cus)) == 256
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        assert mk.mk_plan_simulate(plan, 3, 11) == mk.MK_OK
+    finally:
+        mk.mk_plan_destroy(plan)
+    shape1, batch1, max_ctx1 = SHAPES["llama1b_pos1024"]
+    plan = mk.mk_plan_create(shape_struct(shape1), plan_opts(batch1, max_ctx1, num_cus=256, exec_mode=mk.MK_EXEC_FLAT))
+    try:
+        assert all(d.n_splits == 1 for d in mk.mk_plan_export(plan) if d.op == mk.MK_OP_DOWN)
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_down_slice_missing_a_part_is_rejected():
+    # FFN 6144 at batch 3: three parts per down slice; one part relabelled as
+    # its neighbour leaves the slice's partial sums incomplete
+    s = si.ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=6144, vocab=4096)
+    plan = mk.mk_plan_create(shape_struct(s), plan_opts(3, 128, num_cus=8, exec_mode=mk.MK_EXEC_FLAT))
+    try:
+        assert mk.mk_plan_validate(plan) == mk.MK_OK
+        assert mk.mk_plan_simulate(plan, 50, 5) == mk.MK_OK
+        descs = mk.mk_plan_export(plan)
+        d = next(x for x in descs if x.op == mk.MK_OP_DOWN and x.layer == 1 and x.split == 2)
+        d.split = 1
+        assert mk.mk_plan_set_instructions(plan, descs) == mk.MK_OK
+        assert mk.mk_plan_validate(plan) == mk.MK_ERR_PLAN
+    finally:
+        mk.mk_plan_destroy(plan)
