@@ -794,7 +794,9 @@ MKD int run_instr(const MkProgram &P, const MkStep &S, const MkInstr &in, float 
     if (timed) ts = __builtin_amdgcn_s_memrealtime();
     return ok;
   };
-  if (!SENT && S.batch >= MK_MFMA_MIN_BATCH) {
+  // (a down slice split by input columns runs as parts whatever the step's
+  // batch: its plan counts one trigger per slice, from the merging part)
+  if (!SENT && (S.batch >= MK_MFMA_MIN_BATCH || (in.op == MKOP_DOWN && in.nsplit > 1))) {
     switch (in.op) {
       case MKOP_QKV: return op_qkv_b(P, S, in, wait);
       case MKOP_OPROJ: return op_oproj_b(P, S, in, wait);

@@ -194,6 +194,23 @@ def test_tiny_wide_ffn_batched_decode_matches_oracle(wide_setup, batch, mode):
     check_kv(res, max_rel_err=1e-3)
 
 
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag", "queue-flag"])
+def test_tiny_wide_ffn_batch_below_plan_bound(wide_setup, batch, mode):
+    # a plan for 4 sequences stepped with 1 or 2: with one sequence the
+    # projections take the vector path, except a down slice split by input
+    # columns, which still runs as parts merged by the last one
+    s, w, gw, model = wide_setup
+    wl = si.Workload(f"wide{s.ffn}_b4", s, batch=4, steps=3, start_pos=-1, len_lo=1, len_hi=100,
+                     max_ctx=TINY.max_ctx)
+    res = run_decode(wl, 3, weights=w, gpu_weights=gw, model=model, exec_mode=MODES[mode][0],
+                     sync_mode=MODES[mode][1], batch=batch, max_batch=4)
+    assert res.max_rel_err <= 1e-3
+    assert res.near_ties == 0
+    check_kv(res, max_rel_err=1e-3)
+    assert np.array_equal(res.kv_gpu[:, :, batch:], res.kv_before[:, :, batch:])
+
+
 def test_tiny_batched_split_attention(tiny_setup):
     wl = TINY_BATCHED[16]
     w, gw, model = tiny_setup
