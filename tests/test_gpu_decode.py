@@ -181,7 +181,7 @@ def wide_setup(request):
 
 
 @pytest.mark.parametrize("batch", [3, 16])
-@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag", "queue-flag"])
+@pytest.mark.parametrize("mode", ["flat-counter", "flat-flag", "queue-flag", "flat-levels"])
 def test_tiny_wide_ffn_batched_decode_matches_oracle(wide_setup, batch, mode):
     s, w, gw, model = wide_setup
     wl = si.Workload(f"wide{s.ffn}_b{batch}", s, batch=batch, steps=4, start_pos=-1, len_lo=1, len_hi=100,
